@@ -1,0 +1,59 @@
+// Factor-cache append: cache[b, start_pos + s] = factors[b, s] for the four
+// key/value factor tensors, as a bit copy ("Tensor Product Attention Is All
+// You Need" review on coreui.cn, code walk-through 前向传播: the cache writes
+// at [:bsz, start_pos:start_pos+seqlen]).
+//
+// One launch covers all four tensors (blockIdx.y).  Each sequence's block of
+// S tokens is contiguous in the source and in the cache, so the copy runs over
+// (sequence, byte-range) with the widest unit that every row, stride and
+// pointer allows.
+#include "kernels.h"
+
+namespace tpa {
+
+template <typename U>
+__global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
+  const int t = blockIdx.y;
+  const int64_t units_per_seq = a.width_bytes[t] * a.S / (int64_t)sizeof(U);
+  const int64_t total = units_per_seq * a.n_batch;
+  const char* src = reinterpret_cast<const char*>(a.src[t]);
+  char* dst = reinterpret_cast<char*>(a.dst[t]) + a.start_pos * a.width_bytes[t];
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = idx / units_per_seq;
+    const int64_t u = idx - b * units_per_seq;
+    const U v = reinterpret_cast<const U*>(src + b * a.src_bstride[t])[u];
+    reinterpret_cast<U*>(dst + b * a.dst_bstride[t])[u] = v;
+  }
+}
+
+static bool all_multiple(const AppendArgs& a, int64_t unit) {
+  for (int t = 0; t < 4; ++t) {
+    if ((a.width_bytes[t] * a.S) % unit || a.src_bstride[t] % unit || a.dst_bstride[t] % unit) return false;
+    if (((uintptr_t)a.src[t]) % unit || ((uintptr_t)a.dst[t] + a.start_pos * a.width_bytes[t]) % unit) return false;
+  }
+  return true;
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
+  int64_t max_bytes = 0;
+  for (int t = 0; t < 4; ++t) {
+    const int64_t v = a.width_bytes[t] * a.S * a.n_batch;
+    if (v > max_bytes) max_bytes = v;
+  }
+  auto grid_for = [&](int64_t unit) {
+    int64_t blocks = (max_bytes / unit + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    if (blocks < 1) blocks = 1;
+    return dim3((unsigned)blocks, 4);
+  };
+  if (all_multiple(a, 16))
+    hipLaunchKernelGGL(append_kernel<uint4>, grid_for(16), dim3(256), 0, st, a);
+  else if (all_multiple(a, 4))
+    hipLaunchKernelGGL(append_kernel<uint32_t>, grid_for(4), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(append_kernel<uint16_t>, grid_for(2), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace tpa

@@ -1,0 +1,57 @@
+// Device helpers shared by the libtpa kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpa {
+
+typedef uint16_t bf16_t;
+
+// ---------------------------------------------------------------------------
+// bfloat16 <-> float32.  bf16 is the top half of an IEEE binary32; narrowing
+// rounds to nearest, ties to even, and keeps NaNs quiet.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Element load/store in float32 arithmetic, for either storage type.
+__device__ __forceinline__ float ldf(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ldf(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ void stf(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void stf(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+
+// ---------------------------------------------------------------------------
+// Rotary angles.  rev[i] = base^(-2i/d_h) / (2*pi), computed on the host in
+// float64.  The angle pos*theta_i is formed in float64 as a number of turns,
+// reduced to [-1/2, 1/2] turns, and only then narrowed to float32 for
+// sincospi (so large positions lose no precision to the narrowing).
+// ---------------------------------------------------------------------------
+constexpr int kMaxRopePairs = 128;  // head_dim <= 256
+
+struct RopeTable {
+  double rev[kMaxRopePairs];
+};
+
+__device__ __forceinline__ void rope_cos_sin(const RopeTable& tab, int64_t pos, int pair, float& c, float& s) {
+  double turns = (double)pos * tab.rev[pair];
+  turns -= rint(turns);
+  sincospif((float)(2.0 * turns), &s, &c);
+}
+
+// Softmax runs in base 2: scores are pre-multiplied by log2(e).
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace tpa

@@ -1,0 +1,234 @@
+// Decode attention over the factor cache: one new query per sequence.
+//
+// Scores use the factored form s_t = sum_r A_K[t,h,r] (B~_K[t,r,:] . q_h) with
+// q pre-scaled by log2(e) / (R_Q R_K sqrt(d_h)), so keys are never rebuilt;
+// values are accumulated as sum_t sum_r (p_t A_V[t,h,r]) B_V[t,r,:] and scaled
+// by 1/R_V at the end.  ("Tensor Product Attention Is All You Need" review on
+// coreui.cn: the K_t and V_t equations of 核心机制总结 and the attention of the
+// code walk-through 前向传播; question 2: the cached key factors are already
+// rotated, so decode does no rotation.)
+//
+// The context is split into chunks, one workgroup per (sequence, chunk); each
+// writes its partial (running max m, sum l, unnormalised acc[d_h]) per head to
+// the workspace, and a combine pass merges the chunks in index order, so the
+// result does not depend on scheduling.
+#include "kernels.h"
+
+namespace tpa {
+
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeTile = 16;        // tokens per inner step
+constexpr int kMaxHeadElems = 8192;    // h * d_h limit of this library
+constexpr int kMaxOutPerThread = kMaxHeadElems / kDecodeThreads;
+
+// Query formation for sequence b into LDS, fp32, pre-scaled.
+template <typename T>
+__device__ void form_query(const AttnArgs& a, int64_t b, int64_t s, float* qs) {
+  const int h = a.h, dh = a.d_h;
+  const T* AQ = reinterpret_cast<const T*>(a.a_q);
+  const T* BQ = reinterpret_cast<const T*>(a.b_q);
+  const int64_t tok = b * a.q_bstride_tok + s;
+  for (int idx = threadIdx.x; idx < h * dh; idx += blockDim.x) {
+    const int hh = idx / dh, d = idx - hh * dh;
+    float v;
+    if (a.rq == 0) {
+      v = ldf(BQ, tok * h * dh + idx);
+    } else {
+      v = 0.f;
+      for (int r = 0; r < a.rq; ++r)
+        v = fmaf(ldf(AQ, (tok * h + hh) * a.rq + r), ldf(BQ, (tok * a.rq + r) * dh + d), v);
+    }
+    qs[idx] = v * a.q_scale;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(AttnArgs a, int64_t ctx_len,
+                                                                        int64_t chunk, int64_t n_chunks,
+                                                                        float* ws) {
+  extern __shared__ float smem[];
+  const int h = a.h, dh = a.d_h;
+  float* qs = smem;                      // [h][d_h]
+  float* sc = qs + h * dh;               // [tile][h] scores, then probabilities
+  float* mrow = sc + kDecodeTile * h;    // [h] running max (base-2 units)
+  float* lrow = mrow + h;                // [h] running sum
+  float* alpha = lrow + h;               // [h] rescale of this step
+  const int64_t b = blockIdx.y;
+  const int64_t c = blockIdx.x;
+  const int64_t t0 = c * chunk;
+  const int64_t t1 = (t0 + chunk < ctx_len) ? t0 + chunk : ctx_len;
+  const T* AK = reinterpret_cast<const T*>(a.c_ak);
+  const T* BK = reinterpret_cast<const T*>(a.c_bk);
+  const T* AV = reinterpret_cast<const T*>(a.c_av);
+  const T* BV = reinterpret_cast<const T*>(a.c_bv);
+  const int64_t seq0 = b * a.max_seq;
+
+  form_query<T>(a, b, 0, qs);
+  for (int hh = threadIdx.x; hh < h; hh += blockDim.x) {
+    mrow[hh] = -INFINITY;
+    lrow[hh] = 0.f;
+  }
+  float acc[kMaxOutPerThread];
+#pragma unroll
+  for (int j = 0; j < kMaxOutPerThread; ++j) acc[j] = 0.f;
+  __syncthreads();
+
+  for (int64_t tt0 = t0; tt0 < t1; tt0 += kDecodeTile) {
+    for (int item = threadIdx.x; item < kDecodeTile * h; item += blockDim.x) {
+      const int tl = item / h, hh = item - tl * h;
+      const int64_t t = tt0 + tl;
+      float s = -INFINITY;
+      if (t < t1) {
+        s = 0.f;
+        for (int r = 0; r < a.rk; ++r) {
+          const int64_t brow = ((seq0 + t) * a.rk + r) * dh;
+          float dot = 0.f;
+          for (int d = 0; d < dh; ++d) dot = fmaf(ldf(BK, brow + d), qs[hh * dh + d], dot);
+          s = fmaf(ldf(AK, ((seq0 + t) * h + hh) * a.rk + r), dot, s);
+        }
+      }
+      sc[item] = s;
+    }
+    __syncthreads();
+    for (int hh = threadIdx.x; hh < h; hh += blockDim.x) {
+      float mx = mrow[hh];
+      for (int tl = 0; tl < kDecodeTile; ++tl) mx = fmaxf(mx, sc[tl * h + hh]);
+      const float al = fast_exp2(mrow[hh] - mx);
+      float sum = 0.f;
+      for (int tl = 0; tl < kDecodeTile; ++tl) {
+        const float p = fast_exp2(sc[tl * h + hh] - mx);
+        sc[tl * h + hh] = p;
+        sum += p;
+      }
+      lrow[hh] = lrow[hh] * al + sum;
+      mrow[hh] = mx;
+      alpha[hh] = al;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kMaxOutPerThread; ++j) {
+      const int idx = threadIdx.x + j * kDecodeThreads;
+      if (idx >= h * dh) break;
+      const int hh = idx / dh, d = idx - hh * dh;
+      float o = acc[j] * alpha[hh];
+      for (int tl = 0; tl < kDecodeTile; ++tl) {
+        const int64_t t = tt0 + tl;
+        if (t >= t1) break;
+        const float p = sc[tl * h + hh];
+        for (int r = 0; r < a.rv; ++r)
+          o = fmaf(p * ldf(AV, ((seq0 + t) * h + hh) * a.rv + r), ldf(BV, ((seq0 + t) * a.rv + r) * dh + d), o);
+      }
+      acc[j] = o;
+    }
+    __syncthreads();
+  }
+
+  float* P = ws + ((b * n_chunks + c) * h) * (int64_t)(dh + 2);
+  for (int hh = threadIdx.x; hh < h; hh += blockDim.x) {
+    P[hh * (dh + 2)] = mrow[hh];
+    P[hh * (dh + 2) + 1] = lrow[hh];
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxOutPerThread; ++j) {
+    const int idx = threadIdx.x + j * kDecodeThreads;
+    if (idx >= h * dh) break;
+    const int hh = idx / dh, d = idx - hh * dh;
+    P[hh * (dh + 2) + 2 + d] = acc[j];
+  }
+}
+
+// Log-sum-exp merge of the chunk partials of one (head, sequence), in chunk
+// order; one workgroup per (head, sequence), threads over d.
+template <typename T>
+__global__ void __launch_bounds__(64) decode_combine_kernel(AttnArgs a, int64_t n_chunks, const float* ws) {
+  const int h = a.h, dh = a.d_h;
+  const int hh = blockIdx.x;
+  const int64_t b = blockIdx.y;
+  const float* P = ws + (b * n_chunks * h + hh) * (int64_t)(dh + 2);
+  const int64_t cstride = (int64_t)h * (dh + 2);
+  float M = -INFINITY;
+  for (int64_t c = 0; c < n_chunks; ++c) M = fmaxf(M, P[c * cstride]);
+  float L = 0.f;
+  for (int64_t c = 0; c < n_chunks; ++c) L = fmaf(fast_exp2(P[c * cstride] - M), P[c * cstride + 1], L);
+  const float scale = a.v_scale / L;
+  T* out = reinterpret_cast<T*>(a.out);
+  for (int d = threadIdx.x; d < dh; d += blockDim.x) {
+    float O = 0.f;
+    for (int64_t c = 0; c < n_chunks; ++c) O = fmaf(fast_exp2(P[c * cstride] - M), P[c * cstride + 2 + d], O);
+    stf(out, (b * h + hh) * dh + d, O * scale);
+  }
+}
+
+bool decode_mfma_supported(int dtype, const AttnArgs& a);
+int64_t decode_mfma_wave_tokens(const AttnArgs& a);
+hipError_t launch_decode_mfma(const AttnArgs& a, int64_t ctx_len, int64_t chunk, int64_t n_chunks, float* ws,
+                              hipStream_t st);
+
+static DecodePlan plan_generic(int64_t ctx_len) {
+  DecodePlan p;
+  p.kernel = 0;
+  p.chunk_tokens = 256;
+  p.n_chunks = (ctx_len + p.chunk_tokens - 1) / p.chunk_tokens;
+  return p;
+}
+
+// Matrix-core plan: chunks are whole multiples of the tokens one workgroup
+// covers per step (a value block per wave), sized so that about 512
+// workgroups hold full chunks (two per CU); the last chunk of each sequence
+// takes the remainder.
+static DecodePlan plan_mfma(const AttnArgs& a, int64_t ctx_len) {
+  DecodePlan p;
+  p.kernel = 1;
+  const int64_t vw = decode_mfma_wave_tokens(a);
+  const int64_t units = (ctx_len + vw - 1) / vw;
+  int64_t cu = (a.n_batch * units + 256) / 512;
+  if (cu < 1) cu = 1;
+  p.chunk_tokens = cu * vw;
+  p.n_chunks = (ctx_len + p.chunk_tokens - 1) / p.chunk_tokens;
+  return p;
+}
+
+DecodePlan plan_decode(int dtype, const AttnArgs& a, int64_t ctx_len) {
+  return decode_mfma_supported(dtype, a) ? plan_mfma(a, ctx_len) : plan_generic(ctx_len);
+}
+
+static size_t partial_bytes(const DecodePlan& p, const AttnArgs& a) {
+  return (size_t)a.n_batch * (size_t)p.n_chunks * (size_t)a.h * (size_t)(a.d_h + 2) * sizeof(float);
+}
+
+// Large enough for either plan, so the size does not depend on pointer alignment.
+size_t decode_workspace_bytes(const DecodePlan& p, const AttnArgs& a) {
+  (void)p;
+  const int64_t ctx_len = a.start_pos + 1;
+  size_t n = partial_bytes(plan_generic(ctx_len), a);
+  const size_t m = partial_bytes(plan_mfma(a, ctx_len), a);
+  return n > m ? n : m;
+}
+
+hipError_t launch_decode(int dtype, const AttnArgs& a, int64_t ctx_len, const DecodePlan& p, void* ws,
+                         hipStream_t st) {
+  float* wsf = reinterpret_cast<float*>(ws);
+  if (p.kernel == 1) {
+    hipError_t e = launch_decode_mfma(a, ctx_len, p.chunk_tokens, p.n_chunks, wsf, st);
+    if (e != hipSuccess) return e;
+  } else {
+    const size_t lds = sizeof(float) * ((size_t)a.h * a.d_h + (size_t)kDecodeTile * a.h + 3 * (size_t)a.h);
+    dim3 grid((unsigned)p.n_chunks, (unsigned)a.n_batch);
+    if (dtype == kF32)
+      hipLaunchKernelGGL(decode_generic_kernel<float>, grid, dim3(kDecodeThreads), lds, st, a, ctx_len,
+                         p.chunk_tokens, p.n_chunks, wsf);
+    else
+      hipLaunchKernelGGL(decode_generic_kernel<bf16_t>, grid, dim3(kDecodeThreads), lds, st, a, ctx_len,
+                         p.chunk_tokens, p.n_chunks, wsf);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 cgrid((unsigned)a.h, (unsigned)a.n_batch);
+  if (dtype == kF32)
+    hipLaunchKernelGGL(decode_combine_kernel<float>, cgrid, dim3(64), 0, st, a, p.n_chunks, wsf);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<bf16_t>, cgrid, dim3(64), 0, st, a, p.n_chunks, wsf);
+  return hipGetLastError();
+}
+
+}  // namespace tpa

@@ -1,0 +1,97 @@
+// Internal launch interface between the C ABI layer (tpa_api.cpp) and the HIP
+// kernels.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace tpa {
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+// ---- factor projection ------------------------------------------------------
+// F[M, N] = X[M, K] * W[N, K]^T, column n of F goes to segment e with
+// seg_begin[e] <= n < seg_begin[e+1]; row m = b*S + s lands at
+// dst[e] + b*bstride[e] + s*width[e] + (n - seg_begin[e]).  Columns below
+// rot_cols are rotated (pairs (2i, 2i+1) of each d_h-run) at start_pos + s.
+constexpr int kMaxSeg = 6;
+struct ProjArgs {
+  const void* x;
+  const void* w;
+  int64_t M, K, N;
+  int64_t S;
+  int64_t start_pos;
+  int32_t head_dim;
+  int32_t rot_cols;      // 0 when rotation is off
+  int32_t nseg;
+  int32_t seg_begin[kMaxSeg + 1];
+  int32_t width[kMaxSeg];
+  int64_t bstride[kMaxSeg];  // elements between sequences
+  void* dst[kMaxSeg];
+  RopeTable rope;
+};
+hipError_t launch_factor_proj(int dtype, const ProjArgs& a, hipStream_t st);
+
+// ---- standalone rotary embedding --------------------------------------------
+struct RopeArgs {
+  void* b;
+  int64_t n_tok;  // B*S
+  int64_t S;
+  int64_t start_pos;
+  int32_t rows;
+  int32_t head_dim;
+  RopeTable rope;
+};
+hipError_t launch_rope(int dtype, const RopeArgs& a, hipStream_t st);
+
+// ---- cache append -------------------------------------------------------------
+struct AppendArgs {
+  const void* src[4];
+  void* dst[4];
+  int64_t width_bytes[4];   // bytes per token
+  int64_t src_bstride[4];   // bytes between sequences in src
+  int64_t dst_bstride[4];   // bytes between sequences in the cache
+  int64_t n_batch, S;
+  int64_t start_pos;        // destination token offset
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+
+// ---- attention ---------------------------------------------------------------
+// Shared description of the query factors and the cache for both attention
+// kernels.  Strides are in elements.
+struct AttnArgs {
+  const void* a_q;       // [B, S, h, R_Q] (unused when rank_q == 0)
+  const void* b_q;       // [B, S, R_Q, d_h] or plain Q [B, S, h, d_h]
+  int64_t q_bstride_tok; // tokens between sequences of a_q/b_q
+  const void* c_ak;      // cache tensors, [max_batch, max_seq, ...]
+  const void* c_bk;
+  const void* c_av;
+  const void* c_bv;
+  int64_t max_seq;
+  int32_t h, d_h, rq, rk, rv;
+  int64_t n_batch;
+  int64_t S;             // queries per sequence (1 for decode)
+  int64_t start_pos;     // position of query 0
+  int32_t causal;
+  float q_scale;         // log2(e) / (R_Q * R_K * sqrt(d_h))  (R_Q -> 1 for plain Q)
+  float v_scale;         // 1 / R_V
+  void* out;
+};
+
+// Decode split: chunk_tokens keys per workgroup; partial results
+// (m, l, acc[d_h]) per (b, chunk, head) in float32, then a combine pass.
+struct DecodePlan {
+  int64_t chunk_tokens;
+  int64_t n_chunks;
+  int kernel;            // 0 = general VALU kernel, 1 = MFMA kernel
+};
+DecodePlan plan_decode(int dtype, const AttnArgs& a, int64_t ctx_len);
+size_t decode_workspace_bytes(const DecodePlan& p, const AttnArgs& a);
+hipError_t launch_decode(int dtype, const AttnArgs& a, int64_t ctx_len, const DecodePlan& p, void* ws,
+                         hipStream_t st);
+
+hipError_t launch_prefill(int dtype, const AttnArgs& a, hipStream_t st);
+
+}  // namespace tpa

@@ -1,0 +1,157 @@
+// Prefill attention over the factor cache (causal or full), general kernel.
+//
+// Per (query block, head, sequence): the query block is formed from its
+// factors, and for every key block the keys and values of this head are
+// rebuilt from the cached factors in LDS, k_t = sum_r A_K[t,h,r] B~_K[t,r,:]
+// (the 1/R_K is folded into the query scale, 1/R_V into the output), followed
+// by an online softmax in base 2.  ("Tensor Product Attention Is All You
+// Need" review on coreui.cn: the Q_t/K_t/V_t equations of 核心机制总结 and the
+// masked softmax attention of the code walk-through 前向传播; the attention
+// formula of the jieyibu.net explainer, section Ⅱ.1.)
+#include "kernels.h"
+
+namespace tpa {
+
+constexpr int kPrefillThreads = 256;
+
+template <typename T>
+__device__ __forceinline__ float rebuild(const T* A, const T* Bm, int64_t tok, int hh, int h, int R, int dh, int d) {
+  float v = 0.f;
+  for (int r = 0; r < R; ++r) v = fmaf(ldf(A, (tok * h + hh) * R + r), ldf(Bm, (tok * R + r) * dh + d), v);
+  return v;
+}
+
+template <typename T, int BM, int BN>
+__global__ void __launch_bounds__(kPrefillThreads) prefill_generic_kernel(AttnArgs a) {
+  extern __shared__ float smem[];
+  constexpr int kOut = 16;  // BM * d_h / threads, at most (BM=32,d_h=128 or BM=16,d_h=256)
+  const int h = a.h, dh = a.d_h;
+  float* qs = smem;              // [BM][d_h]
+  float* ks = qs + BM * dh;      // [BN][d_h]
+  float* vs = ks + BN * dh;      // [BN][d_h]
+  float* ss = vs + BN * dh;      // [BM][BN]
+  float* mrow = ss + BM * BN;    // [BM]
+  float* lrow = mrow + BM;       // [BM]
+  float* alpha = lrow + BM;      // [BM]
+  const int64_t q0 = (int64_t)blockIdx.x * BM;
+  const int hh = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const T* AQ = reinterpret_cast<const T*>(a.a_q);
+  const T* BQ = reinterpret_cast<const T*>(a.b_q);
+  const T* AK = reinterpret_cast<const T*>(a.c_ak);
+  const T* BK = reinterpret_cast<const T*>(a.c_bk);
+  const T* AV = reinterpret_cast<const T*>(a.c_av);
+  const T* BV = reinterpret_cast<const T*>(a.c_bv);
+  const int64_t seq0 = b * a.max_seq;
+
+  for (int idx = threadIdx.x; idx < BM * dh; idx += blockDim.x) {
+    const int i = idx / dh, d = idx - i * dh;
+    const int64_t s = q0 + i;
+    float v = 0.f;
+    if (s < a.S) {
+      const int64_t tok = b * a.q_bstride_tok + s;
+      v = (a.rq == 0) ? ldf(BQ, (tok * h + hh) * dh + d) : rebuild(AQ, BQ, tok, hh, h, a.rq, dh, d);
+    }
+    qs[idx] = v * a.q_scale;
+  }
+  for (int i = threadIdx.x; i < BM; i += blockDim.x) {
+    mrow[i] = -INFINITY;
+    lrow[i] = 0.f;
+  }
+  float acc[kOut];
+#pragma unroll
+  for (int j = 0; j < kOut; ++j) acc[j] = 0.f;
+  __syncthreads();
+
+  const int64_t n_keys = a.start_pos + a.S;
+  const int64_t last_q = (q0 + BM < a.S ? q0 + BM : a.S) - 1;
+  const int64_t kend = a.causal ? a.start_pos + last_q + 1 : n_keys;
+
+  for (int64_t k0 = 0; k0 < kend; k0 += BN) {
+    for (int idx = threadIdx.x; idx < BN * dh; idx += blockDim.x) {
+      const int j = idx / dh, d = idx - j * dh;
+      const int64_t t = k0 + j;
+      float kv = 0.f, vv = 0.f;
+      if (t < kend) {
+        kv = rebuild(AK, BK, seq0 + t, hh, h, a.rk, dh, d);
+        vv = rebuild(AV, BV, seq0 + t, hh, h, a.rv, dh, d);
+      }
+      ks[idx] = kv;
+      vs[idx] = vv;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < BM * BN; idx += blockDim.x) {
+      const int i = idx / BN, j = idx - i * BN;
+      const int64_t t = k0 + j;
+      const bool ok = t < kend && (!a.causal || t <= a.start_pos + q0 + i);
+      float s = -INFINITY;
+      if (ok) {
+        s = 0.f;
+        for (int d = 0; d < dh; ++d) s = fmaf(qs[i * dh + d], ks[j * dh + d], s);
+      }
+      ss[idx] = s;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < BM; i += blockDim.x) {
+      float mx = mrow[i];
+      for (int j = 0; j < BN; ++j) mx = fmaxf(mx, ss[i * BN + j]);
+      float al = 1.f, sum = 0.f;
+      if (mx != -INFINITY) {
+        al = fast_exp2(mrow[i] - mx);
+        for (int j = 0; j < BN; ++j) {
+          const float p = fast_exp2(ss[i * BN + j] - mx);
+          ss[i * BN + j] = p;
+          sum += p;
+        }
+      } else {
+        for (int j = 0; j < BN; ++j) ss[i * BN + j] = 0.f;
+      }
+      lrow[i] = lrow[i] * al + sum;
+      mrow[i] = mx;
+      alpha[i] = al;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int jo = 0; jo < kOut; ++jo) {
+      const int idx = threadIdx.x + jo * kPrefillThreads;
+      if (idx >= BM * dh) break;
+      const int i = idx / dh, d = idx - i * dh;
+      float o = acc[jo] * alpha[i];
+      for (int j = 0; j < BN; ++j) o = fmaf(ss[i * BN + j], vs[j * dh + d], o);
+      acc[jo] = o;
+    }
+    __syncthreads();
+  }
+
+  T* out = reinterpret_cast<T*>(a.out);
+#pragma unroll
+  for (int jo = 0; jo < kOut; ++jo) {
+    const int idx = threadIdx.x + jo * kPrefillThreads;
+    if (idx >= BM * dh) break;
+    const int i = idx / dh, d = idx - i * dh;
+    const int64_t s = q0 + i;
+    if (s < a.S) stf(out, ((b * a.S + s) * h + hh) * (int64_t)dh + d, acc[jo] / lrow[i] * a.v_scale);
+  }
+}
+
+template <typename T>
+static hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t st) {
+  if (a.d_h <= 128) {
+    constexpr int BM = 32, BN = 32;
+    const size_t lds = sizeof(float) * ((size_t)(BM + 2 * BN) * a.d_h + BM * BN + 3 * BM);
+    dim3 grid((unsigned)((a.S + BM - 1) / BM), (unsigned)a.h, (unsigned)a.n_batch);
+    hipLaunchKernelGGL((prefill_generic_kernel<T, BM, BN>), grid, dim3(kPrefillThreads), lds, st, a);
+  } else {
+    constexpr int BM = 16, BN = 16;
+    const size_t lds = sizeof(float) * ((size_t)(BM + 2 * BN) * a.d_h + BM * BN + 3 * BM);
+    dim3 grid((unsigned)((a.S + BM - 1) / BM), (unsigned)a.h, (unsigned)a.n_batch);
+    hipLaunchKernelGGL((prefill_generic_kernel<T, BM, BN>), grid, dim3(kPrefillThreads), lds, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
+  return dtype == kF32 ? launch_prefill_t<float>(a, st) : launch_prefill_t<bf16_t>(a, st);
+}
+
+}  // namespace tpa

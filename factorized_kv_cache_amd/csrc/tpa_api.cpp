@@ -1,0 +1,335 @@
+// libtpa C ABI: argument validation and dispatch to the HIP kernels.
+//
+// Every entry point checks all of its arguments before it enqueues anything;
+// on failure it returns a status and records a message for tpa_last_error()
+// in thread-local storage (the library's only state).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/tpa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[320] = "";
+
+tpa_status fail(tpa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+tpa_status ok() {
+  g_err[0] = '\0';
+  return TPA_OK;
+}
+
+tpa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TPA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 31;
+
+tpa_status check_dims(const tpa_dims* d) {
+  if (!d) return fail(TPA_ERR_INVALID_ARGUMENT, "dims is NULL");
+  if (d->d_model < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "d_model must be >= 1 (got %d)", d->d_model);
+  if (d->n_heads < 1 || d->n_heads > 256)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "n_heads must be in 1..256 (got %d)", d->n_heads);
+  if (d->head_dim < 2 || d->head_dim > 256 || (d->head_dim & 1))
+    return fail(TPA_ERR_INVALID_ARGUMENT, "head_dim must be even and in 2..256 (got %d)", d->head_dim);
+  if (d->rank_q < 0 || d->rank_q > 64)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "rank_q must be in 0..64 (got %d)", d->rank_q);
+  if (d->rank_k < 1 || d->rank_k > 64)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "rank_k must be in 1..64 (got %d)", d->rank_k);
+  if (d->rank_v < 1 || d->rank_v > 64)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "rank_v must be in 1..64 (got %d)", d->rank_v);
+  if (!(d->rope_base > 0.0) || !isfinite(d->rope_base))
+    return fail(TPA_ERR_INVALID_ARGUMENT, "rope_base must be finite and > 0");
+  if (d->dtype != TPA_F32 && d->dtype != TPA_BF16)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "unknown dtype %d", d->dtype);
+  if ((int64_t)d->n_heads * d->head_dim > 8192)
+    return fail(TPA_ERR_UNSUPPORTED, "n_heads * head_dim must be <= 8192 (got %lld)",
+                (long long)d->n_heads * d->head_dim);
+  return TPA_OK;
+}
+
+size_t elem_size(const tpa_dims* d) { return d->dtype == TPA_F32 ? 4 : 2; }
+
+tpa::RopeTable rope_table(const tpa_dims* d) {
+  tpa::RopeTable t;
+  memset(&t, 0, sizeof(t));
+  const int half = d->head_dim / 2;
+  for (int i = 0; i < half; ++i)
+    t.rev[i] = pow(d->rope_base, -2.0 * (double)i / (double)d->head_dim) / (2.0 * M_PI);
+  return t;
+}
+
+tpa_status check_cache(const tpa_cache* c) {
+  if (!c) return fail(TPA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (!c->a_k || !c->b_k || !c->a_v || !c->b_v) return fail(TPA_ERR_INVALID_ARGUMENT, "a cache tensor is NULL");
+  if (c->max_batch < 1 || c->max_seq < 1)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "cache capacity must be at least 1 x 1");
+  if (c->max_seq >= kMaxTokens) return fail(TPA_ERR_UNSUPPORTED, "max_seq must be < 2^31");
+  return TPA_OK;
+}
+
+tpa_status check_query(const tpa_dims* d, const tpa_factors* q) {
+  if (!q) return fail(TPA_ERR_INVALID_ARGUMENT, "query factors are NULL");
+  if (!q->b_q) return fail(TPA_ERR_INVALID_ARGUMENT, "b_q (or plain Q) is NULL");
+  if (d->rank_q > 0 && !q->a_q) return fail(TPA_ERR_INVALID_ARGUMENT, "a_q is NULL");
+  return TPA_OK;
+}
+
+tpa_status resolve_stride(int64_t given, int64_t seq_len, const char* name, int64_t* out) {
+  if (given == 0) {
+    *out = seq_len;
+    return TPA_OK;
+  }
+  if (given < seq_len) return fail(TPA_ERR_INVALID_ARGUMENT, "%s (%lld) is below seq_len (%lld)", name,
+                                   (long long)given, (long long)seq_len);
+  *out = given;
+  return TPA_OK;
+}
+
+tpa::AttnArgs attn_args(const tpa_dims* d, const tpa_factors* q, int64_t q_stride, const tpa_cache* c,
+                        int64_t n_batch, int64_t seq_len, int64_t start_pos, int causal, void* out) {
+  tpa::AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.a_q = q->a_q;
+  a.b_q = q->b_q;
+  a.q_bstride_tok = q_stride;
+  a.c_ak = c->a_k;
+  a.c_bk = c->b_k;
+  a.c_av = c->a_v;
+  a.c_bv = c->b_v;
+  a.max_seq = c->max_seq;
+  a.h = d->n_heads;
+  a.d_h = d->head_dim;
+  a.rq = d->rank_q;
+  a.rk = d->rank_k;
+  a.rv = d->rank_v;
+  a.n_batch = n_batch;
+  a.S = seq_len;
+  a.start_pos = start_pos;
+  a.causal = causal ? 1 : 0;
+  const double rq = d->rank_q > 0 ? (double)d->rank_q : 1.0;
+  a.q_scale = (float)(1.4426950408889634 / (rq * (double)d->rank_k * sqrt((double)d->head_dim)));
+  a.v_scale = (float)(1.0 / (double)d->rank_v);
+  a.out = out;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t tpa_packed_weight_rows(const tpa_dims* d) {
+  if (check_dims(d) != TPA_OK) return -1;
+  const int64_t h = d->n_heads, dh = d->head_dim;
+  const int64_t q = d->rank_q > 0 ? h * d->rank_q + d->rank_q * dh : h * dh;
+  return q + (h + dh) * ((int64_t)d->rank_k + d->rank_v);
+}
+
+int64_t tpa_cache_elems_per_token(const tpa_dims* d) {
+  if (check_dims(d) != TPA_OK) return -1;
+  return ((int64_t)d->n_heads + d->head_dim) * ((int64_t)d->rank_k + d->rank_v);
+}
+
+tpa_status tpa_factor_proj(const tpa_dims* d, const void* x, int64_t n_batch, int64_t seq_len, int64_t start_pos,
+                           const void* w_packed, int32_t fuse_rope, const tpa_factors* out, void* stream) {
+  tpa_status st = check_dims(d);
+  if (st != TPA_OK) return st;
+  if (!x || !w_packed) return fail(TPA_ERR_INVALID_ARGUMENT, "x or w_packed is NULL");
+  if (!out) return fail(TPA_ERR_INVALID_ARGUMENT, "out factors are NULL");
+  if ((st = check_query(d, out)) != TPA_OK) return st;
+  if (!out->a_k || !out->b_k || !out->a_v || !out->b_v)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "a key/value output tensor is NULL");
+  if (n_batch < 1 || seq_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and seq_len must be >= 1");
+  if (n_batch >= kMaxTokens || seq_len >= kMaxTokens || n_batch * seq_len >= kMaxTokens)
+    return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
+  if (start_pos < 0 || start_pos + seq_len >= kMaxTokens)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos must be in 0 .. 2^31 - seq_len");
+  int64_t qs, kvs;
+  if ((st = resolve_stride(out->q_batch_stride, seq_len, "q_batch_stride", &qs)) != TPA_OK) return st;
+  if ((st = resolve_stride(out->kv_batch_stride, seq_len, "kv_batch_stride", &kvs)) != TPA_OK) return st;
+
+  tpa::ProjArgs a;
+  memset(&a, 0, sizeof(a));
+  const int32_t h = d->n_heads, dh = d->head_dim;
+  a.x = x;
+  a.w = w_packed;
+  a.M = n_batch * seq_len;
+  a.K = d->d_model;
+  a.N = tpa_packed_weight_rows(d);
+  a.S = seq_len;
+  a.start_pos = start_pos;
+  a.head_dim = dh;
+  struct Seg {
+    int32_t width;
+    void* p;
+    int64_t stride;
+  } segs[6];
+  int n = 0;
+  if (d->rank_q > 0) {
+    segs[n++] = {d->rank_q * dh, out->b_q, qs};
+  } else {
+    segs[n++] = {h * dh, out->b_q, qs};
+  }
+  segs[n++] = {d->rank_k * dh, out->b_k, kvs};
+  segs[n++] = {d->rank_v * dh, out->b_v, kvs};
+  if (d->rank_q > 0) segs[n++] = {h * d->rank_q, out->a_q, qs};
+  segs[n++] = {h * d->rank_k, out->a_k, kvs};
+  segs[n++] = {h * d->rank_v, out->a_v, kvs};
+  a.nseg = n;
+  int32_t col = 0;
+  for (int e = 0; e < n; ++e) {
+    a.seg_begin[e] = col;
+    a.width[e] = segs[e].width;
+    a.dst[e] = segs[e].p;
+    a.bstride[e] = segs[e].stride * segs[e].width;
+    col += segs[e].width;
+  }
+  a.seg_begin[n] = col;
+  a.rot_cols = fuse_rope ? (segs[0].width + segs[1].width) : 0;
+  a.rope = rope_table(d);
+  return hip_status(tpa::launch_factor_proj(d->dtype, a, (hipStream_t)stream), "tpa_factor_proj");
+}
+
+tpa_status tpa_rope_b(const tpa_dims* d, void* b, int64_t n_batch, int64_t seq_len, int32_t rows, int64_t start_pos,
+                      void* stream) {
+  tpa_status st = check_dims(d);
+  if (st != TPA_OK) return st;
+  if (!b) return fail(TPA_ERR_INVALID_ARGUMENT, "b is NULL");
+  if (n_batch < 1 || seq_len < 1 || rows < 1)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch, seq_len and rows must be >= 1");
+  if (n_batch * seq_len >= kMaxTokens) return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
+  if (start_pos < 0 || start_pos + seq_len >= kMaxTokens)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos must be in 0 .. 2^31 - seq_len");
+  tpa::RopeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.b = b;
+  a.n_tok = n_batch * seq_len;
+  a.S = seq_len;
+  a.start_pos = start_pos;
+  a.rows = rows;
+  a.head_dim = d->head_dim;
+  a.rope = rope_table(d);
+  return hip_status(tpa::launch_rope(d->dtype, a, (hipStream_t)stream), "tpa_rope_b");
+}
+
+tpa_status tpa_cache_append(const tpa_dims* d, const tpa_cache* c, const tpa_factors* kv, int64_t n_batch,
+                            int64_t seq_len, int64_t start_pos, void* stream) {
+  tpa_status st = check_dims(d);
+  if (st != TPA_OK) return st;
+  if ((st = check_cache(c)) != TPA_OK) return st;
+  if (!kv || !kv->a_k || !kv->b_k || !kv->a_v || !kv->b_v)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "a key/value factor tensor is NULL");
+  if (n_batch < 1 || seq_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and seq_len must be >= 1");
+  if (start_pos < 0) return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos must be >= 0");
+  if (n_batch > c->max_batch)
+    return fail(TPA_ERR_CAPACITY, "n_batch %lld exceeds max_batch %lld", (long long)n_batch,
+                (long long)c->max_batch);
+  if (seq_len > c->max_seq || start_pos > c->max_seq - seq_len)
+    return fail(TPA_ERR_CAPACITY, "start_pos + seq_len (%lld) exceeds max_seq %lld",
+                (long long)(start_pos + seq_len), (long long)c->max_seq);
+  int64_t kvs;
+  if ((st = resolve_stride(kv->kv_batch_stride, seq_len, "kv_batch_stride", &kvs)) != TPA_OK) return st;
+  const int64_t es = (int64_t)elem_size(d);
+  const int64_t h = d->n_heads, dh = d->head_dim;
+  const int64_t width[4] = {h * d->rank_k * es, d->rank_k * dh * es, h * d->rank_v * es, d->rank_v * dh * es};
+  const void* src[4] = {kv->a_k, kv->b_k, kv->a_v, kv->b_v};
+  void* dst[4] = {c->a_k, c->b_k, c->a_v, c->b_v};
+  tpa::AppendArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int t = 0; t < 4; ++t) {
+    a.src[t] = src[t];
+    a.dst[t] = dst[t];
+    a.width_bytes[t] = width[t];
+    a.src_bstride[t] = kvs * width[t];
+    a.dst_bstride[t] = c->max_seq * width[t];
+  }
+  a.n_batch = n_batch;
+  a.S = seq_len;
+  a.start_pos = start_pos;
+  return hip_status(tpa::launch_append(a, (hipStream_t)stream), "tpa_cache_append");
+}
+
+tpa_status tpa_prefill_attn(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
+                            int64_t seq_len, int64_t start_pos, int32_t causal, void* out, void* stream) {
+  tpa_status st = check_dims(d);
+  if (st != TPA_OK) return st;
+  if ((st = check_query(d, q)) != TPA_OK) return st;
+  if ((st = check_cache(c)) != TPA_OK) return st;
+  if (!out) return fail(TPA_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (n_batch < 1 || seq_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and seq_len must be >= 1");
+  if (n_batch > 65535) return fail(TPA_ERR_UNSUPPORTED, "n_batch must be <= 65535");
+  if (start_pos < 0) return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos must be >= 0");
+  if (n_batch > c->max_batch)
+    return fail(TPA_ERR_CAPACITY, "n_batch %lld exceeds max_batch %lld", (long long)n_batch,
+                (long long)c->max_batch);
+  if (seq_len > c->max_seq || start_pos > c->max_seq - seq_len)
+    return fail(TPA_ERR_CAPACITY, "start_pos + seq_len (%lld) exceeds max_seq %lld",
+                (long long)(start_pos + seq_len), (long long)c->max_seq);
+  int64_t qs;
+  if ((st = resolve_stride(q->q_batch_stride, seq_len, "q_batch_stride", &qs)) != TPA_OK) return st;
+  tpa::AttnArgs a = attn_args(d, q, qs, c, n_batch, seq_len, start_pos, causal, out);
+  return hip_status(tpa::launch_prefill(d->dtype, a, (hipStream_t)stream), "tpa_prefill_attn");
+}
+
+size_t tpa_decode_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t ctx_len) {
+  if (check_dims(d) != TPA_OK || n_batch < 1 || ctx_len < 1) return 0;
+  tpa_factors q;
+  memset(&q, 0, sizeof(q));
+  tpa_cache c;
+  memset(&c, 0, sizeof(c));
+  c.max_seq = ctx_len;
+  tpa::AttnArgs a = attn_args(d, &q, 1, &c, n_batch, 1, ctx_len - 1, 1, nullptr);
+  return tpa::decode_workspace_bytes(tpa::plan_decode(d->dtype, a, ctx_len), a);
+}
+
+tpa_status tpa_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
+                           int64_t ctx_len, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  tpa_status st = check_dims(d);
+  if (st != TPA_OK) return st;
+  if ((st = check_query(d, q)) != TPA_OK) return st;
+  if ((st = check_cache(c)) != TPA_OK) return st;
+  if (!out) return fail(TPA_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (n_batch < 1 || ctx_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and ctx_len must be >= 1");
+  if (n_batch > 65535) return fail(TPA_ERR_UNSUPPORTED, "n_batch must be <= 65535");
+  if (n_batch > c->max_batch)
+    return fail(TPA_ERR_CAPACITY, "n_batch %lld exceeds max_batch %lld", (long long)n_batch,
+                (long long)c->max_batch);
+  if (ctx_len > c->max_seq)
+    return fail(TPA_ERR_CAPACITY, "ctx_len %lld exceeds max_seq %lld", (long long)ctx_len, (long long)c->max_seq);
+  int64_t qs;
+  if ((st = resolve_stride(q->q_batch_stride, 1, "q_batch_stride", &qs)) != TPA_OK) return st;
+  tpa::AttnArgs a = attn_args(d, q, qs, c, n_batch, 1, ctx_len - 1, 1, out);
+  const tpa::DecodePlan p = tpa::plan_decode(d->dtype, a, ctx_len);
+  const size_t need = tpa::decode_workspace_bytes(p, a);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(TPA_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
+                workspace ? "" : ", NULL");
+  return hip_status(tpa::launch_decode(d->dtype, a, ctx_len, p, workspace, (hipStream_t)stream),
+                    "tpa_decode_attn");
+}
+
+const char* tpa_status_string(tpa_status s) {
+  switch (s) {
+    case TPA_OK: return "ok";
+    case TPA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case TPA_ERR_UNSUPPORTED: return "unsupported";
+    case TPA_ERR_CAPACITY: return "cache capacity exceeded";
+    case TPA_ERR_WORKSPACE: return "workspace too small";
+    case TPA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* tpa_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+/*
+ * tpa.h - C ABI of libtpa: Tensor Product Attention (TPA) with a factorised KV
+ * cache, for AMD Instinct MI355X (gfx950).
+ *
+ * TPA writes each token's per-head query, key and value ([h, d_h] each) as a
+ * 1/R-scaled sum of R outer products of a head factor a_r(x_t) (length h) and a
+ * dim factor b_r(x_t) (length d_h); only the key/value factors are cached, and
+ * the key dim factors are rotated (RoPE) before they are cached.
+ *   Definitions: "Tensor Product Attention Is All You Need" review on
+ *   coreui.cn, section 核心机制总结 item 3 (equations for Q_t, K_t, V_t),
+ *   关键问题及回答 question 2 (pre-rotation B~_K <- RoPE_t(B_K)), and its code
+ *   walk-through (类定义与初始化: projection layers and cache shapes;
+ *   前向传播: projections, cache write/read by start_pos, reconstruction,
+ *   softmax attention).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Memory: every data pointer is device memory owned by the caller.  The
+ *   library allocates nothing and keeps no state between calls except a
+ *   thread-local error message.  Pointers must be aligned to the element size;
+ *   16-byte alignment (and the shape limits of each call) selects the fast
+ *   kernels, anything else runs a general kernel with the same results
+ *   up to rounding order.
+ * - Element type: dims->dtype is TPA_F32 (float) or TPA_BF16 (bfloat16, stored
+ *   as 16-bit words).  All tensors of a call use it.  Arithmetic is float32;
+ *   bf16 results are rounded to nearest even.
+ * - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  Every call only enqueues work and returns; ordering between
+ *   calls is the caller's, through the stream.
+ * - Errors: arguments are checked before anything is enqueued.  A non-zero
+ *   status means nothing was launched; tpa_last_error() then describes why.
+ *   TPA_ERR_HIP reports a failed launch (the work before it in the same call
+ *   may have run).
+ * - Positions are zero-based.  Token s of a block that starts at start_pos
+ *   sits at position start_pos + s, in every sequence of the batch.
+ * - Rotary embedding: element pairs (2i, 2i+1) of a d_h-vector are turned by the
+ *   angle pos * rope_base^(-2i/d_h), i < d_h/2; the angle is formed and reduced
+ *   in float64.
+ *
+ * Layouts (all row-major, token-major; "B" is the batch, "S" the block length)
+ * --------------------------------------------------------------------------
+ *   x         [B, S, d_model]
+ *   w_packed  [n_out, d_model]: the six nn.Linear weights stacked by rows in
+ *             the order W_B_q, W_B_k, W_B_v, W_A_q, W_A_k, W_A_v
+ *             (TPA-KVonly, rank_q == 0: W_Q, W_B_k, W_B_v, W_A_k, W_A_v).
+ *             The rotated columns come first, so they are pair-aligned.
+ *   a_q [B,S,h,R_Q]  b_q [B,S,R_Q,d_h]   (KV-only: b_q holds Q [B,S,h,d_h], a_q unused)
+ *   a_k [B,S,h,R_K]  b_k [B,S,R_K,d_h]  a_v [B,S,h,R_V]  b_v [B,S,R_V,d_h]
+ *   cache     a_k [max_batch, max_seq, h, R_K], b_k [max_batch, max_seq, R_K, d_h],
+ *             a_v [max_batch, max_seq, h, R_V], b_v [max_batch, max_seq, R_V, d_h]
+ *             (the page's cache_kA, cache_kB, cache_vA, cache_vB).
+ *   out       prefill [B, S, h*d_h]; decode [B, h*d_h] (head-major per token).
+ */
+#ifndef TPA_H
+#define TPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TPA_OK = 0,
+  TPA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, odd head_dim, ... */
+  TPA_ERR_UNSUPPORTED = 2,      /* valid TPA, but outside what this library runs */
+  TPA_ERR_CAPACITY = 3,         /* batch or positions beyond the cache */
+  TPA_ERR_WORKSPACE = 4,        /* decode workspace missing or too small */
+  TPA_ERR_HIP = 5               /* a HIP launch failed */
+} tpa_status;
+
+typedef enum { TPA_F32 = 0, TPA_BF16 = 1 } tpa_dtype;
+
+/* One layer's dimensions (the page's ModelArgs: dim, n_heads, head_dim, q_rank,
+ * rank; key and value ranks are separate, as in its K_t and V_t equations).
+ * Limits: d_model >= 1; 1 <= n_heads <= 256; head_dim even, 2..256;
+ * rank_k, rank_v in 1..64; rank_q in 0..64, 0 selecting TPA-KVonly (Q is a
+ * plain per-head projection, rotated like the key factors). */
+typedef struct {
+  int32_t d_model;
+  int32_t n_heads;   /* h */
+  int32_t head_dim;  /* d_h */
+  int32_t rank_q;    /* R_Q, or 0 for TPA-KVonly */
+  int32_t rank_k;    /* R_K */
+  int32_t rank_v;    /* R_V */
+  double rope_base;  /* > 1, e.g. 10000 */
+  int32_t dtype;     /* tpa_dtype */
+} tpa_dims;
+
+/* The factor cache: four caller-owned tensors with capacity
+ * [max_batch, max_seq] tokens (layouts above). */
+typedef struct {
+  void* a_k;
+  void* b_k;
+  void* a_v;
+  void* b_v;
+  int64_t max_batch;
+  int64_t max_seq;
+} tpa_cache;
+
+/* A block of factors for B sequences of S tokens (layouts above).
+ * q_batch_stride / kv_batch_stride: tokens between consecutive sequences of
+ * the query tensors (a_q, b_q) and of the key/value tensors; 0 means S (dense).
+ * A kv_batch_stride of max_seq with a_k..b_v pointing at cache slot start_pos
+ * lets tpa_factor_proj write straight into the cache. */
+typedef struct {
+  void* a_q;
+  void* b_q;
+  void* a_k;
+  void* b_k;
+  void* a_v;
+  void* b_v;
+  int64_t q_batch_stride;
+  int64_t kv_batch_stride;
+} tpa_factors;
+
+/* Number of rows n_out of the packed projection weight:
+ * h*R_Q + R_Q*d_h + h*R_K + R_K*d_h + h*R_V + R_V*d_h (KV-only: h*d_h instead of
+ * the query terms).  Returns -1 for invalid dims. */
+int64_t tpa_packed_weight_rows(const tpa_dims* dims);
+
+/* Cached elements per token, h*(R_K+R_V) + d_h*(R_K+R_V); -1 for invalid dims. */
+int64_t tpa_cache_elems_per_token(const tpa_dims* dims);
+
+/* Factor projection: F = x * w_packed^T for all B*S tokens, split into the six
+ * factor tensors of `out` (KV-only: five).  With fuse_rope != 0 the query and
+ * key dim factors (KV-only: Q) are rotated at positions start_pos + s before
+ * they are stored; with fuse_rope == 0 they are stored unrotated and
+ * start_pos is ignored.
+ *   Passage: the A and B projections of the code walk-through (前向传播),
+ *   a^X(x_t) = W_A_X x_t viewed [h, R_X], b^X(x_t) = W_B_X x_t viewed [R_X, d_h];
+ *   the pre-rotation of question 2.
+ * x [B,S,d_model], w_packed [n_out, d_model]; out->* as in the layouts above
+ * (a_q ignored for KV-only).  Errors: any null tensor, B or S < 1 (B*S must fit
+ * in 2^31 tokens), start_pos < 0. */
+tpa_status tpa_factor_proj(const tpa_dims* dims, const void* x, int64_t n_batch, int64_t seq_len,
+                           int64_t start_pos, const void* w_packed, int32_t fuse_rope,
+                           const tpa_factors* out, void* stream);
+
+/* In-place rotary embedding of `rows` d_h-vectors per token:
+ * b [B, S, rows, d_h], token s at position start_pos + s.  Used standalone for
+ * factors projected with fuse_rope == 0 (rows = R_Q, R_K, or h for plain Q).
+ *   Passage: question 2's B~_K <- RoPE_t(B_K); the code walk-through rotates
+ *   q and k, which equals rotating every query and key dim factor.
+ * Errors: null b, B, S or rows < 1, start_pos < 0. */
+tpa_status tpa_rope_b(const tpa_dims* dims, void* b, int64_t n_batch, int64_t seq_len, int32_t rows,
+                      int64_t start_pos, void* stream);
+
+/* Cache append: cache[b, start_pos + s] = kv[b, s] for the four K/V factor
+ * tensors, bit for bit.  kv->a_q / b_q are ignored.
+ *   Passage: the cache writes of the code walk-through (前向传播),
+ *   cache[:bsz, start_pos:start_pos+seqlen] = factor.
+ * Errors: null pointers; n_batch > max_batch or start_pos + S > max_seq
+ * (TPA_ERR_CAPACITY). */
+tpa_status tpa_cache_append(const tpa_dims* dims, const tpa_cache* cache, const tpa_factors* kv,
+                            int64_t n_batch, int64_t seq_len, int64_t start_pos, void* stream);
+
+/* Prefill attention for S query tokens per sequence at positions
+ * start_pos .. start_pos+S-1, over the cached keys/values 0 .. start_pos+S-1
+ * (the caller appends this block's K/V factors first):
+ *   q_{s,h} = (1/R_Q) sum_r a_q[s,h,r] b_q[s,r,:]   (KV-only: b_q[s,h,:])
+ *   k_{t,h} = (1/R_K) sum_r a_k[t,h,r] b_k[t,r,:],  v likewise with R_V,
+ *   out[s, h*d_h:(h+1)*d_h] = sum_t softmax_t(q.k_t / sqrt(d_h)) v_t,
+ * where with causal != 0 key t is visible iff t <= start_pos + s, else every
+ * cached key is.  K and V are never written to memory.
+ *   Passage: the Q_t/K_t/V_t equations; scaled dot-product attention
+ *   (jieyibu.net explainer, section Ⅱ.1; code walk-through, 前向传播).
+ * q: factors of this block (q_batch_stride applies); out [B, S, h*d_h].
+ * Errors: null pointers, B > max_batch or start_pos + S > max_seq. */
+tpa_status tpa_prefill_attn(const tpa_dims* dims, const tpa_factors* q, const tpa_cache* cache,
+                            int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
+                            void* stream);
+
+/* Bytes of device workspace tpa_decode_attn needs for this batch and context. */
+size_t tpa_decode_workspace_bytes(const tpa_dims* dims, int64_t n_batch, int64_t ctx_len);
+
+/* Decode attention: one new query per sequence at position ctx_len - 1 over the
+ * cached keys/values 0 .. ctx_len - 1 (the new token's factors must already be
+ * in the cache).  Same arithmetic as tpa_prefill_attn with S = 1, computed as a
+ * split over the context with a log-sum-exp combine in a fixed order, so
+ * repeated calls give bit-identical results.  Scores use the factored form
+ * s_t = (1/R_K) sum_r a_k[t,h,r] (b_k[t,r,:] . q_h) / sqrt(d_h).
+ *   Passage: as tpa_prefill_attn; the pre-rotated cache needs no rotation at
+ *   decode time (question 2).
+ * q: the new token's query factors, a_q [B,h,R_Q], b_q [B,R_Q,d_h]
+ * (KV-only: b_q = Q [B,h,d_h]); out [B, h*d_h].
+ * workspace: device memory of at least tpa_decode_workspace_bytes(dims, B,
+ * ctx_len) bytes, zero-filled before its first use with this library; every
+ * call leaves it ready for the next one.  Calls that may run at the same time
+ * must not share a workspace.
+ * Errors: null pointers, ctx_len < 1, B > max_batch or ctx_len > max_seq
+ * (TPA_ERR_CAPACITY), workspace too small (TPA_ERR_WORKSPACE). */
+tpa_status tpa_decode_attn(const tpa_dims* dims, const tpa_factors* q, const tpa_cache* cache,
+                           int64_t n_batch, int64_t ctx_len, void* out, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/* Static text for a status code. */
+const char* tpa_status_string(tpa_status status);
+
+/* Description of the last error returned on the calling thread ("" if none). */
+const char* tpa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPA_H */

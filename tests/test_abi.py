@@ -1,0 +1,161 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/tpa.h declares, and rejects bad arguments before it launches anything.
+
+No call here reaches a kernel launch: every call is built to fail validation.
+Device pointers are dummy non-null addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from factorized_kv_cache_amd import tpa as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpa.h")
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+OK, INVALID, UNSUPPORTED, CAPACITY, WORKSPACE = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tpa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_functions_are_exported():
+    lib = ctypes.CDLL(T.library_path())
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in tpa.h but not exported"
+    assert sorted(T.EXPORTED) == names
+
+
+def dims(**kw):
+    base = dict(d_model=1024, n_heads=16, head_dim=64, rank_q=6, rank_k=2, rank_v=2, rope_base=10000.0, dtype=1)
+    base.update(kw)
+    return T.tpa_dims(**base)
+
+
+@pytest.mark.parametrize("kw,n_out,elems", [
+    (dict(d_model=256, n_heads=4, head_dim=64, rank_q=6, rank_k=2, rank_v=2, dtype=0), 680, 272),
+    (dict(), 800, 320),
+    (dict(d_model=4096, n_heads=32, head_dim=128), 1600, 640),
+    (dict(d_model=1536, n_heads=24, head_dim=64, rank_q=0, rank_k=4, rank_v=4), 2240, 704),
+])
+def test_sizes(kw, n_out, elems):
+    lib = T.library()
+    d = dims(**kw)
+    assert lib.tpa_packed_weight_rows(ctypes.byref(d)) == n_out
+    assert lib.tpa_cache_elems_per_token(ctypes.byref(d)) == elems
+
+
+@pytest.mark.parametrize("kw", [
+    dict(head_dim=63), dict(head_dim=0), dict(head_dim=258), dict(n_heads=0), dict(rank_k=0), dict(rank_v=65),
+    dict(rank_q=-1), dict(d_model=0), dict(rope_base=0.0), dict(rope_base=float("inf")), dict(dtype=7),
+])
+def test_invalid_dims(kw):
+    lib = T.library()
+    d = dims(**kw)
+    assert lib.tpa_packed_weight_rows(ctypes.byref(d)) == -1
+    f = T.tpa_factors(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0)
+    st = lib.tpa_factor_proj(ctypes.byref(d), FAKE, 1, 1, 0, FAKE, 1, ctypes.byref(f), None)
+    assert st == INVALID
+    assert lib.tpa_last_error().decode()
+
+
+def test_unsupported_head_elems():
+    lib = T.library()
+    d = dims(n_heads=128, head_dim=128)
+    f = T.tpa_factors(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0)
+    assert lib.tpa_factor_proj(ctypes.byref(d), FAKE, 1, 1, 0, FAKE, 1, ctypes.byref(f), None) == UNSUPPORTED
+
+
+def test_factor_proj_validation():
+    lib = T.library()
+    d = dims()
+    f = T.tpa_factors(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0)
+    call = lambda **k: lib.tpa_factor_proj(ctypes.byref(d), k.get("x", FAKE), k.get("B", 2), k.get("S", 3),
+                                           k.get("sp", 0), k.get("w", FAKE), 1, ctypes.byref(k.get("f", f)), None)
+    assert call(x=None) == INVALID
+    assert call(w=None) == INVALID
+    assert call(B=0) == INVALID
+    assert call(S=-1) == INVALID
+    assert call(sp=-1) == INVALID
+    assert call(f=T.tpa_factors(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0)) == INVALID   # a_q needed
+    assert call(f=T.tpa_factors(FAKE, FAKE, FAKE, None, FAKE, FAKE, 0, 0)) == INVALID
+    assert call(f=T.tpa_factors(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0)) == INVALID   # stride < S
+    assert call(B=1 << 20, S=1 << 12) == UNSUPPORTED
+    assert call(f=T.tpa_factors(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1)) == INVALID   # kv stride < S
+    assert "kv_batch_stride" in lib.tpa_last_error().decode()
+
+
+def test_rope_validation():
+    lib = T.library()
+    d = dims()
+    assert lib.tpa_rope_b(ctypes.byref(d), None, 1, 1, 2, 0, None) == INVALID
+    assert lib.tpa_rope_b(ctypes.byref(d), FAKE, 1, 1, 0, 0, None) == INVALID
+    assert lib.tpa_rope_b(ctypes.byref(d), FAKE, 1, 1, 2, -5, None) == INVALID
+    assert lib.tpa_rope_b(ctypes.byref(dims(head_dim=7)), FAKE, 1, 1, 2, 0, None) == INVALID
+
+
+def test_cache_append_validation():
+    lib = T.library()
+    d = dims()
+    c = T.tpa_cache(FAKE, FAKE, FAKE, FAKE, 4, 100)
+    kv = T.tpa_factors(None, None, FAKE, FAKE, FAKE, FAKE, 0, 0)
+    app = lambda B, S, sp, cc=c, kk=kv: lib.tpa_cache_append(ctypes.byref(d), ctypes.byref(cc), ctypes.byref(kk),
+                                                             B, S, sp, None)
+    assert app(5, 1, 0) == CAPACITY
+    assert app(4, 101, 0) == CAPACITY
+    assert app(4, 10, 91) == CAPACITY
+    assert app(1, 1, -1) == INVALID
+    assert app(1, 1, 0, cc=T.tpa_cache(FAKE, None, FAKE, FAKE, 4, 100)) == INVALID
+    assert app(1, 1, 0, cc=T.tpa_cache(FAKE, FAKE, FAKE, FAKE, 0, 100)) == INVALID
+    assert app(1, 1, 0, kk=T.tpa_factors(None, None, FAKE, FAKE, None, FAKE, 0, 0)) == INVALID
+    assert "max_seq" in lib.tpa_last_error().decode() or "NULL" in lib.tpa_last_error().decode()
+
+
+def test_prefill_validation():
+    lib = T.library()
+    d = dims()
+    c = T.tpa_cache(FAKE, FAKE, FAKE, FAKE, 2, 64)
+    q = T.tpa_factors(FAKE, FAKE, None, None, None, None, 0, 0)
+    pf = lambda B, S, sp, qq=q, out=FAKE: lib.tpa_prefill_attn(ctypes.byref(d), ctypes.byref(qq), ctypes.byref(c),
+                                                               B, S, sp, 1, out, None)
+    assert pf(3, 4, 0) == CAPACITY
+    assert pf(2, 65, 0) == CAPACITY
+    assert pf(2, 8, 57) == CAPACITY
+    assert pf(2, 8, 0, out=None) == INVALID
+    assert pf(2, 8, 0, qq=T.tpa_factors(None, FAKE, None, None, None, None, 0, 0)) == INVALID
+    kvonly = dims(rank_q=0)
+    assert lib.tpa_prefill_attn(ctypes.byref(kvonly), ctypes.byref(T.tpa_factors(None, None, None, None, None, None,
+                                                                                 0, 0)),
+                                ctypes.byref(c), 1, 1, 0, 1, FAKE, None) == INVALID
+
+
+def test_decode_validation():
+    lib = T.library()
+    d = dims()
+    c = T.tpa_cache(FAKE, FAKE, FAKE, FAKE, 16, 4097)
+    q = T.tpa_factors(FAKE, FAKE, None, None, None, None, 0, 0)
+    need = lib.tpa_decode_workspace_bytes(ctypes.byref(d), 16, 4097)
+    assert need > 0
+    dec = lambda B, L, ws, n: lib.tpa_decode_attn(ctypes.byref(d), ctypes.byref(q), ctypes.byref(c), B, L, FAKE,
+                                                  ws, n, None)
+    assert dec(16, 4097, FAKE, need - 1) == WORKSPACE
+    assert dec(16, 4097, None, need) == WORKSPACE
+    assert dec(17, 4097, FAKE, need) == CAPACITY
+    assert dec(16, 4098, FAKE, need * 2) == CAPACITY
+    assert dec(16, 0, FAKE, need) == INVALID
+    assert lib.tpa_decode_workspace_bytes(ctypes.byref(dims(head_dim=5)), 16, 4097) == 0
+
+
+def test_status_strings():
+    lib = T.library()
+    for s in range(6):
+        assert lib.tpa_status_string(s).decode() == T._STATUS[s]
+    assert lib.tpa_status_string(99).decode() == "unknown status"
