@@ -138,7 +138,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(AttnArgs
 }
 
 // Log-sum-exp merge of the chunk partials of one (head, sequence), in chunk
-// order; one workgroup per (head, sequence), threads over d.
+// order; one workgroup per (head, sequence), threads over d.  The chunk loops
+// are unrolled so that their independent loads are in flight together.
 template <typename T>
 __global__ void __launch_bounds__(64) decode_combine_kernel(AttnArgs a, int64_t n_chunks, const float* ws) {
   const int h = a.h, dh = a.d_h;
@@ -147,13 +148,16 @@ __global__ void __launch_bounds__(64) decode_combine_kernel(AttnArgs a, int64_t 
   const float* P = ws + (b * n_chunks * h + hh) * (int64_t)(dh + 2);
   const int64_t cstride = (int64_t)h * (dh + 2);
   float M = -INFINITY;
+#pragma unroll 8
   for (int64_t c = 0; c < n_chunks; ++c) M = fmaxf(M, P[c * cstride]);
   float L = 0.f;
+#pragma unroll 8
   for (int64_t c = 0; c < n_chunks; ++c) L = fmaf(fast_exp2(P[c * cstride] - M), P[c * cstride + 1], L);
   const float scale = a.v_scale / L;
   T* out = reinterpret_cast<T*>(a.out);
   for (int d = threadIdx.x; d < dh; d += blockDim.x) {
     float O = 0.f;
+#pragma unroll 8
     for (int64_t c = 0; c < n_chunks; ++c) O = fmaf(fast_exp2(P[c * cstride] - M), P[c * cstride + 2 + d], O);
     stf(out, (b * h + hh) * dh + d, O * scale);
   }
@@ -196,11 +200,12 @@ static size_t partial_bytes(const DecodePlan& p, const AttnArgs& a) {
   return (size_t)a.n_batch * (size_t)p.n_chunks * (size_t)a.h * (size_t)(a.d_h + 2) * sizeof(float);
 }
 
-// Large enough for either plan, so the size does not depend on pointer alignment.
+// Workspace: partials for either plan, so the size does not depend on pointer
+// alignment.
 size_t decode_workspace_bytes(const DecodePlan& p, const AttnArgs& a) {
   (void)p;
   const int64_t ctx_len = a.start_pos + 1;
-  size_t n = partial_bytes(plan_generic(ctx_len), a);
+  const size_t n = partial_bytes(plan_generic(ctx_len), a);
   const size_t m = partial_bytes(plan_mfma(a, ctx_len), a);
   return n > m ? n : m;
 }

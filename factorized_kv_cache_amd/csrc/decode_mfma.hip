@@ -21,41 +21,37 @@
 //    4g+j of tile 0 for j<4, of tile 1 for j>=4); B_V goes through a
 //    wave-private LDS tile to be read transposed.
 //
+// The next block's loads are issued before the current block is computed
+// (d_h = 64; at d_h = 128 the registers go to a second resident wave instead).
 // The four waves of a workgroup merge their (m, l, O) through LDS in a fixed
-// order, and the workgroup writes one partial per head to the workspace; the
-// combine pass is shared with the general kernel.
+// order and write one partial per head to the workspace; the combine pass,
+// shared with the general kernel, merges the chunks in index order.  (Merging
+// in the last workgroup to finish would need an agent-scope release per
+// workgroup, which writes back the whole L2 of its XCD: far slower than a
+// second launch.)
 #include "kernels.h"
+#include "mfma.h"
 
 namespace tpa {
 
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-__device__ __forceinline__ bf16x8_t pack8(const float* v) {
-  u16x8_t u;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) u[j] = f32_to_bf16(v[j]);
-  return __builtin_bit_cast(bf16x8_t, u);
-}
-
-// R consecutive bf16 values -> floats (R in {1, 2, 4}).
+// R consecutive bf16 values, loaded as one 2R-byte word.
 template <int R>
-__device__ __forceinline__ void load_rank(const bf16_t* p, float* out) {
+struct RankWord;
+template <>
+struct RankWord<1> { typedef uint16_t type; };
+template <>
+struct RankWord<2> { typedef uint32_t type; };
+template <>
+struct RankWord<4> { typedef uint2 type; };
+
+template <int R>
+__device__ __forceinline__ void unpack_rank(typename RankWord<R>::type v, float* out) {
   if constexpr (R == 1) {
-    out[0] = bf16_to_f32(*p);
+    out[0] = bf16_to_f32(v);
   } else if constexpr (R == 2) {
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
     out[0] = __uint_as_float(v << 16);
     out[1] = __uint_as_float(v & 0xffff0000u);
   } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
     out[0] = __uint_as_float(v.x << 16);
     out[1] = __uint_as_float(v.x & 0xffff0000u);
     out[2] = __uint_as_float(v.y << 16);
@@ -78,16 +74,172 @@ struct DecodeMfmaCfg {
   static constexpr int HP = HT * 16;     // padded head count
   static constexpr int LROW = DH + 4;    // LDS row stride (bf16): 4 rows apart = 8 banks apart
   static constexpr int OST = DH + 4;     // LDS row stride (f32) of the merge buffer
+  static constexpr bool kPrefetch = DH == 64;
   static constexpr size_t kLoopBytes = 4 * 32 * LROW * sizeof(bf16_t);
   static constexpr size_t kMergeBytes = (8 * HP + 2 * HP * OST) * sizeof(float);
   static constexpr size_t kLds = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
+  static_assert(kLds <= 65536, "LDS per workgroup");
+};
+
+// LDS the host checks before choosing this kernel: staged query factors (bytes).
+constexpr size_t kDecodeMfmaQueryLds = 16384;
+
+// Everything one value block needs from HBM, in registers.
+template <int DH, int R, int HT>
+struct BlockRegs {
+  using C = DecodeMfmaCfg<DH, R, HT>;
+  uint4 bv[DH / 16];                                 // half a B_V row, for the LDS tile
+  uint4 bk[2][C::KS];                                // B~_K operand slices
+  typename RankWord<R>::type ak[2][HT][C::NT];       // head factors of the lane's tokens
+  typename RankWord<R>::type av[2][HT][C::NT];
+};
+
+// Uniform base pointers of one chunk's cache rows; per-lane offsets from them
+// are 32-bit (the plan keeps a chunk under 2^31 elements per tensor).
+struct ChunkBase {
+  const bf16_t* ak;
+  const bf16_t* bk;
+  const bf16_t* av;
+  const bf16_t* bv;
 };
 
 template <int DH, int R, int HT>
-__global__ void __launch_bounds__(256) decode_mfma_kernel(AttnArgs a, int64_t ctx_len, int64_t chunk,
+__device__ __forceinline__ void load_block(BlockRegs<DH, R, HT>& g, const ChunkBase& cb, int h, int tb, int last,
+                                           int lane) {
+  using C = DecodeMfmaCfg<DH, R, HT>;
+  const int li = lane & 15, lg = lane >> 4;
+  {
+    const int row = lane >> 1, half = lane & 1;
+    int tok = tb + row / R;
+    tok = tok < last ? tok : last;
+    const uint4* src = reinterpret_cast<const uint4*>(cb.bv + ((tok * R + row % R) * DH + half * (DH / 2)));
+#pragma unroll
+    for (int u = 0; u < DH / 16; ++u) g.bv[u] = src[u];
+  }
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int row = st * 16 + li;
+    int tok = tb + row / R;
+    tok = tok < last ? tok : last;
+    const uint4* src = reinterpret_cast<const uint4*>(cb.bk + ((tok * R + row % R) * DH + lg * (DH / 4)));
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) g.bk[st][ks] = src[ks];
+  }
+  typedef typename RankWord<R>::type W;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      int head = ht * 16 + li;
+      head = head < h ? head : h - 1;
+#pragma unroll
+      for (int k = 0; k < C::NT; ++k) {
+        int tok = tb + (st * 16 + lg * 4) / R + k;
+        tok = tok < last ? tok : last;
+        g.ak[st][ht][k] = *reinterpret_cast<const W*>(cb.ak + (tok * h + head) * R);
+        g.av[st][ht][k] = *reinterpret_cast<const W*>(cb.av + (tok * h + head) * R);
+      }
+    }
+}
+
+template <int DH, int R, int HT>
+__device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf16_t* lbv, int tb, int last,
+                                              int lane, const bf16x8_t (&qop)[HT][DecodeMfmaCfg<DH, R, HT>::KS],
+                                              float (&m_run)[HT], float (&l_run)[HT],
+                                              f32x4_t (&oacc)[HT][DecodeMfmaCfg<DH, R, HT>::DT]) {
+  using C = DecodeMfmaCfg<DH, R, HT>;
+  constexpr int KS = C::KS, DT = C::DT, NT = C::NT, LROW = C::LROW;
+  const int li = lane & 15, lg = lane >> 4;
+
+  // B_V half-row -> wave-private LDS tile
+  {
+    const int row = lane >> 1, half = lane & 1;
+    uint2* dst = reinterpret_cast<uint2*>(lbv + row * LROW + half * (DH / 2));
+#pragma unroll
+    for (int u = 0; u < DH / 16; ++u) {
+      dst[2 * u] = make_uint2(g.bv[u].x, g.bv[u].y);
+      dst[2 * u + 1] = make_uint2(g.bv[u].z, g.bv[u].w);
+    }
+  }
+
+  // scores on the matrix cores
+  f32x4_t sacc[2][HT];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      f32x4_t accv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) accv = mfma_bf16(as_bf16x8(g.bk[st][ks]), qop[ht][ks], accv);
+      sacc[st][ht] = accv;
+    }
+
+  // online softmax per head, and the value-product operand C
+  bf16x8_t cop[HT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    float s[2][NT];
+    float av[2][4];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int k = 0; k < NT; ++k) {
+        float ak[R];
+        unpack_rank<R>(g.ak[st][ht][k], ak);
+        unpack_rank<R>(g.av[st][ht][k], &av[st][k * R]);
+        float v = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) v = fmaf(ak[rr], sacc[st][ht][k * R + rr], v);
+        const bool valid = tb + (st * 16 + lg * 4) / R + k <= last;
+        s[st][k] = valid ? v : -INFINITY;
+        bmax = fmaxf(bmax, s[st][k]);
+      }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    const float m_new = fmaxf(m_run[ht], bmax);
+    const float alpha = fast_exp2(m_run[ht] - m_new);
+    m_run[ht] = m_new;
+    float psum = 0.f;
+    float cv[8];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int k = 0; k < NT; ++k) {
+        const float p = fast_exp2(s[st][k] - m_new);
+        psum += p;
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) cv[st * 4 + k * R + rr] = p * av[st][k * R + rr];
+      }
+    l_run[ht] = l_run[ht] * alpha + psum;
+    cop[ht] = pack8(cv);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[ht][dt] *= alpha;
+  }
+
+  // value product: A operand = B_V^T read from LDS in the k-slot order
+  wave_lds_fence();
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int d = dt * 16 + li;
+    u16x8_t e;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = (j < 4) ? 4 * lg + j : 16 + 4 * lg + (j - 4);
+      e[j] = lbv[row * LROW + d];
+    }
+    const bf16x8_t bvop = __builtin_bit_cast(bf16x8_t, e);
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) oacc[ht][dt] = mfma_bf16(bvop, cop[ht], oacc[ht][dt]);
+  }
+  wave_lds_fence();
+}
+
+template <int DH, int R, int HT>
+__global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t ctx_len, int64_t chunk,
                                                           int64_t n_chunks, float* ws) {
   using C = DecodeMfmaCfg<DH, R, HT>;
-  constexpr int KS = C::KS, DT = C::DT, NT = C::NT, VBT = C::VBT, HP = C::HP, LROW = C::LROW, OST = C::OST;
+  constexpr int KS = C::KS, DT = C::DT, VBT = C::VBT, HP = C::HP, LROW = C::LROW, OST = C::OST;
   extern __shared__ __align__(16) unsigned char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -95,19 +247,35 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(AttnArgs a, int64_t ct
   const int64_t b = blockIdx.y, c = blockIdx.x;
   const int64_t t0 = c * chunk;
   const int64_t t1 = (t0 + chunk < ctx_len) ? t0 + chunk : ctx_len;
-  const bf16_t* AK = reinterpret_cast<const bf16_t*>(a.c_ak);
-  const bf16_t* BK = reinterpret_cast<const bf16_t*>(a.c_bk);
-  const bf16_t* AV = reinterpret_cast<const bf16_t*>(a.c_av);
-  const bf16_t* BV = reinterpret_cast<const bf16_t*>(a.c_bv);
-  const int64_t seq0 = b * a.max_seq;
+  const int64_t row0 = b * a.max_seq + t0;   // first cache row of this chunk
+  const ChunkBase cb = {reinterpret_cast<const bf16_t*>(a.c_ak) + row0 * h * R,
+                        reinterpret_cast<const bf16_t*>(a.c_bk) + row0 * R * DH,
+                        reinterpret_cast<const bf16_t*>(a.c_av) + row0 * h * R,
+                        reinterpret_cast<const bf16_t*>(a.c_bv) + row0 * R * DH};
+  const int last = (int)(t1 - t0) - 1;      // chunk-local index of the last token
+  const int nvb = (last + VBT) / VBT;
 
-  // ---- query operand: lane (head = 16*ht + li, slice lg) holds
-  //      q[head][lg*DH/4 + 8*ks + j], j < 8, scaled and rounded to bf16.
+  // The first block's loads go out before the query is formed.
+  BlockRegs<DH, R, HT> cur;
+  if (wave < nvb) load_block<DH, R, HT>(cur, cb, h, wave * VBT, last, lane);
+
+  // ---- query operand, via the query factors staged in LDS (one round trip).
+  //      Lane (head = 16*ht + li, slice lg) holds q[head][lg*DH/4 + 8*ks + j].
   bf16x8_t qop[HT][KS];
   {
     const bf16_t* AQ = reinterpret_cast<const bf16_t*>(a.a_q);
     const bf16_t* BQ = reinterpret_cast<const bf16_t*>(a.b_q);
     const int64_t tok = b * a.q_bstride_tok;
+    const int rq = a.rq;
+    bf16_t* qa = reinterpret_cast<bf16_t*>(smem);     // [h][rq], or the plain Q [h][DH]
+    bf16_t* qb = qa + (rq ? h * rq : h * DH);          // [rq][DH]
+    if (rq == 0) {
+      for (int i = threadIdx.x; i < h * DH; i += blockDim.x) qa[i] = BQ[tok * h * DH + i];
+    } else {
+      for (int i = threadIdx.x; i < h * rq; i += blockDim.x) qa[i] = AQ[tok * h * rq + i];
+      for (int i = threadIdx.x; i < rq * DH; i += blockDim.x) qb[i] = BQ[tok * rq * DH + i];
+    }
+    __syncthreads();
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const int head = ht * 16 + li;
@@ -118,17 +286,14 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(AttnArgs a, int64_t ct
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = 0.f;
         if (head < h) {
-          if (a.rq == 0) {
-            const uint4 u = *reinterpret_cast<const uint4*>(BQ + (tok * h + head) * DH + d0);
-            const bf16x8_t e = as_bf16x8(u);
+          if (rq == 0) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = (float)e[j];
+            for (int j = 0; j < 8; ++j) v[j] = bf16_to_f32(qa[head * DH + d0 + j]);
           } else {
-            for (int r = 0; r < a.rq; ++r) {
-              const float ar = bf16_to_f32(AQ[(tok * h + head) * a.rq + r]);
-              const bf16x8_t e = as_bf16x8(*reinterpret_cast<const uint4*>(BQ + (tok * a.rq + r) * DH + d0));
+            for (int r = 0; r < rq; ++r) {
+              const float ar = bf16_to_f32(qa[head * rq + r]);
 #pragma unroll
-              for (int j = 0; j < 8; ++j) v[j] = fmaf(ar, (float)e[j], v[j]);
+              for (int j = 0; j < 8; ++j) v[j] = fmaf(ar, bf16_to_f32(qb[r * DH + d0 + j]), v[j]);
             }
           }
 #pragma unroll
@@ -137,6 +302,7 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(AttnArgs a, int64_t ct
         qop[ht][ks] = pack8(v);
       }
     }
+    __syncthreads();
   }
 
   float m_run[HT], l_run[HT];
@@ -150,125 +316,18 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(AttnArgs a, int64_t ct
   }
 
   bf16_t* lbv = reinterpret_cast<bf16_t*>(smem) + wave * 32 * LROW;
-  const int64_t last = t1 - 1;
-  const int nvb = (int)((t1 - t0 + VBT - 1) / VBT);
-
   for (int vb = wave; vb < nvb; vb += 4) {
-    const int64_t tb = t0 + (int64_t)vb * VBT;
-
-    // ---- B_V block (32 rows x DH) -> LDS: lane loads half of row lane/2.
-    {
-      const int row = lane >> 1, half = lane & 1;
-      int64_t tok = tb + row / R;
-      tok = tok < last ? tok : last;
-      const uint4* src = reinterpret_cast<const uint4*>(BV + ((seq0 + tok) * R + row % R) * DH + half * (DH / 2));
-      uint4 v[DH / 16];
-#pragma unroll
-      for (int u = 0; u < DH / 16; ++u) v[u] = src[u];
-      uint2* dst = reinterpret_cast<uint2*>(lbv + row * LROW + half * (DH / 2));
-#pragma unroll
-      for (int u = 0; u < DH / 16; ++u) {
-        dst[2 * u] = make_uint2(v[u].x, v[u].y);
-        dst[2 * u + 1] = make_uint2(v[u].z, v[u].w);
-      }
+    const int tb = vb * VBT;
+    if constexpr (C::kPrefetch) {
+      BlockRegs<DH, R, HT> nxt;
+      const bool more = vb + 4 < nvb;
+      if (more) load_block<DH, R, HT>(nxt, cb, h, tb + 4 * VBT, last, lane);
+      compute_block<DH, R, HT>(cur, lbv, tb, last, lane, qop, m_run, l_run, oacc);
+      if (more) cur = nxt;
+    } else {
+      if (vb != wave) load_block<DH, R, HT>(cur, cb, h, tb, last, lane);
+      compute_block<DH, R, HT>(cur, lbv, tb, last, lane, qop, m_run, l_run, oacc);
     }
-
-    // ---- B~_K operand: tile st, row li, slice lg.
-    bf16x8_t kop[2][KS];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int row = st * 16 + li;
-      int64_t tok = tb + row / R;
-      tok = tok < last ? tok : last;
-      const uint4* src = reinterpret_cast<const uint4*>(BK + ((seq0 + tok) * R + row % R) * DH + lg * (DH / 4));
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kop[st][ks] = as_bf16x8(src[ks]);
-    }
-
-    // ---- head factors of the lane's rows: tokens (16*st + 4*lg)/R + k.
-    float ak[2][HT][4], av[2][HT][4];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        int head = ht * 16 + li;
-        head = head < h ? head : h - 1;
-#pragma unroll
-        for (int k = 0; k < NT; ++k) {
-          int64_t tok = tb + (st * 16 + lg * 4) / R + k;
-          tok = tok < last ? tok : last;
-          load_rank<R>(AK + ((seq0 + tok) * h + head) * R, &ak[st][ht][k * R]);
-          load_rank<R>(AV + ((seq0 + tok) * h + head) * R, &av[st][ht][k * R]);
-        }
-      }
-
-    // ---- scores on the matrix cores
-    f32x4_t sacc[2][HT];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        f32x4_t accv = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) accv = mfma_bf16(kop[st][ks], qop[ht][ks], accv);
-        sacc[st][ht] = accv;
-      }
-
-    // ---- online softmax per head, and the value-product operand C
-    bf16x8_t cop[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      float s[2][NT];
-      float bmax = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int k = 0; k < NT; ++k) {
-          float v = 0.f;
-#pragma unroll
-          for (int rr = 0; rr < R; ++rr) v = fmaf(ak[st][ht][k * R + rr], sacc[st][ht][k * R + rr], v);
-          const bool valid = tb + (st * 16 + lg * 4) / R + k <= last;
-          s[st][k] = valid ? v : -INFINITY;
-          bmax = fmaxf(bmax, s[st][k]);
-        }
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      const float m_new = fmaxf(m_run[ht], bmax);
-      const float alpha = fast_exp2(m_run[ht] - m_new);
-      m_run[ht] = m_new;
-      float psum = 0.f;
-      float cv[8];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int k = 0; k < NT; ++k) {
-          const float p = fast_exp2(s[st][k] - m_new);
-          psum += p;
-#pragma unroll
-          for (int rr = 0; rr < R; ++rr) cv[st * 4 + k * R + rr] = p * av[st][ht][k * R + rr];
-        }
-      l_run[ht] = l_run[ht] * alpha + psum;
-      cop[ht] = pack8(cv);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[ht][dt] *= alpha;
-    }
-
-    // ---- value product: A operand = B_V^T read from LDS in the k-slot order
-    wave_lds_fence();
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = dt * 16 + li;
-      u16x8_t e;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = (j < 4) ? 4 * lg + j : 16 + 4 * lg + (j - 4);
-        e[j] = lbv[row * LROW + d];
-      }
-      const bf16x8_t bvop = __builtin_bit_cast(bf16x8_t, e);
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) oacc[ht][dt] = mfma_bf16(bvop, cop[ht], oacc[ht][dt]);
-    }
-    wave_lds_fence();
   }
 
   // ---- merge the four waves (fixed order) and write this chunk's partial
@@ -318,7 +377,8 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(AttnArgs a, int64_t ct
       }
   }
   __syncthreads();
-  float* P = ws + ((b * n_chunks + c) * h) * (int64_t)(DH + 2);
+  const int64_t cstride = (int64_t)h * (DH + 2);
+  float* P = ws + (b * n_chunks + c) * cstride;
   for (int idx = threadIdx.x; idx < h * DH; idx += blockDim.x) {
     const int head = idx / DH, d = idx - head * DH;
     P[head * (DH + 2) + 2 + d] = obuf[head * OST + d] + obuf[(HP + head) * OST + d];
@@ -331,6 +391,7 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(AttnArgs a, int64_t ct
     P[head * (DH + 2)] = M;
     P[head * (DH + 2) + 1] = L;
   }
+
 }
 
 bool decode_mfma_supported(int dtype, const AttnArgs& a) {
@@ -338,19 +399,23 @@ bool decode_mfma_supported(int dtype, const AttnArgs& a) {
   if (a.rk != a.rv || !(a.rk == 1 || a.rk == 2 || a.rk == 4)) return false;
   if (!(a.d_h == 64 || a.d_h == 128)) return false;
   if (a.h > 64) return false;
-  const void* ptrs[6] = {a.b_q, a.c_ak, a.c_bk, a.c_av, a.c_bv, a.a_q};
-  for (int i = 0; i < 6; ++i)
+  if (a.d_h == 128 && a.h > 48) return false;  // merge buffer would pass 64 KB of LDS
+  const size_t qbytes = (a.rq ? (size_t)a.rq * (a.h + a.d_h) : (size_t)a.h * a.d_h) * sizeof(bf16_t);
+  if (qbytes > kDecodeMfmaQueryLds) return false;
+  const void* ptrs[5] = {a.b_q, a.c_ak, a.c_bk, a.c_av, a.c_bv};
+  for (int i = 0; i < 5; ++i)
     if (((uintptr_t)ptrs[i]) % 16) return false;
   return true;
 }
 
-// Value-block tokens times the four waves of a workgroup.
+// Tokens one workgroup covers per step (one value block per wave).
 int64_t decode_mfma_wave_tokens(const AttnArgs& a) { return 4 * (32 / a.rk); }
 
 template <int DH, int R, int HT>
 static void launch_cfg(const AttnArgs& a, int64_t ctx_len, int64_t chunk, int64_t n_chunks, float* ws,
                        hipStream_t st) {
   using C = DecodeMfmaCfg<DH, R, HT>;
+  static_assert(C::kLds >= kDecodeMfmaQueryLds, "LDS area of the staged query factors");
   hipLaunchKernelGGL((decode_mfma_kernel<DH, R, HT>), dim3((unsigned)n_chunks, (unsigned)a.n_batch), dim3(256),
                      C::kLds, st, a, ctx_len, chunk, n_chunks, ws);
 }
@@ -363,7 +428,9 @@ static void launch_dh_r(const AttnArgs& a, int64_t ctx_len, int64_t chunk, int64
     case 1: launch_cfg<DH, R, 1>(a, ctx_len, chunk, n_chunks, ws, st); break;
     case 2: launch_cfg<DH, R, 2>(a, ctx_len, chunk, n_chunks, ws, st); break;
     case 3: launch_cfg<DH, R, 3>(a, ctx_len, chunk, n_chunks, ws, st); break;
-    default: launch_cfg<DH, R, 4>(a, ctx_len, chunk, n_chunks, ws, st); break;
+    default:
+      if constexpr (DH == 64) launch_cfg<DH, R, 4>(a, ctx_len, chunk, n_chunks, ws, st);
+      break;
   }
 }
 

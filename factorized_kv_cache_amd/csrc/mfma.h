@@ -1,0 +1,34 @@
+// gfx950 matrix-core helpers: v_mfma_f32_16x16x32_bf16 and its operand types.
+//
+// Register layout of the 16x16x32 bf16 product D = A B + C for lane l
+// (li = l % 16, lg = l / 16):
+//   A (16 x 32): 8 values A[li][8*lg + j], j < 8
+//   B (32 x 16): 8 values B[8*lg + j][li]
+//   D (16 x 16): 4 values D[4*lg + i][li], i < 4
+// Any bijection between the 32 k indices and the (lg, j) slots may be used, as
+// long as A and B use the same one; the kernels use that freedom to keep each
+// lane's loads contiguous.
+#pragma once
+
+#include "common.h"
+
+namespace tpa {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ bf16x8_t pack8(const float* v) {
+  u16x8_t u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) u[j] = f32_to_bf16(v[j]);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+}  // namespace tpa

@@ -150,7 +150,11 @@ static hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+bool prefill_mfma_supported(int dtype, const AttnArgs& a);
+hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t st);
+
 hipError_t launch_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
+  if (prefill_mfma_supported(dtype, a)) return launch_prefill_mfma(a, st);
   return dtype == kF32 ? launch_prefill_t<float>(a, st) : launch_prefill_t<bf16_t>(a, st);
 }
 

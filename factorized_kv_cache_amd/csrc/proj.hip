@@ -10,6 +10,7 @@
 // W_B_v, W_A_q, W_A_k, W_A_v), so the rotated columns are [0, rot_cols) and
 // every rotary pair (2i, 2i+1) sits on an even column.
 #include "kernels.h"
+#include "mfma.h"
 
 namespace tpa {
 
@@ -89,7 +90,183 @@ __global__ void __launch_bounds__(256) proj_generic_kernel(ProjArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Few tokens (decode): bound by reading the weights once.  One workgroup owns
+// 16 weight rows; its four waves split K.  The product is taken as
+// D[n, m] = W[n, :] . X[m, :], weight rows as the A operand and tokens as the B
+// operand, both read straight from memory (K-contiguous).  The four partial
+// tiles are summed in LDS in wave order, then the epilogue stores pairs.
+// ---------------------------------------------------------------------------
+template <int MT>
+__global__ void __launch_bounds__(256) proj_skinny_kernel(ProjArgs a) {
+  __shared__ float red[4][16][16 * MT + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int K = (int)a.K, M = (int)a.M, N = (int)a.N;
+  const int kq = K / 4;
+  const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
+  const bf16_t* W = reinterpret_cast<const bf16_t*>(a.w);
+  const int nrow = (n0 + li < N) ? n0 + li : N - 1;
+  const bf16_t* wrow = W + (int64_t)nrow * K + wave * kq + lg * 8;
+  const bf16_t* xrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = (mt * 16 + li < M) ? mt * 16 + li : M - 1;
+    xrow[mt] = X + (int64_t)m * K + wave * kq + lg * 8;
+  }
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // four k-steps per trip, their loads issued together (steps past kq repeat
+  // the last step's address and are not multiplied)
+  for (int k = 0; k < kq; k += 128) {
+    uint4 wv[4], xv[4][MT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ku = k + 32 * u < kq ? k + 32 * u : kq - 32;
+      wv[u] = *reinterpret_cast<const uint4*>(wrow + ku);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) xv[u][mt] = *reinterpret_cast<const uint4*>(xrow[mt] + ku);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (k + 32 * u >= kq) break;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16(as_bf16x8(wv[u]), as_bf16x8(xv[u][mt]), acc[mt]);
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][4 * lg + i][mt * 16 + li] = acc[mt][i];
+  __syncthreads();
+  for (int item = threadIdx.x; item < 8 * 16 * MT; item += blockDim.x) {
+    const int p = item & 7, m = item >> 3;   // rows 2p, 2p+1 of the tile, token m
+    const int n = n0 + 2 * p;
+    if (m >= M || n >= N) continue;
+    float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      v0 += red[w][2 * p][m];
+      v1 += red[w][2 * p + 1][m];
+    }
+    proj_store_pair<bf16_t>(a, m, n, v0, v1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Many tokens (prefill): 128 x 128 output tile per workgroup, four waves of
+// 64 x 64, K staged through LDS 64 at a time with the next slab held in
+// registers while the current one is multiplied.
+// ---------------------------------------------------------------------------
+constexpr int kPBM = 128, kPBN = 128, kPBK = 64, kPLDK = kPBK + 8;
+
+__global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
+  __shared__ __align__(16) bf16_t xs[kPBM * kPLDK];
+  __shared__ __align__(16) bf16_t ws[kPBN * kPLDK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.x * kPBM;
+  const int n0 = blockIdx.y * kPBN;
+  const int64_t M = a.M, K = a.K;
+  const int N = (int)a.N;
+  const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
+  const bf16_t* W = reinterpret_cast<const bf16_t*>(a.w);
+
+  // This thread's four 16-byte pieces of each slab: row = idx / 8, piece = idx % 8.
+  // Rows past M or N are clamped to the last row: they only feed outputs that
+  // are never stored.
+  const bf16_t* xsrc[4];
+  const bf16_t* wsrc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = tid + 256 * q, row = idx >> 3, pc = idx & 7;
+    const int64_t xm = m0 + row < M ? m0 + row : M - 1;
+    const int64_t wn_ = n0 + row < N ? n0 + row : N - 1;
+    xsrc[q] = X + xm * K + pc * 8;
+    wsrc[q] = W + wn_ * K + pc * 8;
+  }
+  uint4 xr0 = *reinterpret_cast<const uint4*>(xsrc[0]), xr1 = *reinterpret_cast<const uint4*>(xsrc[1]);
+  uint4 xr2 = *reinterpret_cast<const uint4*>(xsrc[2]), xr3 = *reinterpret_cast<const uint4*>(xsrc[3]);
+  uint4 wr0 = *reinterpret_cast<const uint4*>(wsrc[0]), wr1 = *reinterpret_cast<const uint4*>(wsrc[1]);
+  uint4 wr2 = *reinterpret_cast<const uint4*>(wsrc[2]), wr3 = *reinterpret_cast<const uint4*>(wsrc[3]);
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int srow = tid >> 3, spc = tid & 7;   // row of piece q is srow + 32 q
+  for (int64_t k0 = 0; k0 < K; k0 += kPBK) {
+    *reinterpret_cast<uint4*>(xs + (srow + 0) * kPLDK + spc * 8) = xr0;
+    *reinterpret_cast<uint4*>(xs + (srow + 32) * kPLDK + spc * 8) = xr1;
+    *reinterpret_cast<uint4*>(xs + (srow + 64) * kPLDK + spc * 8) = xr2;
+    *reinterpret_cast<uint4*>(xs + (srow + 96) * kPLDK + spc * 8) = xr3;
+    *reinterpret_cast<uint4*>(ws + (srow + 0) * kPLDK + spc * 8) = wr0;
+    *reinterpret_cast<uint4*>(ws + (srow + 32) * kPLDK + spc * 8) = wr1;
+    *reinterpret_cast<uint4*>(ws + (srow + 64) * kPLDK + spc * 8) = wr2;
+    *reinterpret_cast<uint4*>(ws + (srow + 96) * kPLDK + spc * 8) = wr3;
+    __syncthreads();
+    // next slab (the last iteration reloads the final slab; it is never used)
+    const int64_t kn = k0 + kPBK < K ? k0 + kPBK : k0;
+    xr0 = *reinterpret_cast<const uint4*>(xsrc[0] + kn);
+    xr1 = *reinterpret_cast<const uint4*>(xsrc[1] + kn);
+    xr2 = *reinterpret_cast<const uint4*>(xsrc[2] + kn);
+    xr3 = *reinterpret_cast<const uint4*>(xsrc[3] + kn);
+    wr0 = *reinterpret_cast<const uint4*>(wsrc[0] + kn);
+    wr1 = *reinterpret_cast<const uint4*>(wsrc[1] + kn);
+    wr2 = *reinterpret_cast<const uint4*>(wsrc[2] + kn);
+    wr3 = *reinterpret_cast<const uint4*>(wsrc[3] + kn);
+#pragma unroll
+    for (int ks = 0; ks < kPBK / 32; ++ks) {
+      bf16x8_t af[4], bfr[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        af[t] = as_bf16x8(*reinterpret_cast<const uint4*>(xs + (wm * 64 + t * 16 + li) * kPLDK + ks * 32 + lg * 8));
+        bfr[t] = as_bf16x8(*reinterpret_cast<const uint4*>(ws + (wn * 64 + t * 16 + li) * kPLDK + ks * 32 + lg * 8));
+      }
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma_bf16(af[tm], bfr[tn], acc[tm][tn]);
+    }
+    __syncthreads();
+  }
+  // D[m][n] with n = ... + li: the rotary partner column n^1 is lane li^1.
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = acc[tm][tn][i];
+        const float partner = __shfl_xor(v, 1);
+        const int64_t m = m0 + wm * 64 + tm * 16 + 4 * lg + i;
+        const int n = n0 + wn * 64 + tn * 16 + li;
+        if (!(li & 1) && m < M && n < N) proj_store_pair<bf16_t>(a, m, n, v, partner);
+      }
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 hipError_t launch_factor_proj(int dtype, const ProjArgs& a, hipStream_t st) {
+  if (dtype == kBF16 && aligned16(a.x) && aligned16(a.w) && a.K % 64 == 0) {
+    if (a.M <= 64 && a.K % 128 == 0) {
+      const dim3 grid((unsigned)((a.N + 15) / 16));
+      switch ((a.M + 15) / 16) {
+        case 1: hipLaunchKernelGGL(proj_skinny_kernel<1>, grid, dim3(256), 0, st, a); break;
+        case 2: hipLaunchKernelGGL(proj_skinny_kernel<2>, grid, dim3(256), 0, st, a); break;
+        case 3: hipLaunchKernelGGL(proj_skinny_kernel<3>, grid, dim3(256), 0, st, a); break;
+        default: hipLaunchKernelGGL(proj_skinny_kernel<4>, grid, dim3(256), 0, st, a); break;
+      }
+    } else {
+      const dim3 grid((unsigned)((a.M + kPBM - 1) / kPBM), (unsigned)((a.N + kPBN - 1) / kPBN));
+      hipLaunchKernelGGL(proj_mfma_kernel, grid, dim3(256), 0, st, a);
+    }
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((a.M + 63) / 64), (unsigned)((a.N + 63) / 64));
   if (dtype == kF32)
     hipLaunchKernelGGL(proj_generic_kernel<float>, grid, dim3(256), 0, st, a);

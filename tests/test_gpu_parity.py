@@ -80,6 +80,9 @@ PROJ_CASES = [
     (3, 70, 1024, 16, 64, 6, 2, 2, 11),
     (2, 33, 192, 24, 64, 0, 4, 4, 100),
     (1, 1, 4096, 32, 128, 6, 2, 2, 131072),
+    (16, 1, 1024, 16, 64, 6, 2, 2, 4096),       # decode batch: few-token kernel
+    (40, 1, 1536, 24, 64, 0, 4, 4, 16384),
+    (3, 150, 1536, 24, 64, 0, 4, 4, 0),          # KV-only, many tokens
 ]
 
 
@@ -261,3 +264,60 @@ def test_tiny_fp32_end_to_end():
     ref = O.layer_forward(I.to_f64(x), {k: I.to_f64(v) for k, v in w.items()}, od, O.cache_new(od, B, S + steps),
                           0, True)
     assert_close(got, ref, "f32", "tiny fp32 end to end")
+
+
+def _misaligned(t: torch.Tensor) -> torch.Tensor:
+    """Same values at an address 2 bytes past a 16-byte boundary."""
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    v = flat[1:1 + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def test_decode_general_path_matches_fast_path():
+    """An MFMA-eligible shape with misaligned cache pointers runs the general
+    kernel; both must meet the oracle bound."""
+    require_gpu()
+    dims = D(1024, 16, 64, 6, 2, 2, "bf16")
+    B, ctx = 4, 700
+    announce("decode general vs fast path")
+    sh = shape_of(dims)
+    kv = I.factors(sh, B, ctx, seed=91, dtype="bf16", with_query=False)
+    fq = I.factors(sh, B, 1, seed=92, dtype="bf16")
+    cache = T.new_cache(dims, B, ctx)
+    fill_cache(cache, kv)
+    q = query_factors_gpu(T, dims, fq, squeeze=True)
+    ws = T.new_workspace(dims, B, ctx)
+    fast = T.tpa_decode_attn(dims, q, cache, ctx, ws)
+    mis = T.Cache(*(_misaligned(getattr(cache, k)) for k in ("a_k", "b_k", "a_v", "b_v")))
+    slow = T.tpa_decode_attn(dims, q, mis, ctx, ws)
+    torch.cuda.synchronize()
+    od = oracle_dims(dims)
+    ref = O.decode(oracle_query(fq, dims), oracle_cache(kv, od, B, ctx), od, B, ctx)
+    assert_close(fast, ref, "bf16", "decode fast path")
+    assert_close(slow, ref, "bf16", "decode general path")
+
+
+@pytest.mark.parametrize("wl_name,B,S,n_rows", [
+    ("prefill_b4_s4k", 4, 4096, 48),       # the causal prefill workload at full size
+    ("kvonly_b32_ctx16k", 2, 2048, 32),    # the KV-only shape, two sequences of 2048
+])
+def test_prefill_full_size_sampled_rows(wl_name, B, S, n_rows):
+    """Prefill in the launch configuration the benchmark times; the oracle computes
+    sampled query rows one by one (each row is its own definition)."""
+    require_gpu()
+    wl = I.WORKLOADS[wl_name]
+    sh = wl.shape
+    dims = D(sh.d_model, sh.n_heads, sh.head_dim, sh.rank_q, sh.rank_k, sh.rank_v, "bf16")
+    announce(f"prefill full size {wl_name} B={B} S={S}")
+    kv = I.factors(sh, B, S, seed=101, dtype="bf16", with_query=False)
+    fq = I.factors(sh, B, S, seed=102, dtype="bf16")
+    cache = T.new_cache(dims, B, S)
+    fill_cache(cache, kv)
+    out = T.tpa_prefill_attn(dims, query_factors_gpu(T, dims, fq), cache, 0, True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, S - 1], rng.integers(0, S, n_rows)]))
+    od = oracle_dims(dims)
+    ref = O.prefill(oracle_query(fq, dims), oracle_cache(kv, od, B, S), od, B, S, 0, True, rows=rows)
+    assert_close(out[:, rows], ref[:, rows], "bf16", f"prefill {wl_name} sampled rows")
