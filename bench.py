@@ -5,17 +5,20 @@
 A step is one decode step of one TPA attention layer for the whole batch of
 the decode workload (batch 16, 4096 cached tokens plus the new one, d_model
 1024, 16 heads of 64, R_Q 6, R_K = R_V 2, bf16): factor projection of the new
-tokens with fused RoPE, cache append, decode attention over the 4097 keys
-(main pass + combine).  Eight independent layers (weights and factor caches,
+tokens with fused RoPE, whose epilogue appends their K/V factors straight into
+cache slot 4096, then decode attention over the 4097 keys (main pass +
+combine).  Eight independent layers (weights and factor caches,
 336 MB of cache) are visited in turn, so each step reads its cache cold from
 HBM, as in a multi-layer model; the caches are built through the same
 projection and append kernels from synthetic N(0,1) activations and
 N(0,0.02) weights.
 
 Prints one JSON line.  `value` is decode throughput in tokens/s (batch /
-step time).  `roofline` covers the decode attention call (the dominant
-kernel): algorithmic factor-cache bytes per call over its average duration,
-timed with HIP events on the stream it runs on.  `cpu_baseline` is the fp64
+step time), with the eight-layer step captured once as a HIP graph and
+replayed (K steps = K/8 replays).  `roofline` covers the decode attention call
+(the dominant kernel): algorithmic factor-cache bytes per call over its
+average duration, timed with HIP events on the stream it runs on in an eager
+pass over the same steps.  `cpu_baseline` is the fp64
 oracle timed on a bounded sample of the same decode step.  `prefill` reports
 the causal prefill workload (batch 4, 4096 tokens) in TFLOP/s.
 """
@@ -98,7 +101,10 @@ class DecodeBench:
             del f
             x_new = torch.randn(self.B, 1, d.d_model, generator=g, device=dev).to(torch.bfloat16)
             qf = T.new_factors(d, self.B, 1)
-            self.layers.append(dict(wp=wp, cache=cache, x_new=x_new, qf=qf,
+            slot = cache.slot_factors(self.ctx - 1)
+            # the new token's K/V factors are written straight into their cache slot
+            into = T.Factors(qf.a_q, qf.b_q, slot.a_k, slot.b_k, slot.a_v, slot.b_v, 0, self.ctx)
+            self.layers.append(dict(wp=wp, cache=cache, x_new=x_new, qf=qf, into=into,
                                     q=T.Factors(qf.a_q[:, 0] if qf.a_q is not None else None, qf.b_q[:, 0],
                                                 None, None, None, None),
                                     ws=T.new_workspace(d, self.B, self.ctx),
@@ -110,8 +116,7 @@ class DecodeBench:
     def step(self, k: int, ev=None):
         d = self.dims
         L = self.layers[k % LAYERS]
-        T.tpa_factor_proj(d, L["x_new"], L["wp"], L["qf"], start_pos=self.ctx - 1)
-        T.tpa_cache_append(d, L["cache"], L["qf"], self.ctx - 1)
+        T.tpa_factor_proj(d, L["x_new"], L["wp"], L["into"], start_pos=self.ctx - 1)
         if ev is not None:
             ev[0].record()
         T.tpa_decode_attn(d, L["q"], L["cache"], self.ctx, L["ws"], out=L["out"])
@@ -123,26 +128,49 @@ class DecodeBench:
 
 
 def run_decode(args):
+    """Returns (bench, workload, graph ms/step, eager ms/step, decode-call avg ms, median ms).
+
+    Two timed regions over the same steps: an eager one, with events around every
+    decode call (the per-call duration of the roofline), and a replay of the
+    eight-layer step captured once as a HIP graph (the throughput)."""
     wl = I.WORKLOADS["decode_b16_ctx4k"]
     log(f"[bench] building {LAYERS} layer caches for {wl.name}")
     db = DecodeBench(wl)
     for k in range(args.warmup):
         db.step(k)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    n = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
-    for k in range(args.steps):
+    for k in range(n):
         db.step(k, evs[k])
     stop.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
+    eager_ms = start.elapsed_time(stop) / n
     dec_ms = sorted(a.elapsed_time(b) for a, b in evs)
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     dec_med_ms = dec_ms[len(dec_ms) // 2]
-    return db, wl, ms_per_step, dec_avg_ms, dec_med_ms
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for k in range(LAYERS):
+                db.step(k)
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(max(1, args.warmup // LAYERS)):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, (n + LAYERS - 1) // LAYERS)
+    start.record()
+    for _ in range(reps):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(stop) / (reps * LAYERS)
+    return db, wl, graph_ms, eager_ms, dec_avg_ms, dec_med_ms, reps * LAYERS
 
 
 # ---------------------------------------------------------------------------
@@ -243,7 +271,7 @@ def calibrate_copy(tokens: int = 26214, batch: int = 16):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -260,7 +288,7 @@ def main():
         calibrate_copy()
         return
 
-    db, wl, ms_per_step, dec_avg_ms, dec_med_ms = run_decode(args)
+    db, wl, ms_per_step, eager_ms, dec_avg_ms, dec_med_ms, graph_steps = run_decode(args)
     bytes_per_call = db.cache_bytes()
     achieved = bytes_per_call / (dec_avg_ms * 1e-3) / 1e9
     traffic = load_traffic(["decode_mfma.hip", "decode.hip"])
@@ -272,7 +300,7 @@ def main():
         "metric": METRIC,
         "value": round(db.B / (ms_per_step * 1e-3), 1),
         "unit": "tok/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": graph_steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
@@ -280,6 +308,7 @@ def main():
                    "heads": wl.shape.n_heads, "head_dim": wl.shape.head_dim, "rank_q": wl.shape.rank_q,
                    "rank_k": wl.shape.rank_k, "rank_v": wl.shape.rank_v, "layers_cycled": LAYERS},
         "roofline": roofline,
+        "launch": {"hip_graph_ms_per_step": round(ms_per_step, 5), "eager_ms_per_step": round(eager_ms, 5)},
     }
     if not args.no_prefill:
         log("[bench] prefill workload")

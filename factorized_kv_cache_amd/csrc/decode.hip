@@ -137,29 +137,61 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(AttnArgs
   }
 }
 
-// Log-sum-exp merge of the chunk partials of one (head, sequence), in chunk
-// order; one workgroup per (head, sequence), threads over d.  The chunk loops
-// are unrolled so that their independent loads are in flight together.
+// Log-sum-exp merge of the chunk partials of one (head, sequence); one
+// workgroup per (head, sequence).  Thread (d, g) sums the chunks c = g, g+G, ...
+// of element d (G = 256 / d_h groups), with the first 16 of its partial
+// vectors loaded together with the chunk maxima and sums, so that the merge
+// costs about one memory round trip; groups are then added in order g = 0..G-1.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineRegs = 16;
+constexpr int kCombineMaxChunks = 2048;   // LDS: maxima and sums of the chunks
+
 template <typename T>
-__global__ void __launch_bounds__(64) decode_combine_kernel(AttnArgs a, int64_t n_chunks, const float* ws) {
+__global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(AttnArgs a, int64_t n_chunks,
+                                                                         const float* ws) {
+  __shared__ float mloc[kCombineMaxChunks];
+  __shared__ float lloc[kCombineMaxChunks];
+  __shared__ float part[kCombineThreads];
   const int h = a.h, dh = a.d_h;
   const int hh = blockIdx.x;
   const int64_t b = blockIdx.y;
   const float* P = ws + (b * n_chunks * h + hh) * (int64_t)(dh + 2);
   const int64_t cstride = (int64_t)h * (dh + 2);
+  const int G = kCombineThreads / dh;
+  const int d = threadIdx.x % dh, g = threadIdx.x / dh;
+  const bool active = g < G;
+  const int nc = (int)n_chunks;
+
+  float accv[kCombineRegs];
+#pragma unroll
+  for (int j = 0; j < kCombineRegs; ++j) {
+    const int c = g + G * j;
+    accv[j] = (active && c < nc) ? P[(int64_t)c * cstride + 2 + d] : 0.f;
+  }
+  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+    mloc[c] = P[(int64_t)c * cstride];
+    lloc[c] = P[(int64_t)c * cstride + 1];
+  }
+  __syncthreads();
   float M = -INFINITY;
-#pragma unroll 8
-  for (int64_t c = 0; c < n_chunks; ++c) M = fmaxf(M, P[c * cstride]);
-  float L = 0.f;
-#pragma unroll 8
-  for (int64_t c = 0; c < n_chunks; ++c) L = fmaf(fast_exp2(P[c * cstride] - M), P[c * cstride + 1], L);
-  const float scale = a.v_scale / L;
-  T* out = reinterpret_cast<T*>(a.out);
-  for (int d = threadIdx.x; d < dh; d += blockDim.x) {
-    float O = 0.f;
-#pragma unroll 8
-    for (int64_t c = 0; c < n_chunks; ++c) O = fmaf(fast_exp2(P[c * cstride] - M), P[c * cstride + 2 + d], O);
-    stf(out, (b * h + hh) * dh + d, O * scale);
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, mloc[c]);
+  float O = 0.f;
+#pragma unroll
+  for (int j = 0; j < kCombineRegs; ++j) {
+    const int c = g + G * j;
+    if (c < nc) O = fmaf(fast_exp2(mloc[c] - M), accv[j], O);
+  }
+  for (int c = g + G * kCombineRegs; active && c < nc; c += G)
+    O = fmaf(fast_exp2(mloc[c] - M), P[(int64_t)c * cstride + 2 + d], O);
+  part[threadIdx.x] = O;
+  __syncthreads();
+  if (threadIdx.x < dh) {
+    float L = 0.f;
+    for (int c = 0; c < nc; ++c) L = fmaf(fast_exp2(mloc[c] - M), lloc[c], L);
+    float tot = 0.f;
+    for (int gg = 0; gg < G; ++gg) tot += part[gg * dh + d];
+    T* out = reinterpret_cast<T*>(a.out);
+    stf(out, (b * h + hh) * dh + d, tot * (a.v_scale / L));
   }
 }
 
@@ -172,21 +204,28 @@ static DecodePlan plan_generic(int64_t ctx_len) {
   DecodePlan p;
   p.kernel = 0;
   p.chunk_tokens = 256;
+  if ((ctx_len + p.chunk_tokens - 1) / p.chunk_tokens > kCombineMaxChunks)
+    p.chunk_tokens = (ctx_len + kCombineMaxChunks - 1) / kCombineMaxChunks;
   p.n_chunks = (ctx_len + p.chunk_tokens - 1) / p.chunk_tokens;
   return p;
 }
 
 // Matrix-core plan: chunks are whole multiples of the tokens one workgroup
-// covers per step (a value block per wave), sized so that about 512
-// workgroups hold full chunks (two per CU); the last chunk of each sequence
+// covers per step (a value block per wave), sized so that about
+// kDecodeTargetWorkgroups hold full chunks; the last chunk of each sequence
 // takes the remainder.
+#ifndef TPA_DECODE_TARGET_WGS
+#define TPA_DECODE_TARGET_WGS 512
+#endif
+constexpr int64_t kDecodeTargetWorkgroups = TPA_DECODE_TARGET_WGS;
 static DecodePlan plan_mfma(const AttnArgs& a, int64_t ctx_len) {
   DecodePlan p;
   p.kernel = 1;
   const int64_t vw = decode_mfma_wave_tokens(a);
   const int64_t units = (ctx_len + vw - 1) / vw;
-  int64_t cu = (a.n_batch * units + 256) / 512;
+  int64_t cu = (a.n_batch * units + kDecodeTargetWorkgroups / 2) / kDecodeTargetWorkgroups;
   if (cu < 1) cu = 1;
+  if ((units + cu - 1) / cu > kCombineMaxChunks) cu = (units + kCombineMaxChunks - 1) / kCombineMaxChunks;
   p.chunk_tokens = cu * vw;
   p.n_chunks = (ctx_len + p.chunk_tokens - 1) / p.chunk_tokens;
   return p;
@@ -230,9 +269,9 @@ hipError_t launch_decode(int dtype, const AttnArgs& a, int64_t ctx_len, const De
   }
   dim3 cgrid((unsigned)a.h, (unsigned)a.n_batch);
   if (dtype == kF32)
-    hipLaunchKernelGGL(decode_combine_kernel<float>, cgrid, dim3(64), 0, st, a, p.n_chunks, wsf);
+    hipLaunchKernelGGL(decode_combine_kernel<float>, cgrid, dim3(kCombineThreads), 0, st, a, p.n_chunks, wsf);
   else
-    hipLaunchKernelGGL(decode_combine_kernel<bf16_t>, cgrid, dim3(64), 0, st, a, p.n_chunks, wsf);
+    hipLaunchKernelGGL(decode_combine_kernel<bf16_t>, cgrid, dim3(kCombineThreads), 0, st, a, p.n_chunks, wsf);
   return hipGetLastError();
 }
 

@@ -21,8 +21,9 @@
 //    4g+j of tile 0 for j<4, of tile 1 for j>=4); B_V goes through a
 //    wave-private LDS tile to be read transposed.
 //
-// The next block's loads are issued before the current block is computed
-// (d_h = 64; at d_h = 128 the registers go to a second resident wave instead).
+// At d_h = 64 each wave keeps two blocks' loads in flight, both issued before
+// the query is formed; at d_h = 128 the registers go to a second resident
+// wave instead.
 // The four waves of a workgroup merge their (m, l, O) through LDS in a fixed
 // order and write one partial per head to the workspace; the combine pass,
 // shared with the general kernel, merges the chunks in index order.  (Merging
@@ -255,9 +256,14 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
   const int last = (int)(t1 - t0) - 1;      // chunk-local index of the last token
   const int nvb = (last + VBT) / VBT;
 
-  // The first block's loads go out before the query is formed.
-  BlockRegs<DH, R, HT> cur;
-  if (wave < nvb) load_block<DH, R, HT>(cur, cb, h, wave * VBT, last, lane);
+  // The first blocks' loads go out before the query is formed (two blocks per
+  // wave at d_h = 64, one at d_h = 128).
+  BlockRegs<DH, R, HT> r0;
+  BlockRegs<DH, R, HT> r1;
+  if (wave < nvb) load_block<DH, R, HT>(r0, cb, h, wave * VBT, last, lane);
+  if constexpr (C::kPrefetch) {
+    if (wave + 4 < nvb) load_block<DH, R, HT>(r1, cb, h, (wave + 4) * VBT, last, lane);
+  }
 
   // ---- query operand, via the query factors staged in LDS (one round trip).
   //      Lane (head = 16*ht + li, slice lg) holds q[head][lg*DH/4 + 8*ks + j].
@@ -316,17 +322,20 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
   }
 
   bf16_t* lbv = reinterpret_cast<bf16_t*>(smem) + wave * 32 * LROW;
-  for (int vb = wave; vb < nvb; vb += 4) {
-    const int tb = vb * VBT;
-    if constexpr (C::kPrefetch) {
-      BlockRegs<DH, R, HT> nxt;
-      const bool more = vb + 4 < nvb;
-      if (more) load_block<DH, R, HT>(nxt, cb, h, tb + 4 * VBT, last, lane);
-      compute_block<DH, R, HT>(cur, lbv, tb, last, lane, qop, m_run, l_run, oacc);
-      if (more) cur = nxt;
-    } else {
-      if (vb != wave) load_block<DH, R, HT>(cur, cb, h, tb, last, lane);
-      compute_block<DH, R, HT>(cur, lbv, tb, last, lane, qop, m_run, l_run, oacc);
+  if constexpr (C::kPrefetch) {
+    // two register sets in flight: blocks vb and vb+4 of this wave
+    for (int vb = wave; vb < nvb; vb += 8) {
+      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, lane, qop, m_run, l_run, oacc);
+      if (vb + 8 < nvb) load_block<DH, R, HT>(r0, cb, h, (vb + 8) * VBT, last, lane);
+      if (vb + 4 < nvb) {
+        compute_block<DH, R, HT>(r1, lbv, (vb + 4) * VBT, last, lane, qop, m_run, l_run, oacc);
+        if (vb + 12 < nvb) load_block<DH, R, HT>(r1, cb, h, (vb + 12) * VBT, last, lane);
+      }
+    }
+  } else {
+    for (int vb = wave; vb < nvb; vb += 4) {
+      if (vb != wave) load_block<DH, R, HT>(r0, cb, h, vb * VBT, last, lane);
+      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, lane, qop, m_run, l_run, oacc);
     }
   }
 

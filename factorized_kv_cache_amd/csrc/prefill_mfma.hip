@@ -9,7 +9,8 @@
 //
 //  * rebuild: the whole workgroup forms k_t = sum_r A_K[t,h,r] B~_K[t,r,:] and
 //    v_t = sum_r A_V[t,h,r] B_V[t,r,:] for the block in fp32, and stores K
-//    row-major and V transposed (V^T[d][t]) in LDS as bf16;
+//    row-major and V transposed (V^T[d][t]) in LDS as bf16; at d_h = 64 the
+//    factors of the next block are loaded while this block is multiplied;
 //  * scores, transposed: S^T[t, q] = K[t,:] . Q[q,:] with K as the A operand
 //    (from LDS) and Q^T as the B operand (registers, formed once), so each
 //    lane's scores belong to one query (its column);
@@ -26,6 +27,28 @@
 
 namespace tpa {
 
+// R consecutive bf16 values, loaded as one 2R-byte word.
+template <int R>
+struct RankWordP;
+template <>
+struct RankWordP<1> { typedef uint16_t type; };
+template <>
+struct RankWordP<2> { typedef uint32_t type; };
+template <>
+struct RankWordP<4> { typedef uint2 type; };
+
+template <int R>
+__device__ __forceinline__ float rank_elem(typename RankWordP<R>::type v, int r) {
+  if constexpr (R == 1) {
+    return bf16_to_f32(v);
+  } else if constexpr (R == 2) {
+    return r ? __uint_as_float(v & 0xffff0000u) : __uint_as_float(v << 16);
+  } else {
+    const uint32_t w = (r < 2) ? v.x : v.y;
+    return (r & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+}
+
 template <int DH>
 struct PrefillMfmaCfg {
   static constexpr int BM = 128;         // queries per workgroup
@@ -35,9 +58,77 @@ struct PrefillMfmaCfg {
   static constexpr int DT = DH / 16;     // d tiles of the value product
   static constexpr int LDK = DH + 8;     // K row stride in LDS (bf16)
   static constexpr int LDV = BN + 4;     // V^T row stride in LDS (bf16), 8-byte aligned rows
+  static constexpr int IT = BN * DH / 8 / 256;  // rebuild items (key, 8 d's) per thread
+  // the next block's factors are loaded during this block's products (d_h = 64;
+  // at d_h = 128 those registers would spill)
+  static constexpr bool kPipelined = DH == 64;
 };
 
-template <int DH>
+// The cached factors one thread needs to rebuild its items of one key block.
+template <int DH, int R>
+struct RebuildRegs {
+  static constexpr int IT = PrefillMfmaCfg<DH>::IT;
+  uint4 bk[IT][R];
+  uint4 bv[IT][R];
+  typename RankWordP<R>::type ak[IT];
+  typename RankWordP<R>::type av[IT];
+};
+
+// Keys past kend are clamped to the last valid key: they are masked out of
+// every score, so only finiteness matters.
+template <int DH, int R>
+__device__ __forceinline__ void load_rebuild(RebuildRegs<DH, R>& g, const AttnArgs& a, int64_t seq0, int hh,
+                                             int64_t k0, int64_t kend) {
+  using C = PrefillMfmaCfg<DH>;
+  typedef typename RankWordP<R>::type W;
+  const bf16_t* AK = reinterpret_cast<const bf16_t*>(a.c_ak);
+  const bf16_t* BK = reinterpret_cast<const bf16_t*>(a.c_bk);
+  const bf16_t* AV = reinterpret_cast<const bf16_t*>(a.c_av);
+  const bf16_t* BV = reinterpret_cast<const bf16_t*>(a.c_bv);
+#pragma unroll
+  for (int it = 0; it < C::IT; ++it) {
+    const int item = threadIdx.x + 256 * it;
+    const int kl = item % C::BN, d0 = (item / C::BN) * 8;
+    int64_t t = k0 + kl;
+    t = t < kend ? t : kend - 1;
+    const int64_t row = seq0 + t;
+    g.ak[it] = *reinterpret_cast<const W*>(AK + (row * a.h + hh) * R);
+    g.av[it] = *reinterpret_cast<const W*>(AV + (row * a.h + hh) * R);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      g.bk[it][r] = *reinterpret_cast<const uint4*>(BK + (row * R + r) * DH + d0);
+      g.bv[it][r] = *reinterpret_cast<const uint4*>(BV + (row * R + r) * DH + d0);
+    }
+  }
+}
+
+template <int DH, int R>
+__device__ __forceinline__ void store_rebuild(const RebuildRegs<DH, R>& g, bf16_t* ks_lds, bf16_t* vt_lds) {
+  using C = PrefillMfmaCfg<DH>;
+#pragma unroll
+  for (int it = 0; it < C::IT; ++it) {
+    const int item = threadIdx.x + 256 * it;
+    const int kl = item % C::BN, d0 = (item / C::BN) * 8;
+    float kv[8], vv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kv[j] = vv[j] = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float ar = rank_elem<R>(g.ak[it], r), vr = rank_elem<R>(g.av[it], r);
+      const bf16x8_t ek = as_bf16x8(g.bk[it][r]), ev = as_bf16x8(g.bv[it][r]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        kv[j] = fmaf(ar, (float)ek[j], kv[j]);
+        vv[j] = fmaf(vr, (float)ev[j], vv[j]);
+      }
+    }
+    *reinterpret_cast<bf16x8_t*>(ks_lds + kl * C::LDK + d0) = pack8(kv);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vt_lds[(d0 + j) * C::LDV + kl] = f32_to_bf16(vv[j]);
+  }
+}
+
+template <int DH, int R>
 __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_qblocks) {
   using C = PrefillMfmaCfg<DH>;
   constexpr int BM = C::BM, BN = C::BN, QT = C::QT, KS = C::KS, DT = C::DT, LDK = C::LDK, LDV = C::LDV;
@@ -50,6 +141,12 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
   const int qb = n_qblocks - 1 - (int)blockIdx.x;       // heaviest first
   const int64_t q0 = (int64_t)qb * BM;
   const int64_t seq0 = b * a.max_seq;
+  const int64_t last_q = (q0 + BM < a.S ? q0 + BM : a.S) - 1;
+  const int64_t kend = a.causal ? a.start_pos + last_q + 1 : a.start_pos + a.S;
+
+  // The first key block's factors go out before the query is formed.
+  RebuildRegs<DH, R> rg;
+  if constexpr (C::kPipelined) load_rebuild<DH, R>(rg, a, seq0, hh, 0, kend);
 
   // ---- query operand: lane (query q0 + 32*wave + 16*qt + li, slice lg)
   bf16x8_t qop[QT][KS];
@@ -95,43 +192,18 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
     for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int64_t last_q = (q0 + BM < a.S ? q0 + BM : a.S) - 1;
-  const int64_t kend = a.causal ? a.start_pos + last_q + 1 : a.start_pos + a.S;
-  // first position of this wave's queries, and of the workgroup's
+  // first position of this wave's queries
   const int64_t wpos0 = a.start_pos + q0 + 32 * wave;
-  const bf16_t* AK = reinterpret_cast<const bf16_t*>(a.c_ak);
-  const bf16_t* BK = reinterpret_cast<const bf16_t*>(a.c_bk);
-  const bf16_t* AV = reinterpret_cast<const bf16_t*>(a.c_av);
-  const bf16_t* BV = reinterpret_cast<const bf16_t*>(a.c_bv);
 
   for (int64_t k0 = 0; k0 < kend; k0 += BN) {
-    // ---- rebuild K and V^T of this head for keys k0 .. k0+63 (items: key, 8 d's)
-    for (int item = threadIdx.x; item < BN * (DH / 8); item += blockDim.x) {
-      const int kl = item % BN, d0 = (item / BN) * 8;
-      const int64_t t = k0 + kl;
-      float kv[8], vv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) kv[j] = vv[j] = 0.f;
-      if (t < kend) {
-        const int64_t row = seq0 + t;
-        for (int r = 0; r < a.rk; ++r) {
-          const float ar = bf16_to_f32(AK[(row * h + hh) * a.rk + r]);
-          const bf16x8_t e = as_bf16x8(*reinterpret_cast<const uint4*>(BK + (row * a.rk + r) * DH + d0));
-#pragma unroll
-          for (int j = 0; j < 8; ++j) kv[j] = fmaf(ar, (float)e[j], kv[j]);
-        }
-        for (int r = 0; r < a.rv; ++r) {
-          const float ar = bf16_to_f32(AV[(row * h + hh) * a.rv + r]);
-          const bf16x8_t e = as_bf16x8(*reinterpret_cast<const uint4*>(BV + (row * a.rv + r) * DH + d0));
-#pragma unroll
-          for (int j = 0; j < 8; ++j) vv[j] = fmaf(ar, (float)e[j], vv[j]);
-        }
-      }
-      *reinterpret_cast<bf16x8_t*>(ks_lds + kl * LDK + d0) = pack8(kv);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) vt_lds[(d0 + j) * LDV + kl] = f32_to_bf16(vv[j]);
-    }
+    // ---- rebuild K and V^T of this head for keys k0 .. k0+63 from the
+    //      registers, then start loading the next block's factors
+    if constexpr (!C::kPipelined) load_rebuild<DH, R>(rg, a, seq0, hh, k0, kend);
+    store_rebuild<DH, R>(rg, ks_lds, vt_lds);
     __syncthreads();
+    if constexpr (C::kPipelined) {
+      if (k0 + BN < kend) load_rebuild<DH, R>(rg, a, seq0, hh, k0 + BN, kend);
+    }
 
     // ---- scores S^T[key, query] for the block's 4 key tiles
     f32x4_t sacc[4][QT];
@@ -239,6 +311,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
 bool prefill_mfma_supported(int dtype, const AttnArgs& a) {
   if (dtype != kBF16) return false;
   if (!(a.d_h == 64 || a.d_h == 128)) return false;
+  if (a.rk != a.rv || !(a.rk == 1 || a.rk == 2 || a.rk == 4)) return false;
   const void* ptrs[4] = {a.b_q, a.c_bk, a.c_bv, a.out};   // read/written 8 or 16 bytes at a time
   for (int i = 0; i < 4; ++i)
     if (((uintptr_t)ptrs[i]) % 16) return false;
@@ -248,10 +321,18 @@ bool prefill_mfma_supported(int dtype, const AttnArgs& a) {
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t st) {
   const int nqb = (int)((a.S + 127) / 128);
   const dim3 grid((unsigned)nqb, (unsigned)a.h, (unsigned)a.n_batch);
-  if (a.d_h == 64)
-    hipLaunchKernelGGL(prefill_mfma_kernel<64>, grid, dim3(256), 0, st, a, nqb);
-  else
-    hipLaunchKernelGGL(prefill_mfma_kernel<128>, grid, dim3(256), 0, st, a, nqb);
+#define TPA_PREFILL_LAUNCH(DH_, R_) \
+  hipLaunchKernelGGL((prefill_mfma_kernel<DH_, R_>), grid, dim3(256), 0, st, a, nqb)
+  if (a.d_h == 64) {
+    if (a.rk == 1) TPA_PREFILL_LAUNCH(64, 1);
+    else if (a.rk == 2) TPA_PREFILL_LAUNCH(64, 2);
+    else TPA_PREFILL_LAUNCH(64, 4);
+  } else {
+    if (a.rk == 1) TPA_PREFILL_LAUNCH(128, 1);
+    else if (a.rk == 2) TPA_PREFILL_LAUNCH(128, 2);
+    else TPA_PREFILL_LAUNCH(128, 4);
+  }
+#undef TPA_PREFILL_LAUNCH
   return hipGetLastError();
 }
 

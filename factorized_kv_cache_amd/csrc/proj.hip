@@ -92,19 +92,22 @@ __global__ void __launch_bounds__(256) proj_generic_kernel(ProjArgs a) {
 
 // ---------------------------------------------------------------------------
 // Few tokens (decode): bound by reading the weights once.  One workgroup owns
-// 16 weight rows; its four waves split K.  The product is taken as
+// 16 weight rows; its eight waves split K.  The product is taken as
 // D[n, m] = W[n, :] . X[m, :], weight rows as the A operand and tokens as the B
-// operand, both read straight from memory (K-contiguous).  The four partial
-// tiles are summed in LDS in wave order, then the epilogue stores pairs.
+// operand, both read straight from memory (K-contiguous), up to eight k-steps'
+// loads issued together.  The eight partial tiles are summed in LDS in wave
+// order, then the epilogue stores pairs.
 // ---------------------------------------------------------------------------
+constexpr int kSkinnyWaves = 8;
+
 template <int MT>
-__global__ void __launch_bounds__(256) proj_skinny_kernel(ProjArgs a) {
-  __shared__ float red[4][16][16 * MT + 1];
+__global__ void __launch_bounds__(64 * kSkinnyWaves) proj_skinny_kernel(ProjArgs a) {
+  __shared__ float red[kSkinnyWaves][16][16 * MT + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int K = (int)a.K, M = (int)a.M, N = (int)a.N;
-  const int kq = K / 4;
+  const int kq = K / kSkinnyWaves;
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
   const bf16_t* W = reinterpret_cast<const bf16_t*>(a.w);
   const int nrow = (n0 + li < N) ? n0 + li : N - 1;
@@ -118,19 +121,18 @@ __global__ void __launch_bounds__(256) proj_skinny_kernel(ProjArgs a) {
   f32x4_t acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // four k-steps per trip, their loads issued together (steps past kq repeat
-  // the last step's address and are not multiplied)
-  for (int k = 0; k < kq; k += 128) {
-    uint4 wv[4], xv[4][MT];
+  // eight k-steps per trip (steps past kq repeat the last address, unused)
+  for (int k = 0; k < kq; k += 256) {
+    uint4 wv[8], xv[8][MT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const int ku = k + 32 * u < kq ? k + 32 * u : kq - 32;
       wv[u] = *reinterpret_cast<const uint4*>(wrow + ku);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) xv[u][mt] = *reinterpret_cast<const uint4*>(xrow[mt] + ku);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       if (k + 32 * u >= kq) break;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16(as_bf16x8(wv[u]), as_bf16x8(xv[u][mt]), acc[mt]);
@@ -147,7 +149,7 @@ __global__ void __launch_bounds__(256) proj_skinny_kernel(ProjArgs a) {
     if (m >= M || n >= N) continue;
     float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kSkinnyWaves; ++w) {
       v0 += red[w][2 * p][m];
       v1 += red[w][2 * p + 1][m];
     }
@@ -253,13 +255,13 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 hipError_t launch_factor_proj(int dtype, const ProjArgs& a, hipStream_t st) {
   if (dtype == kBF16 && aligned16(a.x) && aligned16(a.w) && a.K % 64 == 0) {
-    if (a.M <= 64 && a.K % 128 == 0) {
-      const dim3 grid((unsigned)((a.N + 15) / 16));
+    if (a.M <= 64 && a.K % (32 * kSkinnyWaves) == 0) {
+      const dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * kSkinnyWaves);
       switch ((a.M + 15) / 16) {
-        case 1: hipLaunchKernelGGL(proj_skinny_kernel<1>, grid, dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL(proj_skinny_kernel<2>, grid, dim3(256), 0, st, a); break;
-        case 3: hipLaunchKernelGGL(proj_skinny_kernel<3>, grid, dim3(256), 0, st, a); break;
-        default: hipLaunchKernelGGL(proj_skinny_kernel<4>, grid, dim3(256), 0, st, a); break;
+        case 1: hipLaunchKernelGGL(proj_skinny_kernel<1>, grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL(proj_skinny_kernel<2>, grid, block, 0, st, a); break;
+        case 3: hipLaunchKernelGGL(proj_skinny_kernel<3>, grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL(proj_skinny_kernel<4>, grid, block, 0, st, a); break;
       }
     } else {
       const dim3 grid((unsigned)((a.M + kPBM - 1) / kPBM), (unsigned)((a.N + kPBN - 1) / kPBN));

@@ -321,3 +321,48 @@ def test_prefill_full_size_sampled_rows(wl_name, B, S, n_rows):
     od = oracle_dims(dims)
     ref = O.prefill(oracle_query(fq, dims), oracle_cache(kv, od, B, S), od, B, S, 0, True, rows=rows)
     assert_close(out[:, rows], ref[:, rows], "bf16", f"prefill {wl_name} sampled rows")
+
+
+def test_decode_step_graph_replay_matches_eager():
+    """The decode step (projection into the cache slot, decode attention) captured
+    as a HIP graph and replayed several times, with eager work and synchronisation
+    between replays, gives the eager result bit for bit every time."""
+    require_gpu()
+    dims = D(1024, 16, 64, 6, 2, 2, "bf16")
+    B, ctx = 8, 1500
+    announce("decode step graph replay")
+    sh = shape_of(dims)
+    kv = I.factors(sh, B, ctx - 1, seed=111, dtype="bf16", with_query=False)
+    w = I.weights(sh, seed=111, dtype="bf16")
+    wp = T.pack_weights({k: v.cuda() for k, v in w.items()}, False)
+    x_new = I.activations(B, 1, 1024, seed=112, dtype="bf16").cuda()
+    cache = T.new_cache(dims, B, ctx)
+    fill_cache(cache, kv)
+    qf = T.new_factors(dims, B, 1)
+    slot = cache.slot_factors(ctx - 1)
+    into = T.Factors(qf.a_q, qf.b_q, slot.a_k, slot.b_k, slot.a_v, slot.b_v, 0, ctx)
+    q = T.Factors(qf.a_q[:, 0], qf.b_q[:, 0], None, None, None, None)
+    ws = T.new_workspace(dims, B, ctx)
+    out = torch.empty(B, 16 * 64, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        T.tpa_factor_proj(dims, x_new, wp, into, start_pos=ctx - 1)
+        T.tpa_decode_attn(dims, q, cache, ctx, ws, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        out.zero_()
+        slot.a_k.zero_()                      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager step"
