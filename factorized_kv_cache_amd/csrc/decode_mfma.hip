@@ -35,6 +35,24 @@
 
 namespace tpa {
 
+// Narrowing to bf16 (round to nearest, ties to even, NaNs kept quiet) with
+// integer operations.  This kernel is bound by HBM, not by its VALU; with the
+// packed hardware conversion the compiler schedules the d_h = 128 value loop
+// past the two-waves-per-SIMD register budget (spills), with this form it fits.
+__device__ __forceinline__ uint16_t bf16_rne_int(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ bf16x8_t pack8_int(const float* v) {
+  u16x8_t u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) u[j] = bf16_rne_int(v[j]);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
 // R consecutive bf16 values, loaded as one 2R-byte word.
 template <int R>
 struct RankWord;
@@ -213,7 +231,7 @@ __device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf1
         for (int rr = 0; rr < R; ++rr) cv[st * 4 + k * R + rr] = p * av[st][k * R + rr];
       }
     l_run[ht] = l_run[ht] * alpha + psum;
-    cop[ht] = pack8(cv);
+    cop[ht] = pack8_int(cv);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[ht][dt] *= alpha;
   }
@@ -305,7 +323,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] *= a.q_scale;
         }
-        qop[ht][ks] = pack8(v);
+        qop[ht][ks] = pack8_int(v);
       }
     }
     __syncthreads();
@@ -408,7 +426,7 @@ bool decode_mfma_supported(int dtype, const AttnArgs& a) {
   if (a.rk != a.rv || !(a.rk == 1 || a.rk == 2 || a.rk == 4)) return false;
   if (!(a.d_h == 64 || a.d_h == 128)) return false;
   if (a.h > 64) return false;
-  if (a.d_h == 128 && a.h > 48) return false;  // merge buffer would pass 64 KB of LDS
+  if (a.d_h == 128 && a.h > 32) return false;  // three head tiles at d_h = 128 spill registers
   const size_t qbytes = (a.rq ? (size_t)a.rq * (a.h + a.d_h) : (size_t)a.h * a.d_h) * sizeof(bf16_t);
   if (qbytes > kDecodeMfmaQueryLds) return false;
   const void* ptrs[5] = {a.b_q, a.c_ak, a.c_bk, a.c_av, a.c_bv};
@@ -436,9 +454,13 @@ static void launch_dh_r(const AttnArgs& a, int64_t ctx_len, int64_t chunk, int64
   switch (ht) {
     case 1: launch_cfg<DH, R, 1>(a, ctx_len, chunk, n_chunks, ws, st); break;
     case 2: launch_cfg<DH, R, 2>(a, ctx_len, chunk, n_chunks, ws, st); break;
-    case 3: launch_cfg<DH, R, 3>(a, ctx_len, chunk, n_chunks, ws, st); break;
     default:
-      if constexpr (DH == 64) launch_cfg<DH, R, 4>(a, ctx_len, chunk, n_chunks, ws, st);
+      if constexpr (DH == 64) {
+        if (ht == 3)
+          launch_cfg<DH, R, 3>(a, ctx_len, chunk, n_chunks, ws, st);
+        else
+          launch_cfg<DH, R, 4>(a, ctx_len, chunk, n_chunks, ws, st);
+      }
       break;
   }
 }

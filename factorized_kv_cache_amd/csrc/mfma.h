@@ -25,9 +25,8 @@ __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ bf16x8_t pack8(const float* v) {
-  u16x8_t u;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) u[j] = f32_to_bf16(v[j]);
+  const uint4 u = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                             pack_bf16x2(v[6], v[7]));
   return __builtin_bit_cast(bf16x8_t, u);
 }
 

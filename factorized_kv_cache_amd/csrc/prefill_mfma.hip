@@ -21,7 +21,7 @@
 //    lane group g is key 4g+j of one 16-key tile for j<4, of the next for j>=4),
 //    and the matching V^T rows are two 8-byte LDS reads.
 //
-// Query blocks are scheduled heaviest (most keys) first.
+// Query blocks are scheduled heaviest (most keys) first, evenly across XCDs.
 #include "kernels.h"
 #include "mfma.h"
 
@@ -136,9 +136,16 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
   __shared__ __align__(16) bf16_t vt_lds[DH * LDV];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int h = a.h, hh = blockIdx.y;
-  const int64_t b = blockIdx.z;
-  const int qb = n_qblocks - 1 - (int)blockIdx.x;       // heaviest first
+  // One-dimensional grid.  Work items (query block, head, sequence) in order of
+  // decreasing key count are numbered by the linear workgroup id; since
+  // workgroups go to the XCDs round-robin by that id, every XCD gets an equal
+  // share of every query block, heaviest first.
+  const int h = a.h;
+  const int64_t hb = (int64_t)h * a.n_batch;
+  const int64_t L = blockIdx.x;
+  const int qb = n_qblocks - 1 - (int)(L / hb);
+  const int hh = (int)(L % h);
+  const int64_t b = (L % hb) / h;
   const int64_t q0 = (int64_t)qb * BM;
   const int64_t seq0 = b * a.max_seq;
   const int64_t last_q = (q0 + BM < a.S ? q0 + BM : a.S) - 1;
@@ -310,6 +317,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
 
 bool prefill_mfma_supported(int dtype, const AttnArgs& a) {
   if (dtype != kBF16) return false;
+  if ((a.S + 127) / 128 * (int64_t)a.h * a.n_batch >= ((int64_t)1 << 31)) return false;
   if (!(a.d_h == 64 || a.d_h == 128)) return false;
   if (a.rk != a.rv || !(a.rk == 1 || a.rk == 2 || a.rk == 4)) return false;
   const void* ptrs[4] = {a.b_q, a.c_bk, a.c_bv, a.out};   // read/written 8 or 16 bytes at a time
@@ -320,7 +328,7 @@ bool prefill_mfma_supported(int dtype, const AttnArgs& a) {
 
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t st) {
   const int nqb = (int)((a.S + 127) / 128);
-  const dim3 grid((unsigned)nqb, (unsigned)a.h, (unsigned)a.n_batch);
+  const dim3 grid((unsigned)((int64_t)nqb * a.h * a.n_batch));
 #define TPA_PREFILL_LAUNCH(DH_, R_) \
   hipLaunchKernelGGL((prefill_mfma_kernel<DH_, R_>), grid, dim3(256), 0, st, a, nqb)
   if (a.d_h == 64) {
