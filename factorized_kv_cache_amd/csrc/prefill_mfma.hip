@@ -8,18 +8,24 @@
 // waves owns 32 of them (two 16-query tiles).  For every block of 64 keys:
 //
 //  * rebuild: the whole workgroup forms k_t = sum_r A_K[t,h,r] B~_K[t,r,:] and
-//    v_t = sum_r A_V[t,h,r] B_V[t,r,:] for the block in fp32, and stores K
-//    row-major and V transposed (V^T[d][t]) in LDS as bf16; at d_h = 64 the
-//    factors of the next block are loaded while this block is multiplied;
+//    v_t = sum_r A_V[t,h,r] B_V[t,r,:] for the block (rank pairs through
+//    v_dot2_f32_bf16, fp32 sums), and stores K row-major and V transposed
+//    (V^T[d][t]) in LDS as bf16.  The tiles are double-buffered: block i+1 is
+//    rebuilt while block i is multiplied (at d_h = 64 from factors loaded one
+//    block earlier still), so each block costs one barrier;
 //  * scores, transposed: S^T[t, q] = K[t,:] . Q[q,:] with K as the A operand
 //    (from LDS) and Q^T as the B operand (registers, formed once), so each
 //    lane's scores belong to one query (its column);
 //  * online softmax per query in base 2 (the scale log2(e) / (R_Q R_K sqrt(d_h))
-//    is folded into Q), masking only on blocks that reach past a query;
+//    is folded into Q), masking only on blocks that reach past a query.  The
+//    running maximum moves only when a block's maximum exceeds it by more than
+//    8 (then every probability stays below 2^8), so most blocks skip the
+//    rescale; the result does not depend on the reference maximum;
 //  * values, transposed: O^T[d, q] += V^T[d, t] P^T[t, q]; the score tiles'
 //    output registers are already the B operand of this product (k-slot j of
 //    lane group g is key 4g+j of one 16-key tile for j<4, of the next for j>=4),
-//    and the matching V^T rows are two 8-byte LDS reads.
+//    and the matching V^T rows are two 8-byte LDS reads.  One extra V^T tile
+//    holds a row of ones, so the same product also yields sum_t p_t.
 //
 // Query blocks are scheduled heaviest (most keys) first, evenly across XCDs.
 #include "kernels.h"
@@ -37,15 +43,69 @@ struct RankWordP<2> { typedef uint32_t type; };
 template <>
 struct RankWordP<4> { typedef uint2 type; };
 
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a), __builtin_bit_cast(bf16x2_v, b), c, false);
+}
+
+// sum_r a_r * b_r[j] for the 8 elements j of one 16-byte slice per rank.
+// Ranks are paired: word w of rank r holds elements (2w, 2w+1); v_perm_b32
+// regroups them as (rank r, rank r+1) pairs for v_dot2_f32_bf16.
+#ifndef TPA_PF_DOT2
+#define TPA_PF_DOT2 1
+#endif
+#ifndef TPA_PF_LAZY
+#define TPA_PF_LAZY 1
+#endif
+
 template <int R>
-__device__ __forceinline__ float rank_elem(typename RankWordP<R>::type v, int r) {
-  if constexpr (R == 1) {
-    return bf16_to_f32(v);
-  } else if constexpr (R == 2) {
-    return r ? __uint_as_float(v & 0xffff0000u) : __uint_as_float(v << 16);
+__device__ __forceinline__ void factor_combine(typename RankWordP<R>::type a, const uint4 (&b)[R], float (&out)[8]) {
+  if constexpr (R == 1 || !TPA_PF_DOT2) {
+    float ar[R];
+    if constexpr (R == 1) ar[0] = bf16_to_f32(a);
+    else if constexpr (R == 2) { ar[0] = __uint_as_float(a << 16); ar[1] = __uint_as_float(a & 0xffff0000u); }
+    else {
+      ar[0] = __uint_as_float(a.x << 16); ar[1] = __uint_as_float(a.x & 0xffff0000u);
+      ar[2] = __uint_as_float(a.y << 16); ar[3] = __uint_as_float(a.y & 0xffff0000u);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t w[4] = {b[r].x, b[r].y, b[r].z, b[r].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        out[2 * q] = fmaf(ar[r], __uint_as_float(w[q] << 16), out[2 * q]);
+        out[2 * q + 1] = fmaf(ar[r], __uint_as_float(w[q] & 0xffff0000u), out[2 * q + 1]);
+      }
+    }
+  } else if constexpr (R == 1) {
+    const uint32_t w[4] = {b[0].x, b[0].y, b[0].z, b[0].w};
+    const float a0 = bf16_to_f32(a);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      out[2 * q] = a0 * __uint_as_float(w[q] << 16);
+      out[2 * q + 1] = a0 * __uint_as_float(w[q] & 0xffff0000u);
+    }
   } else {
-    const uint32_t w = (r < 2) ? v.x : v.y;
-    return (r & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = 0.f;
+#pragma unroll
+    for (int rp = 0; rp < R / 2; ++rp) {
+      uint32_t apair;
+      if constexpr (R == 2) apair = a;
+      else apair = rp ? a.y : a.x;
+      const uint32_t w0[4] = {b[2 * rp].x, b[2 * rp].y, b[2 * rp].z, b[2 * rp].w};
+      const uint32_t w1[4] = {b[2 * rp + 1].x, b[2 * rp + 1].y, b[2 * rp + 1].z, b[2 * rp + 1].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = __builtin_amdgcn_perm(w1[q], w0[q], 0x05040100u);  // (r0[2q], r1[2q])
+        const uint32_t hi = __builtin_amdgcn_perm(w1[q], w0[q], 0x07060302u);  // (r0[2q+1], r1[2q+1])
+        out[2 * q] = dot2_bf16(lo, apair, out[2 * q]);
+        out[2 * q + 1] = dot2_bf16(hi, apair, out[2 * q + 1]);
+      }
+    }
   }
 }
 
@@ -55,24 +115,37 @@ struct PrefillMfmaCfg {
   static constexpr int BN = 64;          // keys per block
   static constexpr int QT = 2;           // 16-query tiles per wave
   static constexpr int KS = DH / 32;     // k-steps of the score product
-  static constexpr int DT = DH / 16;     // d tiles of the value product
+  static constexpr int DT = DH / 16;     // d tiles of the value product (one more holds the ones row)
   static constexpr int LDK = DH + 8;     // K row stride in LDS (bf16)
   static constexpr int LDV = BN + 4;     // V^T row stride in LDS (bf16), 8-byte aligned rows
-  static constexpr int IT = BN * DH / 8 / 256;  // rebuild items (key, 8 d's) per thread
-  // the next block's factors are loaded during this block's products (d_h = 64;
-  // at d_h = 128 those registers would spill)
+  static constexpr int IT = DH / 64;     // rebuild items (2 keys x 8 d's) per thread
+  static constexpr int KTILE = BN * LDK;            // bf16 elements of one K buffer
+  static constexpr int VTILE = (DH + 16) * LDV;     // bf16 elements of one V^T buffer
+  static constexpr size_t kLds = (size_t)2 * (KTILE + VTILE) * sizeof(bf16_t);
+  static constexpr float kRescaleSlack = 8.f;       // log2 units
+  // factors are loaded a block ahead at d_h = 64; at d_h = 128 (two items per
+  // thread) those registers would spill, so each block's are loaded just
+  // before its rebuild
   static constexpr bool kPipelined = DH == 64;
 };
 
-// The cached factors one thread needs to rebuild its items of one key block.
+// The cached factors one thread needs for its rebuild items of one key block:
+// keys 2*kp and 2*kp+1, d slice d0 .. d0+7.
 template <int DH, int R>
 struct RebuildRegs {
   static constexpr int IT = PrefillMfmaCfg<DH>::IT;
-  uint4 bk[IT][R];
-  uint4 bv[IT][R];
-  typename RankWordP<R>::type ak[IT];
-  typename RankWordP<R>::type av[IT];
+  uint4 bk[IT][2][R];
+  uint4 bv[IT][2][R];
+  typename RankWordP<R>::type ak[IT][2];
+  typename RankWordP<R>::type av[IT][2];
 };
+
+template <int DH>
+__device__ __forceinline__ void rebuild_item(int it, int& kp, int& d0) {
+  const int item = threadIdx.x + 256 * it;
+  kp = item % 32;
+  d0 = (item / 32) * 8;
+}
 
 // Keys past kend are clamped to the last valid key: they are masked out of
 // every score, so only finiteness matters.
@@ -87,17 +160,20 @@ __device__ __forceinline__ void load_rebuild(RebuildRegs<DH, R>& g, const AttnAr
   const bf16_t* BV = reinterpret_cast<const bf16_t*>(a.c_bv);
 #pragma unroll
   for (int it = 0; it < C::IT; ++it) {
-    const int item = threadIdx.x + 256 * it;
-    const int kl = item % C::BN, d0 = (item / C::BN) * 8;
-    int64_t t = k0 + kl;
-    t = t < kend ? t : kend - 1;
-    const int64_t row = seq0 + t;
-    g.ak[it] = *reinterpret_cast<const W*>(AK + (row * a.h + hh) * R);
-    g.av[it] = *reinterpret_cast<const W*>(AV + (row * a.h + hh) * R);
+    int kp, d0;
+    rebuild_item<DH>(it, kp, d0);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      g.bk[it][r] = *reinterpret_cast<const uint4*>(BK + (row * R + r) * DH + d0);
-      g.bv[it][r] = *reinterpret_cast<const uint4*>(BV + (row * R + r) * DH + d0);
+    for (int k = 0; k < 2; ++k) {
+      int64_t t = k0 + 2 * kp + k;
+      t = t < kend ? t : kend - 1;
+      const int64_t row = seq0 + t;
+      g.ak[it][k] = *reinterpret_cast<const W*>(AK + (row * a.h + hh) * R);
+      g.av[it][k] = *reinterpret_cast<const W*>(AV + (row * a.h + hh) * R);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        g.bk[it][k][r] = *reinterpret_cast<const uint4*>(BK + (row * R + r) * DH + d0);
+        g.bv[it][k][r] = *reinterpret_cast<const uint4*>(BV + (row * R + r) * DH + d0);
+      }
     }
   }
 }
@@ -107,24 +183,18 @@ __device__ __forceinline__ void store_rebuild(const RebuildRegs<DH, R>& g, bf16_
   using C = PrefillMfmaCfg<DH>;
 #pragma unroll
   for (int it = 0; it < C::IT; ++it) {
-    const int item = threadIdx.x + 256 * it;
-    const int kl = item % C::BN, d0 = (item / C::BN) * 8;
-    float kv[8], vv[8];
+    int kp, d0;
+    rebuild_item<DH>(it, kp, d0);
+    float kv[2][8], vv[2][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kv[j] = vv[j] = 0.f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float ar = rank_elem<R>(g.ak[it], r), vr = rank_elem<R>(g.av[it], r);
-      const bf16x8_t ek = as_bf16x8(g.bk[it][r]), ev = as_bf16x8(g.bv[it][r]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        kv[j] = fmaf(ar, (float)ek[j], kv[j]);
-        vv[j] = fmaf(vr, (float)ev[j], vv[j]);
-      }
+    for (int k = 0; k < 2; ++k) {
+      factor_combine<R>(g.ak[it][k], g.bk[it][k], kv[k]);
+      factor_combine<R>(g.av[it][k], g.bv[it][k], vv[k]);
+      *reinterpret_cast<bf16x8_t*>(ks_lds + (2 * kp + k) * C::LDK + d0) = pack8(kv[k]);
     }
-    *reinterpret_cast<bf16x8_t*>(ks_lds + kl * C::LDK + d0) = pack8(kv);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vt_lds[(d0 + j) * C::LDV + kl] = f32_to_bf16(vv[j]);
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint32_t*>(vt_lds + (d0 + j) * C::LDV + 2 * kp) = pack_bf16x2(vv[0][j], vv[1][j]);
   }
 }
 
@@ -132,8 +202,11 @@ template <int DH, int R>
 __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_qblocks) {
   using C = PrefillMfmaCfg<DH>;
   constexpr int BM = C::BM, BN = C::BN, QT = C::QT, KS = C::KS, DT = C::DT, LDK = C::LDK, LDV = C::LDV;
-  __shared__ __align__(16) bf16_t ks_lds[BN * LDK];
-  __shared__ __align__(16) bf16_t vt_lds[DH * LDV];
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16_t* const lds = reinterpret_cast<bf16_t*>(smem);
+  // buffer i: K at lds + i*KTILE, V^T at lds + 2*KTILE + i*VTILE
+#define KS_BUF(i) (lds + (i) * C::KTILE)
+#define VT_BUF(i) (lds + 2 * C::KTILE + (i) * C::VTILE)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
   // One-dimensional grid.  Work items (query block, head, sequence) in order of
@@ -150,10 +223,19 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
   const int64_t seq0 = b * a.max_seq;
   const int64_t last_q = (q0 + BM < a.S ? q0 + BM : a.S) - 1;
   const int64_t kend = a.causal ? a.start_pos + last_q + 1 : a.start_pos + a.S;
+  const int nblk = (int)((kend + BN - 1) / BN);
 
-  // The first key block's factors go out before the query is formed.
+  // The first key block's factors go out before anything else.
   RebuildRegs<DH, R> rg;
-  if constexpr (C::kPipelined) load_rebuild<DH, R>(rg, a, seq0, hh, 0, kend);
+  load_rebuild<DH, R>(rg, a, seq0, hh, 0, kend);
+
+  // The ones row (and fifteen zero rows) of the extra V^T tile, in both buffers.
+  for (int i = threadIdx.x; i < 16 * BN; i += blockDim.x) {
+    const int rr = i / BN, col = i % BN;
+    const bf16_t v = rr == 0 ? (bf16_t)0x3f80 : (bf16_t)0;
+    VT_BUF(0)[(DH + rr) * LDV + col] = v;
+    VT_BUF(1)[(DH + rr) * LDV + col] = v;
+  }
 
   // ---- query operand: lane (query q0 + 32*wave + 16*qt + li, slice lg)
   bf16x8_t qop[QT][KS];
@@ -189,28 +271,27 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
     }
   }
 
-  float m_run[QT], l_run[QT];
-  f32x4_t oacc[QT][DT];
+  float m_run[QT];
+  f32x4_t oacc[QT][DT + 1];     // tile DT: row 0 accumulates sum_t p_t
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     m_run[qt] = -INFINITY;
-    l_run[qt] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt <= DT; ++dt) oacc[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // first position of this wave's queries
-  const int64_t wpos0 = a.start_pos + q0 + 32 * wave;
+  // block 0 into buffer 0; block 1's factors go out (pipelined form)
+  store_rebuild<DH, R>(rg, KS_BUF(0), VT_BUF(0));
+  if constexpr (C::kPipelined) {
+    if (nblk > 1) load_rebuild<DH, R>(rg, a, seq0, hh, BN, kend);
+  }
+  __syncthreads();
 
-  for (int64_t k0 = 0; k0 < kend; k0 += BN) {
-    // ---- rebuild K and V^T of this head for keys k0 .. k0+63 from the
-    //      registers, then start loading the next block's factors
-    if constexpr (!C::kPipelined) load_rebuild<DH, R>(rg, a, seq0, hh, k0, kend);
-    store_rebuild<DH, R>(rg, ks_lds, vt_lds);
-    __syncthreads();
-    if constexpr (C::kPipelined) {
-      if (k0 + BN < kend) load_rebuild<DH, R>(rg, a, seq0, hh, k0 + BN, kend);
-    }
+  const int64_t wpos0 = a.start_pos + q0 + 32 * wave;   // first position of this wave's queries
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int64_t k0 = (int64_t)blk * BN;
+    const bf16_t* ks_lds = KS_BUF(blk & 1);
+    const bf16_t* vt_lds = VT_BUF(blk & 1);
 
     // ---- scores S^T[key, query] for the block's 4 key tiles
     f32x4_t sacc[4][QT];
@@ -245,7 +326,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
           }
     }
 
-    // ---- online softmax per query, P^T operands
+    // ---- online softmax per query (lazy rescale), P^T operands
     bf16x8_t pop[QT][2];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
@@ -256,31 +337,28 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
         for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, sacc[kt][qt][i]);
       bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      const float m_new = fmaxf(m_run[qt], bmax);
-      // a query with no visible key yet keeps m = -inf; its p and alpha are 0 and 1
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[qt] - m_use);
-      m_run[qt] = m_new;
-      float psum = 0.f;
+      const bool grow = bmax > m_run[qt] + (TPA_PF_LAZY ? C::kRescaleSlack : 0.f);
+      if (__any(grow)) {
+        const float m_new = grow ? bmax : m_run[qt];
+        const float alpha = fast_exp2(m_run[qt] - m_new);   // 0 on the first block, 1 where m stays
+        m_run[qt] = m_new;
+#pragma unroll
+        for (int dt = 0; dt <= DT; ++dt) oacc[qt][dt] *= alpha;
+      }
+      // a query with no visible key yet keeps m = -inf; its probabilities are 0
+      const float m_use = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float pv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = fast_exp2(sacc[2 * kb + (j >> 2)][qt][j & 3] - m_use);
-          pv[j] = p;
-          psum += p;
-        }
+        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(sacc[2 * kb + (j >> 2)][qt][j & 3] - m_use);
         pop[qt][kb] = pack8(pv);
       }
-      l_run[qt] = l_run[qt] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[qt][dt] *= alpha;
     }
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T (and the ones row: sum_t p_t)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt <= DT; ++dt) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16_t* vrow = vt_lds + (dt * 16 + li) * LDV + kb * 32 + 4 * lg;
@@ -291,16 +369,27 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
         for (int qt = 0; qt < QT; ++qt) oacc[qt][dt] = mfma_bf16(vf, pop[qt][kb], oacc[qt][dt]);
       }
     }
+
+    // ---- rebuild the next block into the other buffer; its factors were
+    //      loaded a block ago.  Start loading the block after it.
+    if (blk + 1 < nblk) {
+      if constexpr (!C::kPipelined) load_rebuild<DH, R>(rg, a, seq0, hh, k0 + BN, kend);
+      store_rebuild<DH, R>(rg, KS_BUF((blk + 1) & 1), VT_BUF((blk + 1) & 1));
+      if constexpr (C::kPipelined) {
+        if (blk + 2 < nblk) load_rebuild<DH, R>(rg, a, seq0, hh, k0 + 2 * BN, kend);
+      }
+    }
     __syncthreads();
   }
+#undef KS_BUF
+#undef VT_BUF
 
-  // ---- normalise and store: lane holds d = 16*dt + 4*lg + i of its query
+  // ---- normalise and store: lane holds d = 16*dt + 4*lg + i of its query;
+  //      sum_t p_t of query li sits in lane li (row 0 of the ones tile)
   bf16_t* out = reinterpret_cast<bf16_t*>(a.out);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float l = l_run[qt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = __shfl(oacc[qt][DT][0], li);
     const float inv = a.v_scale / l;
     const int64_t s = q0 + 32 * wave + 16 * qt + li;
     if (s < a.S) {
@@ -320,6 +409,7 @@ bool prefill_mfma_supported(int dtype, const AttnArgs& a) {
   if ((a.S + 127) / 128 * (int64_t)a.h * a.n_batch >= ((int64_t)1 << 31)) return false;
   if (!(a.d_h == 64 || a.d_h == 128)) return false;
   if (a.rk != a.rv || !(a.rk == 1 || a.rk == 2 || a.rk == 4)) return false;
+  if (a.d_h == 128 && a.rk == 4) return false;   // its registers would spill
   const void* ptrs[4] = {a.b_q, a.c_bk, a.c_bv, a.out};   // read/written 8 or 16 bytes at a time
   for (int i = 0; i < 4; ++i)
     if (((uintptr_t)ptrs[i]) % 16) return false;
@@ -329,16 +419,16 @@ bool prefill_mfma_supported(int dtype, const AttnArgs& a) {
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t st) {
   const int nqb = (int)((a.S + 127) / 128);
   const dim3 grid((unsigned)((int64_t)nqb * a.h * a.n_batch));
-#define TPA_PREFILL_LAUNCH(DH_, R_) \
-  hipLaunchKernelGGL((prefill_mfma_kernel<DH_, R_>), grid, dim3(256), 0, st, a, nqb)
+#define TPA_PREFILL_LAUNCH(DH_, R_)                                                               \
+  hipLaunchKernelGGL((prefill_mfma_kernel<DH_, R_>), grid, dim3(256), PrefillMfmaCfg<DH_>::kLds, st, a, \
+                     nqb)
   if (a.d_h == 64) {
     if (a.rk == 1) TPA_PREFILL_LAUNCH(64, 1);
     else if (a.rk == 2) TPA_PREFILL_LAUNCH(64, 2);
     else TPA_PREFILL_LAUNCH(64, 4);
   } else {
     if (a.rk == 1) TPA_PREFILL_LAUNCH(128, 1);
-    else if (a.rk == 2) TPA_PREFILL_LAUNCH(128, 2);
-    else TPA_PREFILL_LAUNCH(128, 4);
+    else TPA_PREFILL_LAUNCH(128, 2);
   }
 #undef TPA_PREFILL_LAUNCH
   return hipGetLastError();

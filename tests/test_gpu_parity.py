@@ -366,3 +366,78 @@ def test_decode_step_graph_replay_matches_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {rep} differs from the eager step"
+
+
+def _oracle_decode_heads(fq: dict, kv: dict, dims, pairs, ctx):
+    """fp64 oracle decode output of the sampled (sequence, head) pairs only: each
+    pair is reconstructed and attended on its own (its own definition)."""
+    od = oracle_dims(dims)
+    Q = O.queries(oracle_query(fq, dims), od)                   # [B, 1, h, d_h]
+    out = {}
+    for b, hh in pairs:
+        ak = I.to_f64(kv["a_k"][b, :ctx, hh:hh + 1])
+        bk = I.to_f64(kv["b_k"][b, :ctx])
+        av = I.to_f64(kv["a_v"][b, :ctx, hh:hh + 1])
+        bv = I.to_f64(kv["b_v"][b, :ctx])
+        k = O.reconstruct(ak, bk)[:, 0, :]
+        v = O.reconstruct(av, bv)[:, 0, :]
+        out[(b, hh)] = O.attend_head(Q[b, :, hh], k, v, np.array([ctx - 1]), True)[0]
+    return out
+
+
+@pytest.mark.parametrize("wl_name,pairs", [
+    ("decode_b8_ctx128k", [(0, 0), (3, 17), (7, 31)]),
+    ("kvonly_b32_ctx16k", [(0, 0), (13, 5), (31, 23)]),
+])
+def test_decode_full_size_sampled(wl_name, pairs):
+    """Decode at the workload's full size, in the launch configuration of a real
+    call; the oracle computes sampled (sequence, head) outputs one by one."""
+    require_gpu()
+    wl = I.WORKLOADS[wl_name]
+    sh = wl.shape
+    dims = D(sh.d_model, sh.n_heads, sh.head_dim, sh.rank_q, sh.rank_k, sh.rank_v, "bf16")
+    B, ctx = wl.batch, wl.seq + 1
+    announce(f"decode full size {wl_name} B={B} ctx={ctx}")
+    kv = I.factors(sh, B, ctx, seed=121, dtype="bf16", with_query=False)
+    fq = I.factors(sh, B, 1, seed=122, dtype="bf16")
+    cache = T.new_cache(dims, B, ctx)
+    fill_cache(cache, kv)
+    out = T.tpa_decode_attn(dims, query_factors_gpu(T, dims, fq, squeeze=True), cache, ctx,
+                            T.new_workspace(dims, B, ctx))
+    torch.cuda.synchronize()
+    ref = _oracle_decode_heads(fq, kv, dims, pairs, ctx)
+    dh = sh.head_dim
+    got = torch.stack([out[b, hh * dh:(hh + 1) * dh] for b, hh in pairs])
+    assert_close(got, np.stack([ref[p] for p in pairs]), "bf16", f"decode {wl_name} sampled heads")
+    del cache, kv
+
+
+def test_mqa_equivalence_kvonly_shape():
+    """R_K = R_V = 1 with the head factors constant 1 is multi-query attention
+    (one K/V head shared by all query heads).  Decode and prefill at the KV-only
+    shape (24 heads of 64, plain Q) against textbook MQA through torch's scaled
+    dot-product attention in fp64, written without the factor machinery."""
+    require_gpu()
+    import textbook
+    B, S, ctx = 4, 257, 2048
+    dims = D(1536, 24, 64, 0, 1, 1, "bf16")
+    announce("MQA equivalence at the KV-only shape")
+    sh = shape_of(dims)
+    kv = I.factors(sh, B, ctx, seed=131, dtype="bf16", std=1.0, with_query=False)
+    for k in ("a_k", "a_v"):
+        kv[k] = torch.ones_like(kv[k])
+    fq = I.factors(sh, B, S, seed=132, dtype="bf16", std=1.0)
+    cache = T.new_cache(dims, B, ctx)
+    fill_cache(cache, kv)
+    # prefill of the last S positions (queries at ctx-S .. ctx-1), and a decode at ctx-1
+    pre = T.tpa_prefill_attn(dims, query_factors_gpu(T, dims, fq), cache, ctx - S, True)
+    dq = {"q": fq["q"][:, -1:]}
+    dec = T.tpa_decode_attn(dims, query_factors_gpu(T, dims, dq, squeeze=True), cache, ctx,
+                            T.new_workspace(dims, B, ctx))
+    torch.cuda.synchronize()
+    q = I.to_f64(fq["q"])                                     # [B, S, 24, 64]
+    k = I.to_f64(kv["b_k"])                                   # [B, ctx, 1, 64]: the shared head
+    v = I.to_f64(kv["b_v"])
+    ref = textbook.attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), ctx - S, True).numpy()
+    assert_close(pre, ref, "bf16", "prefill vs textbook MQA")
+    assert_close(dec, ref[:, -1], "bf16", "decode vs textbook MQA")
