@@ -26,6 +26,9 @@ struct ProjArgs {
   int32_t head_dim;
   int32_t rot_cols;      // 0 when rotation is off
   int32_t nseg;
+  int32_t vec8;          // 1: head_dim, every segment begin, width and batch
+                         // stride are multiples of 8 and every destination is
+                         // 16-byte aligned, so 8-column pieces store whole
   int32_t seg_begin[kMaxSeg + 1];
   int32_t width[kMaxSeg];
   int64_t bstride[kMaxSeg];  // elements between sequences

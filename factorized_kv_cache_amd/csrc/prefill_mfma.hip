@@ -123,11 +123,16 @@ struct PrefillMfmaCfg {
   static constexpr int VTILE = (DH + 16) * LDV;     // bf16 elements of one V^T buffer
   static constexpr size_t kLds = (size_t)2 * (KTILE + VTILE) * sizeof(bf16_t);
   static constexpr float kRescaleSlack = 8.f;       // log2 units
-  // factors are loaded a block ahead at d_h = 64; at d_h = 128 (two items per
-  // thread) those registers would spill, so each block's are loaded just
-  // before its rebuild
-  static constexpr bool kPipelined = DH == 64;
 };
+
+// How far ahead of its rebuild a key block's factors are loaded: one block at
+// d_h = 64; at d_h = 128 (two items per thread) those registers would spill,
+// so each block's factors are loaded just before its rebuild.  (A second
+// register set, two blocks ahead, spills at d_h = 64 as well.)
+template <int DH, int R>
+constexpr int prefill_prefetch_depth() {
+  return DH == 64 ? 1 : 0;
+}
 
 // The cached factors one thread needs for its rebuild items of one key block:
 // keys 2*kp and 2*kp+1, d slice d0 .. d0+7.
@@ -140,11 +145,14 @@ struct RebuildRegs {
   typename RankWordP<R>::type av[IT][2];
 };
 
+// Item = (key pair kp, 8-wide d slice d0).  Consecutive lanes take consecutive
+// d slices of one key pair, so the DH/8 lanes of a key read each rank row of
+// B~_K / B_V as whole, contiguous cache lines.
 template <int DH>
 __device__ __forceinline__ void rebuild_item(int it, int& kp, int& d0) {
   const int item = threadIdx.x + 256 * it;
-  kp = item % 32;
-  d0 = (item / 32) * 8;
+  kp = item / (DH / 8);
+  d0 = (item % (DH / 8)) * 8;
 }
 
 // Keys past kend are clamped to the last valid key: they are masked out of
@@ -198,6 +206,95 @@ __device__ __forceinline__ void store_rebuild(const RebuildRegs<DH, R>& g, bf16_
   }
 }
 
+// One key block of the online-softmax attention for this wave's 2 x 16 queries
+// (positions wpos0 ..), reading K and V^T of the block from LDS.
+template <int DH>
+__device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t* vt_lds, int64_t k0, int64_t kend,
+                                             int64_t wpos0, bool causal, int li, int lg,
+                                             const bf16x8_t (&qop)[PrefillMfmaCfg<DH>::QT][PrefillMfmaCfg<DH>::KS],
+                                             float (&m_run)[PrefillMfmaCfg<DH>::QT],
+                                             f32x4_t (&oacc)[PrefillMfmaCfg<DH>::QT][PrefillMfmaCfg<DH>::DT + 1]) {
+  using C = PrefillMfmaCfg<DH>;
+  constexpr int BN = C::BN, QT = C::QT, KS = C::KS, DT = C::DT, LDK = C::LDK, LDV = C::LDV;
+    // ---- scores S^T[key, query] for the block's 4 key tiles
+    f32x4_t sacc[4][QT];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      bf16x8_t kf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[ks] = *reinterpret_cast<const bf16x8_t*>(ks_lds + (kt * 16 + li) * LDK + lg * (DH / 4) + 8 * ks);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16(kf[ks], qop[qt][ks], acc);
+        sacc[kt][qt] = acc;
+      }
+    }
+
+    // ---- mask (only where the block reaches past a query of this wave)
+    const bool need_mask = (causal && k0 + BN - 1 > wpos0) || (k0 + BN > kend);
+    if (need_mask) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t t = k0 + kt * 16 + 4 * lg + i;
+            const int64_t p = wpos0 + 16 * qt + li;
+            const bool ok = t < kend && (!causal || t <= p);
+            if (!ok) sacc[kt][qt][i] = -INFINITY;
+          }
+    }
+
+    // ---- online softmax per query (lazy rescale), P^T operands
+    bf16x8_t pop[QT][2];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, sacc[kt][qt][i]);
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      const bool grow = bmax > m_run[qt] + (TPA_PF_LAZY ? C::kRescaleSlack : 0.f);
+      if (__any(grow)) {
+        const float m_new = grow ? bmax : m_run[qt];
+        const float alpha = fast_exp2(m_run[qt] - m_new);   // 0 on the first block, 1 where m stays
+        m_run[qt] = m_new;
+#pragma unroll
+        for (int dt = 0; dt <= DT; ++dt) oacc[qt][dt] *= alpha;
+      }
+      // a query with no visible key yet keeps m = -inf; its probabilities are 0
+      const float m_use = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(sacc[2 * kb + (j >> 2)][qt][j & 3] - m_use);
+        pop[qt][kb] = pack8(pv);
+      }
+    }
+
+    // ---- O^T += V^T P^T (and the ones row: sum_t p_t)
+#pragma unroll
+    for (int dt = 0; dt <= DT; ++dt) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16_t* vrow = vt_lds + (dt * 16 + li) * LDV + kb * 32 + 4 * lg;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        const bf16x8_t vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) oacc[qt][dt] = mfma_bf16(vf, pop[qt][kb], oacc[qt][dt]);
+      }
+    }
+
+}
+
 template <int DH, int R>
 __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_qblocks) {
   using C = PrefillMfmaCfg<DH>;
@@ -212,13 +309,18 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
   // One-dimensional grid.  Work items (query block, head, sequence) in order of
   // decreasing key count are numbered by the linear workgroup id; since
   // workgroups go to the XCDs round-robin by that id, every XCD gets an equal
-  // share of every query block, heaviest first.
+  // share of every query block, heaviest first.  When the (sequence, head)
+  // pairs split evenly over the eight XCDs, XCD x takes the x-th contiguous
+  // range of them (sequence-major), so the factors it reads span as few
+  // sequences as possible and stay in its L2.
   const int h = a.h;
   const int64_t hb = (int64_t)h * a.n_batch;
   const int64_t L = blockIdx.x;
   const int qb = n_qblocks - 1 - (int)(L / hb);
-  const int hh = (int)(L % h);
-  const int64_t b = (L % hb) / h;
+  int64_t u = L % hb;
+  if (hb % 8 == 0) u = (u & 7) * (hb >> 3) + (u >> 3);
+  const int hh = (int)(u % h);
+  const int64_t b = u / h;
   const int64_t q0 = (int64_t)qb * BM;
   const int64_t seq0 = b * a.max_seq;
   const int64_t last_q = (q0 + BM < a.S ? q0 + BM : a.S) - 1;
@@ -280,102 +382,24 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
     for (int dt = 0; dt <= DT; ++dt) oacc[qt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // block 0 into buffer 0; block 1's factors go out (pipelined form)
+  constexpr int kDepth = prefill_prefetch_depth<DH, R>();
+  const int64_t wpos0 = a.start_pos + q0 + 32 * wave;   // first position of this wave's queries
+  const bool causal = a.causal != 0;
+  // Block i is rebuilt into buffer i & 1 while block i - 1 is attended to.
   store_rebuild<DH, R>(rg, KS_BUF(0), VT_BUF(0));
-  if constexpr (C::kPipelined) {
+  if constexpr (kDepth == 1) {
     if (nblk > 1) load_rebuild<DH, R>(rg, a, seq0, hh, BN, kend);
   }
   __syncthreads();
-
-  const int64_t wpos0 = a.start_pos + q0 + 32 * wave;   // first position of this wave's queries
   for (int blk = 0; blk < nblk; ++blk) {
     const int64_t k0 = (int64_t)blk * BN;
-    const bf16_t* ks_lds = KS_BUF(blk & 1);
-    const bf16_t* vt_lds = VT_BUF(blk & 1);
-
-    // ---- scores S^T[key, query] for the block's 4 key tiles
-    f32x4_t sacc[4][QT];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      bf16x8_t kf[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[ks] = *reinterpret_cast<const bf16x8_t*>(ks_lds + (kt * 16 + li) * LDK + lg * (DH / 4) + 8 * ks);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16(kf[ks], qop[qt][ks], acc);
-        sacc[kt][qt] = acc;
-      }
-    }
-
-    // ---- mask (only where the block reaches past a query of this wave)
-    const bool need_mask = (a.causal && k0 + BN - 1 > wpos0) || (k0 + BN > kend);
-    if (need_mask) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t t = k0 + kt * 16 + 4 * lg + i;
-            const int64_t p = wpos0 + 16 * qt + li;
-            const bool ok = t < kend && (!a.causal || t <= p);
-            if (!ok) sacc[kt][qt][i] = -INFINITY;
-          }
-    }
-
-    // ---- online softmax per query (lazy rescale), P^T operands
-    bf16x8_t pop[QT][2];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float bmax = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, sacc[kt][qt][i]);
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      const bool grow = bmax > m_run[qt] + (TPA_PF_LAZY ? C::kRescaleSlack : 0.f);
-      if (__any(grow)) {
-        const float m_new = grow ? bmax : m_run[qt];
-        const float alpha = fast_exp2(m_run[qt] - m_new);   // 0 on the first block, 1 where m stays
-        m_run[qt] = m_new;
-#pragma unroll
-        for (int dt = 0; dt <= DT; ++dt) oacc[qt][dt] *= alpha;
-      }
-      // a query with no visible key yet keeps m = -inf; its probabilities are 0
-      const float m_use = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float pv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(sacc[2 * kb + (j >> 2)][qt][j & 3] - m_use);
-        pop[qt][kb] = pack8(pv);
-      }
-    }
-
-    // ---- O^T += V^T P^T (and the ones row: sum_t p_t)
-#pragma unroll
-    for (int dt = 0; dt <= DT; ++dt) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16_t* vrow = vt_lds + (dt * 16 + li) * LDV + kb * 32 + 4 * lg;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        const bf16x8_t vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) oacc[qt][dt] = mfma_bf16(vf, pop[qt][kb], oacc[qt][dt]);
-      }
-    }
-
-    // ---- rebuild the next block into the other buffer; its factors were
-    //      loaded a block ago.  Start loading the block after it.
+    attend_block<DH>(KS_BUF(blk & 1), VT_BUF(blk & 1), k0, kend, wpos0, causal, li, lg, qop, m_run, oacc);
+    // rebuild the next block into the other buffer; with depth 1 its factors
+    // were loaded a block ago and the block after it starts loading now
     if (blk + 1 < nblk) {
-      if constexpr (!C::kPipelined) load_rebuild<DH, R>(rg, a, seq0, hh, k0 + BN, kend);
+      if constexpr (kDepth == 0) load_rebuild<DH, R>(rg, a, seq0, hh, k0 + BN, kend);
       store_rebuild<DH, R>(rg, KS_BUF((blk + 1) & 1), VT_BUF((blk + 1) & 1));
-      if constexpr (C::kPipelined) {
+      if constexpr (kDepth == 1) {
         if (blk + 2 < nblk) load_rebuild<DH, R>(rg, a, seq0, hh, k0 + 2 * BN, kend);
       }
     }
@@ -404,8 +428,18 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
   }
 }
 
+// LDS a workgroup may allocate on the current device.
+static size_t device_lds_per_block() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 0;
+  return (size_t)v;
+}
+
 bool prefill_mfma_supported(int dtype, const AttnArgs& a) {
   if (dtype != kBF16) return false;
+  const size_t lds = a.d_h == 64 ? PrefillMfmaCfg<64>::kLds : PrefillMfmaCfg<128>::kLds;
+  if (lds > device_lds_per_block()) return false;
   if ((a.S + 127) / 128 * (int64_t)a.h * a.n_batch >= ((int64_t)1 << 31)) return false;
   if (!(a.d_h == 64 || a.d_h == 128)) return false;
   if (a.rk != a.rv || !(a.rk == 1 || a.rk == 2 || a.rk == 4)) return false;

@@ -38,6 +38,55 @@ __device__ __forceinline__ void proj_store_pair(const ProjArgs& a, int64_t m, in
   }
 }
 
+// Writes columns n .. n+7 of row m = b*S + s (n a multiple of 8) from float32
+// values v, rotating the pairs below rot_cols.  With vec8 the piece lies in one
+// segment and one head and goes out as a single 16-byte store; otherwise each
+// column is placed on its own (columns past N are dropped).
+__device__ __forceinline__ void proj_store_piece8(const ProjArgs& a, uint32_t b, uint32_t s, int n, float* v) {
+  const int64_t pos = a.start_pos + s;
+  if (a.vec8) {
+    if (n < a.rot_cols) {
+      const int p0 = (n % a.head_dim) >> 1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float c, sn;
+        rope_cos_sin(a.rope, pos, p0 + j, c, sn);
+        const float r0 = v[2 * j] * c - v[2 * j + 1] * sn;
+        const float r1 = v[2 * j] * sn + v[2 * j + 1] * c;
+        v[2 * j] = r0;
+        v[2 * j + 1] = r1;
+      }
+    }
+    int e = 0;
+    while (e + 1 < a.nseg && n >= a.seg_begin[e + 1]) ++e;
+    bf16_t* d = reinterpret_cast<bf16_t*>(a.dst[e]) + (int64_t)b * a.bstride[e] + (int64_t)s * a.width[e] +
+                (n - a.seg_begin[e]);
+    *reinterpret_cast<uint4*>(d) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c0 = n + 2 * j;
+    if (c0 < a.rot_cols) {
+      float c, sn;
+      rope_cos_sin(a.rope, pos, (c0 % a.head_dim) >> 1, c, sn);
+      const float r0 = v[2 * j] * c - v[2 * j + 1] * sn;
+      const float r1 = v[2 * j] * sn + v[2 * j + 1] * c;
+      v[2 * j] = r0;
+      v[2 * j + 1] = r1;
+    }
+  }
+  for (int q = 0; q < 8; ++q) {
+    const int col = n + q;
+    if (col >= a.N) break;
+    int e = 0;
+    while (e + 1 < a.nseg && col >= a.seg_begin[e + 1]) ++e;
+    bf16_t* d = reinterpret_cast<bf16_t*>(a.dst[e]);
+    d[(int64_t)b * a.bstride[e] + (int64_t)s * a.width[e] + (col - a.seg_begin[e])] = f32_to_bf16(v[q]);
+  }
+}
+
 // General tiled GEMM on the vector ALUs: 64x64 output tile per 256-thread
 // workgroup, 4x4 outputs per thread, K staged through LDS in steps of 16.
 template <typename T>
@@ -100,7 +149,8 @@ __global__ void __launch_bounds__(256) proj_generic_kernel(ProjArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyWaves = 8;
 
-template <int MT>
+// U = k-steps of 32 whose loads are issued together; it divides K / (32 * 8).
+template <int MT, int U>
 __global__ void __launch_bounds__(64 * kSkinnyWaves) proj_skinny_kernel(ProjArgs a) {
   __shared__ float red[kSkinnyWaves][16][16 * MT + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -121,40 +171,38 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) proj_skinny_kernel(ProjArgs
   f32x4_t acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // eight k-steps per trip (steps past kq repeat the last address, unused)
-  for (int k = 0; k < kq; k += 256) {
-    uint4 wv[8], xv[8][MT];
+  for (int k = 0; k < kq; k += 32 * U) {
+    uint4 wv[U], xv[U][MT];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int ku = k + 32 * u < kq ? k + 32 * u : kq - 32;
-      wv[u] = *reinterpret_cast<const uint4*>(wrow + ku);
+    for (int u = 0; u < U; ++u) {
+      wv[u] = *reinterpret_cast<const uint4*>(wrow + k + 32 * u);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) xv[u][mt] = *reinterpret_cast<const uint4*>(xrow[mt] + ku);
+      for (int mt = 0; mt < MT; ++mt) xv[u][mt] = *reinterpret_cast<const uint4*>(xrow[mt] + k + 32 * u);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (k + 32 * u >= kq) break;
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_bf16(as_bf16x8(wv[u]), as_bf16x8(xv[u][mt]), acc[mt]);
-    }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][4 * lg + i][mt * 16 + li] = acc[mt][i];
   __syncthreads();
-  for (int item = threadIdx.x; item < 8 * 16 * MT; item += blockDim.x) {
-    const int p = item & 7, m = item >> 3;   // rows 2p, 2p+1 of the tile, token m
-    const int n = n0 + 2 * p;
-    if (m >= M || n >= N) continue;
-    float v0 = 0.f, v1 = 0.f;
+  // one 8-column piece (half of the 16 weight rows) of one token per thread
+  const int item = threadIdx.x;
+  const int m = item >> 1, n = n0 + 8 * (item & 1);
+  if (item >= 2 * 16 * MT || m >= M || n >= N) return;
+  float v[8];
 #pragma unroll
-    for (int w = 0; w < kSkinnyWaves; ++w) {
-      v0 += red[w][2 * p][m];
-      v1 += red[w][2 * p + 1][m];
-    }
-    proj_store_pair<bf16_t>(a, m, n, v0, v1);
-  }
+  for (int q = 0; q < 8; ++q) v[q] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kSkinnyWaves; ++w)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] += red[w][8 * (item & 1) + q][m];
+  const uint32_t S = (uint32_t)a.S;
+  const uint32_t b = (uint32_t)m / S;
+  proj_store_piece8(a, b, (uint32_t)m - b * S, n, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -164,14 +212,29 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) proj_skinny_kernel(ProjArgs
 // ---------------------------------------------------------------------------
 constexpr int kPBM = 128, kPBN = 128, kPBK = 64, kPLDK = kPBK + 8;
 
+// The epilogue stages half of the fp32 tile (64 rows) at a time in the same
+// LDS, then each thread rotates and stores 8-column pieces.
+constexpr int kPLDT = kPBN + 4;
+static_assert(64 * kPLDT * 4 <= (kPBM + kPBN) * kPLDK * 2, "epilogue tile must fit the slab buffers");
+
 __global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
-  __shared__ __align__(16) bf16_t xs[kPBM * kPLDK];
-  __shared__ __align__(16) bf16_t ws[kPBN * kPLDK];
+  __shared__ __align__(16) bf16_t lds[(kPBM + kPBN) * kPLDK];
+  bf16_t* xs = lds;
+  bf16_t* ws = lds + kPBM * kPLDK;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.x * kPBM;
-  const int n0 = blockIdx.y * kPBN;
+  // Workgroups go to the eight XCDs round-robin by linear index.  The grid is
+  // padded to a multiple of 8 row tiles and ordered so that each XCD takes its
+  // row tiles in turn with all column tiles of one row tile back to back:
+  // those share the X rows, which then come from that XCD's L2.
+  const int n_ntiles = (int)((a.N + kPBN - 1) / kPBN);
+  const int n_mtiles = (int)((a.M + kPBM - 1) / kPBM);
+  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+  const int mtile = (q / n_ntiles) * 8 + xcd, ntile = q % n_ntiles;
+  if (mtile >= n_mtiles) return;
+  const int64_t m0 = (int64_t)mtile * kPBM;
+  const int n0 = ntile * kPBN;
   const int64_t M = a.M, K = a.K;
   const int N = (int)a.N;
   const bf16_t* X = reinterpret_cast<const bf16_t*>(a.x);
@@ -236,35 +299,69 @@ __global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
     }
     __syncthreads();
   }
-  // D[m][n] with n = ... + li: the rotary partner column n^1 is lane li^1.
+  // Tile rows wm*64 + tm*16 + 4*lg + i, columns wn*64 + tn*16 + li.
+  float* tile = reinterpret_cast<float*>(lds);
+  const int pc = tid & 15;          // this thread's 8-column piece
+  const int n = n0 + 8 * pc;
+  const uint32_t S = (uint32_t)a.S;
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm)
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn)
+      for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = acc[tm][tn][i];
-        const float partner = __shfl_xor(v, 1);
-        const int64_t m = m0 + wm * 64 + tm * 16 + 4 * lg + i;
-        const int n = n0 + wn * 64 + tn * 16 + li;
-        if (!(li & 1) && m < M && n < N) proj_store_pair<bf16_t>(a, m, n, v, partner);
+        for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tile[(tm * 16 + 4 * lg + i) * kPLDT + wn * 64 + tn * 16 + li] = acc[tm][tn][i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = (tid >> 4) + 16 * j;
+      const int64_t m = m0 + half * 64 + r;
+      if (m < M && n < N) {
+        float v[8];
+        const float4 lo = *reinterpret_cast<const float4*>(tile + r * kPLDT + 8 * pc);
+        const float4 hi = *reinterpret_cast<const float4*>(tile + r * kPLDT + 8 * pc + 4);
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+        const uint32_t b = (uint32_t)m / S;
+        proj_store_piece8(a, b, (uint32_t)m - b * S, n, v);
       }
+    }
+    if (half == 0) __syncthreads();
+  }
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 hipError_t launch_factor_proj(int dtype, const ProjArgs& a, hipStream_t st) {
-  if (dtype == kBF16 && aligned16(a.x) && aligned16(a.w) && a.K % 64 == 0) {
+  const int64_t mfma_grid = ((a.M + kPBM * 8 - 1) / (kPBM * 8)) * 8 * ((a.N + kPBN - 1) / kPBN);
+  if (dtype == kBF16 && aligned16(a.x) && aligned16(a.w) && a.K % 64 == 0 && mfma_grid <= INT32_MAX) {
     if (a.M <= 64 && a.K % (32 * kSkinnyWaves) == 0) {
       const dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * kSkinnyWaves);
-      switch ((a.M + 15) / 16) {
-        case 1: hipLaunchKernelGGL(proj_skinny_kernel<1>, grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL(proj_skinny_kernel<2>, grid, block, 0, st, a); break;
-        case 3: hipLaunchKernelGGL(proj_skinny_kernel<3>, grid, block, 0, st, a); break;
-        default: hipLaunchKernelGGL(proj_skinny_kernel<4>, grid, block, 0, st, a); break;
+      const int64_t steps = a.K / (32 * kSkinnyWaves);
+      const int u = steps % 8 == 0 ? 8 : steps % 4 == 0 ? 4 : steps % 2 == 0 ? 2 : 1;
+      const int mt = (int)((a.M + 15) / 16);
+#define TPA_SKINNY(MT, U) hipLaunchKernelGGL((proj_skinny_kernel<MT, U>), grid, block, 0, st, a)
+#define TPA_SKINNY_U(MT)               \
+  switch (u) {                         \
+    case 8: TPA_SKINNY(MT, 8); break;  \
+    case 4: TPA_SKINNY(MT, 4); break;  \
+    case 2: TPA_SKINNY(MT, 2); break;  \
+    default: TPA_SKINNY(MT, 1); break; \
+  }
+      switch (mt) {
+        case 1: TPA_SKINNY_U(1); break;
+        case 2: TPA_SKINNY_U(2); break;
+        case 3: TPA_SKINNY_U(3); break;
+        default: TPA_SKINNY_U(4); break;
       }
+#undef TPA_SKINNY_U
+#undef TPA_SKINNY
     } else {
-      const dim3 grid((unsigned)((a.M + kPBM - 1) / kPBM), (unsigned)((a.N + kPBN - 1) / kPBN));
+      const int64_t mt = (a.M + kPBM - 1) / kPBM, nt = (a.N + kPBN - 1) / kPBN;
+      const dim3 grid((unsigned)(((mt + 7) / 8) * 8 * nt));
       hipLaunchKernelGGL(proj_mfma_kernel, grid, dim3(256), 0, st, a);
     }
     return hipGetLastError();

@@ -196,6 +196,9 @@ tpa_status tpa_factor_proj(const tpa_dims* d, const void* x, int64_t n_batch, in
   }
   a.seg_begin[n] = col;
   a.rot_cols = fuse_rope ? (segs[0].width + segs[1].width) : 0;
+  a.vec8 = dh % 8 == 0;
+  for (int e = 0; e < n; ++e)
+    if (a.seg_begin[e] % 8 || a.width[e] % 8 || a.bstride[e] % 8 || ((uintptr_t)a.dst[e] & 15)) a.vec8 = 0;
   a.rope = rope_table(d);
   return hip_status(tpa::launch_factor_proj(d->dtype, a, (hipStream_t)stream), "tpa_factor_proj");
 }

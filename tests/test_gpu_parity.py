@@ -188,6 +188,8 @@ PREFILL_CASES = [
     ("kvonly_bf16", "bf16", 2, 150, 0, True, 1536, 24, 64, 0, 4, 4, 1.0),
     ("dh128_bf16", "bf16", 1, 97, 30, True, 4096, 32, 128, 6, 2, 2, 1.0),
     ("dh256_f32", "f32", 1, 40, 0, True, 64, 2, 256, 2, 2, 2, 0.5),
+    ("odd_heads_r1_bf16", "bf16", 2, 200, 7, True, 320, 5, 64, 3, 1, 1, 1.0),
+    ("odd_heads_dh128_bf16", "bf16", 1, 150, 0, True, 384, 3, 128, 2, 2, 2, 1.0),
 ]
 
 
