@@ -21,9 +21,9 @@
 //    4g+j of tile 0 for j<4, of tile 1 for j>=4); B_V goes through a
 //    wave-private LDS tile to be read transposed.
 //
-// At d_h = 64 each wave keeps two blocks' loads in flight, both issued before
-// the query is formed; at d_h = 128 the registers go to a second resident
-// wave instead.
+// At d_h = 64 (up to 32 heads, 16 at rank 1) each wave keeps two blocks' loads
+// in flight, both issued before the query is formed; at d_h = 128 or with more
+// heads the registers go to a second resident wave instead.
 // The four waves of a workgroup merge their (m, l, O) through LDS in a fixed
 // order and write one partial per head to the workspace; the combine pass,
 // shared with the general kernel, merges the chunks in index order.  (Merging
@@ -93,7 +93,8 @@ struct DecodeMfmaCfg {
   static constexpr int HP = HT * 16;     // padded head count
   static constexpr int LROW = DH + 4;    // LDS row stride (bf16): 4 rows apart = 8 banks apart
   static constexpr int OST = DH + 4;     // LDS row stride (f32) of the merge buffer
-  static constexpr bool kPrefetch = DH == 64;
+  // a second block in flight (its registers spill beyond these sizes)
+  static constexpr bool kPrefetch = DH == 64 && (R == 1 ? HT == 1 : HT <= 2);
   static constexpr size_t kLoopBytes = 4 * 32 * LROW * sizeof(bf16_t);
   static constexpr size_t kMergeBytes = (8 * HP + 2 * HP * OST) * sizeof(float);
   static constexpr size_t kLds = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
@@ -107,7 +108,7 @@ constexpr size_t kDecodeMfmaQueryLds = 16384;
 template <int DH, int R, int HT>
 struct BlockRegs {
   using C = DecodeMfmaCfg<DH, R, HT>;
-  uint4 bv[DH / 16];                                 // half a B_V row, for the LDS tile
+  uint4 bv[DH / 16];                                 // B_V pieces, for the LDS tile
   uint4 bk[2][C::KS];                                // B~_K operand slices
   typename RankWord<R>::type ak[2][HT][C::NT];       // head factors of the lane's tokens
   typename RankWord<R>::type av[2][HT][C::NT];
@@ -127,13 +128,15 @@ __device__ __forceinline__ void load_block(BlockRegs<DH, R, HT>& g, const ChunkB
                                            int lane) {
   using C = DecodeMfmaCfg<DH, R, HT>;
   const int li = lane & 15, lg = lane >> 4;
-  {
-    const int row = lane >> 1, half = lane & 1;
+  // B_V rows of the block, 16-byte piece u*64 + lane of the block's 64*DH
+  // bytes: every load instruction reads whole contiguous cache lines.
+#pragma unroll
+  for (int u = 0; u < DH / 16; ++u) {
+    const int piece = u * 64 + lane;
+    const int row = piece / (DH / 8), col = (piece % (DH / 8)) * 8;
     int tok = tb + row / R;
     tok = tok < last ? tok : last;
-    const uint4* src = reinterpret_cast<const uint4*>(cb.bv + ((tok * R + row % R) * DH + half * (DH / 2)));
-#pragma unroll
-    for (int u = 0; u < DH / 16; ++u) g.bv[u] = src[u];
+    g.bv[u] = *reinterpret_cast<const uint4*>(cb.bv + ((tok * R + row % R) * DH + col));
   }
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
@@ -170,15 +173,14 @@ __device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf1
   constexpr int KS = C::KS, DT = C::DT, NT = C::NT, LROW = C::LROW;
   const int li = lane & 15, lg = lane >> 4;
 
-  // B_V half-row -> wave-private LDS tile
-  {
-    const int row = lane >> 1, half = lane & 1;
-    uint2* dst = reinterpret_cast<uint2*>(lbv + row * LROW + half * (DH / 2));
+  // B_V pieces -> wave-private LDS tile
 #pragma unroll
-    for (int u = 0; u < DH / 16; ++u) {
-      dst[2 * u] = make_uint2(g.bv[u].x, g.bv[u].y);
-      dst[2 * u + 1] = make_uint2(g.bv[u].z, g.bv[u].w);
-    }
+  for (int u = 0; u < DH / 16; ++u) {
+    const int piece = u * 64 + lane;
+    const int row = piece / (DH / 8), col = (piece % (DH / 8)) * 8;
+    uint2* dst = reinterpret_cast<uint2*>(lbv + row * LROW + col);
+    dst[0] = make_uint2(g.bv[u].x, g.bv[u].y);
+    dst[1] = make_uint2(g.bv[u].z, g.bv[u].w);
   }
 
   // scores on the matrix cores
@@ -427,6 +429,7 @@ bool decode_mfma_supported(int dtype, const AttnArgs& a) {
   if (!(a.d_h == 64 || a.d_h == 128)) return false;
   if (a.h > 64) return false;
   if (a.d_h == 128 && a.h > 32) return false;  // three head tiles at d_h = 128 spill registers
+  if (a.rk == 1 && a.h > 48) return false;     // so do four at rank 1
   const size_t qbytes = (a.rq ? (size_t)a.rq * (a.h + a.d_h) : (size_t)a.h * a.d_h) * sizeof(bf16_t);
   if (qbytes > kDecodeMfmaQueryLds) return false;
   const void* ptrs[5] = {a.b_q, a.c_ak, a.c_bk, a.c_av, a.c_bv};
@@ -458,7 +461,7 @@ static void launch_dh_r(const AttnArgs& a, int64_t ctx_len, int64_t chunk, int64
       if constexpr (DH == 64) {
         if (ht == 3)
           launch_cfg<DH, R, 3>(a, ctx_len, chunk, n_chunks, ws, st);
-        else
+        else if constexpr (R > 1)
           launch_cfg<DH, R, 4>(a, ctx_len, chunk, n_chunks, ws, st);
       }
       break;

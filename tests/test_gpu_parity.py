@@ -150,6 +150,11 @@ DECODE_CASES = [
     ("dh128_h32_bf16", "bf16", 2, 1500, 4096, 32, 128, 6, 2, 2, None),
     ("single_token", "bf16", 5, 1, 1024, 16, 64, 6, 2, 2, None),
     ("r1_bf16", "bf16", 3, 300, 256, 8, 64, 2, 1, 1, 1.5),
+    ("h24_r1_bf16", "bf16", 2, 500, 768, 24, 64, 3, 1, 1, 1.0),      # two head tiles at rank 1
+    ("h40_r2_bf16", "bf16", 2, 700, 640, 40, 64, 4, 2, 2, 1.0),      # three head tiles
+    ("h64_r4_bf16", "bf16", 2, 333, 1024, 64, 64, 2, 4, 4, 1.0),     # four head tiles
+    ("h20_dh128_bf16", "bf16", 1, 999, 2560, 20, 128, 2, 2, 2, 1.0),
+    ("h10_r2_bf16", "bf16", 2, 400, 640, 10, 64, 3, 2, 2, 1.0),
 ]
 
 
