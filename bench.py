@@ -174,6 +174,60 @@ def run_decode(args):
 
 
 # ---------------------------------------------------------------------------
+# Paged decode (reported alongside): the same caches moved into shuffled pages
+# ---------------------------------------------------------------------------
+
+PAGE_TOKENS = 64
+
+
+def run_paged(db, reps: int = 64):
+    """Decode-call time over paged copies of the benchmark's caches (64-token
+    pages in a seeded random order), once with every sequence at full length
+    and once with seeded random lengths in [1, ctx]; layers visited in turn so
+    each call reads its pages cold."""
+    d, B, ctx = db.dims, db.B, db.ctx
+    pps = (ctx + PAGE_TOKENS - 1) // PAGE_TOKENS
+    g = torch.Generator().manual_seed(4242)
+    layers = []
+    for L in db.layers:
+        table = torch.randperm(B * pps, generator=g).to(torch.int32).reshape(B, pps).contiguous()
+        pc = T.new_paged_cache(d, B * pps, PAGE_TOKENS, table)
+        t = torch.arange(ctx)
+        for k in ("a_k", "b_k", "a_v", "b_v"):
+            pool, dense = getattr(pc, k), getattr(L["cache"], k)
+            for b in range(B):
+                pool[table[b, t // PAGE_TOKENS].long().cuda(), (t % PAGE_TOKENS).cuda()] = dense[b, :ctx]
+        layers.append(pc)
+    full = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+    ragged_cpu = torch.randint(1, ctx + 1, (B,), generator=g, dtype=torch.int32)
+    ragged = ragged_cpu.cuda()
+    e_tok = T.tpa_cache_elems_per_token(d)
+
+    def timed(lens):
+        for i in range(2 * LAYERS):
+            L = db.layers[i % LAYERS]
+            T.tpa_paged_decode_attn(d, L["q"], layers[i % LAYERS], lens, ctx, L["ws"], out=L["out"])
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            L = db.layers[i % LAYERS]
+            evs[i][0].record()
+            T.tpa_paged_decode_attn(d, L["q"], layers[i % LAYERS], lens, ctx, L["ws"], out=L["out"])
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+    full_ms = timed(full)
+    ragged_ms = timed(ragged)
+    full_bytes = B * ctx * e_tok * 2
+    ragged_bytes = int(ragged_cpu.sum()) * e_tok * 2
+    return {"page_tokens": PAGE_TOKENS, "pages": B * pps, "table": "seeded random permutation",
+            "full_call_us": round(full_ms * 1e3, 2), "full_GBps": round(full_bytes / (full_ms * 1e-3) / 1e9, 1),
+            "ragged_keys": int(ragged_cpu.sum()), "ragged_call_us": round(ragged_ms * 1e3, 2),
+            "ragged_GBps": round(ragged_bytes / (ragged_ms * 1e-3) / 1e9, 1)}
+
+
+# ---------------------------------------------------------------------------
 # Prefill workload (reported alongside)
 # ---------------------------------------------------------------------------
 
@@ -310,6 +364,8 @@ def main():
         "roofline": roofline,
         "launch": {"hip_graph_ms_per_step": round(ms_per_step, 5), "eager_ms_per_step": round(eager_ms, 5)},
     }
+    log("[bench] paged decode")
+    result["paged_decode"] = run_paged(db)
     if not args.no_prefill:
         log("[bench] prefill workload")
         result["prefill"] = run_prefill()

@@ -6,7 +6,8 @@
 // One launch covers all four tensors (blockIdx.y).  Each sequence's block of
 // S tokens is contiguous in the source and in the cache, so the copy runs over
 // (sequence, byte-range) with the widest unit that every row, stride and
-// pointer allows.
+// pointer allows.  The paged form copies token rows to the pool rows its block
+// table names.
 #include "kernels.h"
 
 namespace tpa {
@@ -53,6 +54,58 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(append_kernel<uint32_t>, grid_for(4), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(append_kernel<uint16_t>, grid_for(2), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// Paged cache: token s of sequence b goes to position start_pos[b] + s, i.e.
+// to the pool row the block table gives for it; positions outside
+// [0, max_pos) are skipped.  One thread copies one unit of one token's row.
+template <typename U>
+__global__ void __launch_bounds__(256) append_paged_kernel(PagedAppendArgs a) {
+  const int t = blockIdx.y;
+  const int64_t units_per_tok = a.width_bytes[t] / (int64_t)sizeof(U);
+  const int64_t total = units_per_tok * a.S * a.n_batch;
+  const char* src = reinterpret_cast<const char*>(a.src[t]);
+  char* dst = reinterpret_cast<char*>(a.dst[t]);
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t tok = idx / units_per_tok;
+    const int64_t u = idx - tok * units_per_tok;
+    const int64_t b = tok / a.S, s = tok - b * a.S;
+    const int64_t pos = (int64_t)a.start_pos[b] + s;
+    if (pos < 0 || pos >= a.max_pos) continue;
+    const int64_t row = paged_row(a.pm, b, pos);
+    const U v = reinterpret_cast<const U*>(src + b * a.src_bstride[t] + s * a.width_bytes[t])[u];
+    reinterpret_cast<U*>(dst + row * a.width_bytes[t])[u] = v;
+  }
+}
+
+static bool paged_multiple(const PagedAppendArgs& a, int64_t unit) {
+  for (int t = 0; t < 4; ++t) {
+    if (a.width_bytes[t] % unit || a.src_bstride[t] % unit) return false;
+    if (((uintptr_t)a.src[t]) % unit || ((uintptr_t)a.dst[t]) % unit) return false;
+  }
+  return true;
+}
+
+hipError_t launch_append_paged(const PagedAppendArgs& a, hipStream_t st) {
+  int64_t max_bytes = 0;
+  for (int t = 0; t < 4; ++t) {
+    const int64_t v = a.width_bytes[t] * a.S * a.n_batch;
+    if (v > max_bytes) max_bytes = v;
+  }
+  auto grid_for = [&](int64_t unit) {
+    int64_t blocks = (max_bytes / unit + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    if (blocks < 1) blocks = 1;
+    return dim3((unsigned)blocks, 4);
+  };
+  if (paged_multiple(a, 16))
+    hipLaunchKernelGGL(append_paged_kernel<uint4>, grid_for(16), dim3(256), 0, st, a);
+  else if (paged_multiple(a, 4))
+    hipLaunchKernelGGL(append_paged_kernel<uint32_t>, grid_for(4), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(append_paged_kernel<uint16_t>, grid_for(2), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

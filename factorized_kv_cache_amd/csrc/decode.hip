@@ -11,7 +11,10 @@
 // The context is split into chunks, one workgroup per (sequence, chunk); each
 // writes its partial (running max m, sum l, unnormalised acc[d_h]) per head to
 // the workspace, and a combine pass merges the chunks in index order, so the
-// result does not depend on scheduling.
+// result does not depend on scheduling.  With ragged lengths, chunks past a
+// sequence's keys write an empty partial (m = -inf, l = 0, acc = 0), which the
+// combine weighs by 0; with a paged cache every token's row goes through the
+// block table.
 #include "kernels.h"
 
 namespace tpa {
@@ -53,15 +56,21 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(AttnArgs
   float* mrow = sc + kDecodeTile * h;    // [h] running max (base-2 units)
   float* lrow = mrow + h;                // [h] running sum
   float* alpha = lrow + h;               // [h] rescale of this step
+  __shared__ int64_t rows[kDecodeTile];   // cache rows of the tile's tokens
   const int64_t b = blockIdx.y;
   const int64_t c = blockIdx.x;
+  const int64_t len = seq_keys(a, b, ctx_len);
   const int64_t t0 = c * chunk;
-  const int64_t t1 = (t0 + chunk < ctx_len) ? t0 + chunk : ctx_len;
+  if (t0 >= len) {                       // past this sequence's keys: an empty partial
+    float* P = ws + ((b * n_chunks + c) * h) * (int64_t)(dh + 2);
+    for (int i = threadIdx.x; i < h * (dh + 2); i += blockDim.x) P[i] = i % (dh + 2) ? 0.f : -INFINITY;
+    return;
+  }
+  const int64_t t1 = (t0 + chunk < len) ? t0 + chunk : len;
   const T* AK = reinterpret_cast<const T*>(a.c_ak);
   const T* BK = reinterpret_cast<const T*>(a.c_bk);
   const T* AV = reinterpret_cast<const T*>(a.c_av);
   const T* BV = reinterpret_cast<const T*>(a.c_bv);
-  const int64_t seq0 = b * a.max_seq;
 
   form_query<T>(a, b, 0, qs);
   for (int hh = threadIdx.x; hh < h; hh += blockDim.x) {
@@ -74,17 +83,20 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(AttnArgs
   __syncthreads();
 
   for (int64_t tt0 = t0; tt0 < t1; tt0 += kDecodeTile) {
+    if (threadIdx.x < kDecodeTile && tt0 + threadIdx.x < t1) rows[threadIdx.x] = cache_row(a, b, tt0 + threadIdx.x);
+    __syncthreads();
     for (int item = threadIdx.x; item < kDecodeTile * h; item += blockDim.x) {
       const int tl = item / h, hh = item - tl * h;
       const int64_t t = tt0 + tl;
       float s = -INFINITY;
       if (t < t1) {
+        const int64_t row = rows[tl];
         s = 0.f;
         for (int r = 0; r < a.rk; ++r) {
-          const int64_t brow = ((seq0 + t) * a.rk + r) * dh;
+          const int64_t brow = (row * a.rk + r) * dh;
           float dot = 0.f;
           for (int d = 0; d < dh; ++d) dot = fmaf(ldf(BK, brow + d), qs[hh * dh + d], dot);
-          s = fmaf(ldf(AK, ((seq0 + t) * h + hh) * a.rk + r), dot, s);
+          s = fmaf(ldf(AK, (row * h + hh) * a.rk + r), dot, s);
         }
       }
       sc[item] = s;
@@ -115,8 +127,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(AttnArgs
         const int64_t t = tt0 + tl;
         if (t >= t1) break;
         const float p = sc[tl * h + hh];
+        const int64_t row = rows[tl];
         for (int r = 0; r < a.rv; ++r)
-          o = fmaf(p * ldf(AV, ((seq0 + t) * h + hh) * a.rv + r), ldf(BV, ((seq0 + t) * a.rv + r) * dh + d), o);
+          o = fmaf(p * ldf(AV, (row * h + hh) * a.rv + r), ldf(BV, (row * a.rv + r) * dh + d), o);
       }
       acc[j] = o;
     }
@@ -175,6 +188,10 @@ __global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(AttnArg
   __syncthreads();
   float M = -INFINITY;
   for (int c = 0; c < nc; ++c) M = fmaxf(M, mloc[c]);
+  if (M == -INFINITY) {   // every chunk empty: a sequence without keys
+    if (threadIdx.x < dh) stf(reinterpret_cast<T*>(a.out), (b * h + hh) * dh + threadIdx.x, 0.f);
+    return;
+  }
   float O = 0.f;
 #pragma unroll
   for (int j = 0; j < kCombineRegs; ++j) {

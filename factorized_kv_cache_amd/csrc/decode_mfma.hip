@@ -114,8 +114,10 @@ struct BlockRegs {
   typename RankWord<R>::type av[2][HT][C::NT];
 };
 
-// Uniform base pointers of one chunk's cache rows; per-lane offsets from them
-// are 32-bit (the plan keeps a chunk under 2^31 elements per tensor).
+// Uniform base pointers of the cache rows a block is read from (the chunk's
+// first row, or with a paged cache the block's own first row: a page holds a
+// whole number of value blocks); per-lane offsets from them are 32-bit (the
+// plan keeps a chunk under 2^31 elements per tensor).
 struct ChunkBase {
   const bf16_t* ak;
   const bf16_t* bk;
@@ -256,33 +258,56 @@ __device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf1
   wave_lds_fence();
 }
 
-template <int DH, int R, int HT>
+// PAGED: cache rows through the block table, and per-sequence key counts.
+template <int DH, int R, int HT, bool PAGED>
 __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t ctx_len, int64_t chunk,
                                                           int64_t n_chunks, float* ws) {
   using C = DecodeMfmaCfg<DH, R, HT>;
   constexpr int KS = C::KS, DT = C::DT, VBT = C::VBT, HP = C::HP, LROW = C::LROW, OST = C::OST;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform within a wave: keep it scalar, so per-block
+  // addresses (and page lookups) stay on the scalar unit
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const int h = a.h;
   const int64_t b = blockIdx.y, c = blockIdx.x;
   const int64_t t0 = c * chunk;
-  const int64_t t1 = (t0 + chunk < ctx_len) ? t0 + chunk : ctx_len;
-  const int64_t row0 = b * a.max_seq + t0;   // first cache row of this chunk
+  const int64_t len = PAGED ? seq_keys(a, b, ctx_len) : ctx_len;
+  if (PAGED && t0 >= len) {                  // past this sequence's keys: an empty partial
+    float* P = ws + (b * n_chunks + c) * (int64_t)h * (DH + 2);
+    for (int i = threadIdx.x; i < h * (DH + 2); i += blockDim.x) P[i] = i % (DH + 2) ? 0.f : -INFINITY;
+    return;
+  }
+  const int64_t t1 = (t0 + chunk < len) ? t0 + chunk : len;
+  const int64_t row0 = b * a.max_seq + t0;   // first cache row of this chunk (dense)
   const ChunkBase cb = {reinterpret_cast<const bf16_t*>(a.c_ak) + row0 * h * R,
                         reinterpret_cast<const bf16_t*>(a.c_bk) + row0 * R * DH,
                         reinterpret_cast<const bf16_t*>(a.c_av) + row0 * h * R,
                         reinterpret_cast<const bf16_t*>(a.c_bv) + row0 * R * DH};
   const int last = (int)(t1 - t0) - 1;      // chunk-local index of the last token
+  // Loads of value block vb: dense, from the chunk's base at token vb*VBT;
+  // paged, from the block's own first row (so its tokens count from 0).
+  auto load = [&](BlockRegs<DH, R, HT>& g, int vb) {
+    if constexpr (PAGED) {
+      const int64_t row = paged_row(a.pm, b, t0 + (int64_t)vb * VBT);
+      const ChunkBase pb = {reinterpret_cast<const bf16_t*>(a.c_ak) + row * h * R,
+                            reinterpret_cast<const bf16_t*>(a.c_bk) + row * R * DH,
+                            reinterpret_cast<const bf16_t*>(a.c_av) + row * h * R,
+                            reinterpret_cast<const bf16_t*>(a.c_bv) + row * R * DH};
+      load_block<DH, R, HT>(g, pb, h, 0, last - vb * VBT, lane);
+    } else {
+      load_block<DH, R, HT>(g, cb, h, vb * VBT, last, lane);
+    }
+  };
   const int nvb = (last + VBT) / VBT;
 
   // The first blocks' loads go out before the query is formed (two blocks per
   // wave at d_h = 64, one at d_h = 128).
   BlockRegs<DH, R, HT> r0;
   BlockRegs<DH, R, HT> r1;
-  if (wave < nvb) load_block<DH, R, HT>(r0, cb, h, wave * VBT, last, lane);
+  if (wave < nvb) load(r0, wave);
   if constexpr (C::kPrefetch) {
-    if (wave + 4 < nvb) load_block<DH, R, HT>(r1, cb, h, (wave + 4) * VBT, last, lane);
+    if (wave + 4 < nvb) load(r1, wave + 4);
   }
 
   // ---- query operand, via the query factors staged in LDS (one round trip).
@@ -346,15 +371,15 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
     // two register sets in flight: blocks vb and vb+4 of this wave
     for (int vb = wave; vb < nvb; vb += 8) {
       compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, lane, qop, m_run, l_run, oacc);
-      if (vb + 8 < nvb) load_block<DH, R, HT>(r0, cb, h, (vb + 8) * VBT, last, lane);
+      if (vb + 8 < nvb) load(r0, vb + 8);
       if (vb + 4 < nvb) {
         compute_block<DH, R, HT>(r1, lbv, (vb + 4) * VBT, last, lane, qop, m_run, l_run, oacc);
-        if (vb + 12 < nvb) load_block<DH, R, HT>(r1, cb, h, (vb + 12) * VBT, last, lane);
+        if (vb + 12 < nvb) load(r1, vb + 12);
       }
     }
   } else {
     for (int vb = wave; vb < nvb; vb += 4) {
-      if (vb != wave) load_block<DH, R, HT>(r0, cb, h, vb * VBT, last, lane);
+      if (vb != wave) load(r0, vb);
       compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, lane, qop, m_run, l_run, oacc);
     }
   }
@@ -432,6 +457,7 @@ bool decode_mfma_supported(int dtype, const AttnArgs& a) {
   if (a.rk == 1 && a.h > 48) return false;     // so do four at rank 1
   const size_t qbytes = (a.rq ? (size_t)a.rq * (a.h + a.d_h) : (size_t)a.h * a.d_h) * sizeof(bf16_t);
   if (qbytes > kDecodeMfmaQueryLds) return false;
+  if (a.pm.block_table && a.pm.page_tokens % 32) return false;   // pages of whole value blocks
   const void* ptrs[5] = {a.b_q, a.c_ak, a.c_bk, a.c_av, a.c_bv};
   for (int i = 0; i < 5; ++i)
     if (((uintptr_t)ptrs[i]) % 16) return false;
@@ -446,8 +472,13 @@ static void launch_cfg(const AttnArgs& a, int64_t ctx_len, int64_t chunk, int64_
                        hipStream_t st) {
   using C = DecodeMfmaCfg<DH, R, HT>;
   static_assert(C::kLds >= kDecodeMfmaQueryLds, "LDS area of the staged query factors");
-  hipLaunchKernelGGL((decode_mfma_kernel<DH, R, HT>), dim3((unsigned)n_chunks, (unsigned)a.n_batch), dim3(256),
-                     C::kLds, st, a, ctx_len, chunk, n_chunks, ws);
+  const dim3 grid((unsigned)n_chunks, (unsigned)a.n_batch);
+  if (a.pm.block_table)
+    hipLaunchKernelGGL((decode_mfma_kernel<DH, R, HT, true>), grid, dim3(256), C::kLds, st, a, ctx_len, chunk,
+                       n_chunks, ws);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<DH, R, HT, false>), grid, dim3(256), C::kLds, st, a, ctx_len, chunk,
+                       n_chunks, ws);
 }
 
 template <int DH, int R>

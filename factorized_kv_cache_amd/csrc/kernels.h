@@ -61,6 +61,38 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 
+// ---- paged factor cache ------------------------------------------------------
+// Sequence b's token t is row block_table[b * max_pages + t / page_tokens] *
+// page_tokens + t % page_tokens of the page pools.  Page slots past max_pages
+// and page ids outside [0, n_pages) are clamped (bad table contents give wrong
+// values, never accesses outside the pools).
+struct PageMap {
+  const int32_t* block_table;   // nullptr: dense cache
+  int32_t page_tokens;
+  int32_t max_pages;
+  int32_t n_pages;
+};
+
+__device__ __forceinline__ int64_t paged_row(const PageMap& pm, int64_t b, int64_t t) {
+  int64_t slot = t / pm.page_tokens;
+  slot = slot < pm.max_pages ? slot : pm.max_pages - 1;
+  int32_t page = pm.block_table[b * pm.max_pages + slot];
+  page = page < 0 ? 0 : (page >= pm.n_pages ? pm.n_pages - 1 : page);
+  return (int64_t)page * pm.page_tokens + t % pm.page_tokens;
+}
+
+struct PagedAppendArgs {
+  const void* src[4];
+  void* dst[4];               // page pools
+  int64_t width_bytes[4];     // bytes per token
+  int64_t src_bstride[4];     // bytes between sequences in src
+  int64_t n_batch, S;
+  const int32_t* start_pos;   // [n_batch] position of each sequence's token 0
+  int64_t max_pos;            // positions >= max_pos (or < 0) are not written
+  PageMap pm;
+};
+hipError_t launch_append_paged(const PagedAppendArgs& a, hipStream_t st);
+
 // ---- attention ---------------------------------------------------------------
 // Shared description of the query factors and the cache for both attention
 // kernels.  Strides are in elements.
@@ -81,7 +113,24 @@ struct AttnArgs {
   float q_scale;         // log2(e) / (R_Q * R_K * sqrt(d_h))  (R_Q -> 1 for plain Q)
   float v_scale;         // 1 / R_V
   void* out;
+  // decode over a paged cache (pm.block_table != nullptr) and/or ragged
+  // lengths (ctx_lens != nullptr: sequence b has ctx_lens[b] keys, clamped to
+  // [0, ctx_len]; a sequence with none gets a zero output)
+  PageMap pm;
+  const int32_t* ctx_lens;
 };
+
+// Cache row of token t of sequence b.
+__device__ __forceinline__ int64_t cache_row(const AttnArgs& a, int64_t b, int64_t t) {
+  return a.pm.block_table ? paged_row(a.pm, b, t) : b * a.max_seq + t;
+}
+
+// Keys of sequence b.
+__device__ __forceinline__ int64_t seq_keys(const AttnArgs& a, int64_t b, int64_t ctx_len) {
+  if (!a.ctx_lens) return ctx_len;
+  const int64_t n = a.ctx_lens[b];
+  return n < 0 ? 0 : (n > ctx_len ? ctx_len : n);
+}
 
 // Decode split: chunk_tokens keys per workgroup; partial results
 // (m, l, acc[d_h]) per (b, chunk, head) in float32, then a combine pass.

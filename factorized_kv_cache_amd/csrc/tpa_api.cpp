@@ -78,6 +78,30 @@ tpa_status check_cache(const tpa_cache* c) {
   return TPA_OK;
 }
 
+tpa_status check_paged(const tpa_paged_cache* c, int64_t n_batch) {
+  if (!c) return fail(TPA_ERR_INVALID_ARGUMENT, "paged cache is NULL");
+  if (!c->a_k || !c->b_k || !c->a_v || !c->b_v) return fail(TPA_ERR_INVALID_ARGUMENT, "a page pool is NULL");
+  if (!c->block_table) return fail(TPA_ERR_INVALID_ARGUMENT, "block_table is NULL");
+  if (c->n_pages < 1 || c->page_tokens < 1 || c->max_pages < 1 || c->max_batch < 1)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "n_pages, page_tokens, max_pages and max_batch must be >= 1");
+  if (c->n_pages >= kMaxTokens || c->page_tokens >= kMaxTokens || c->max_pages >= kMaxTokens ||
+      c->max_pages * c->page_tokens >= kMaxTokens)
+    return fail(TPA_ERR_UNSUPPORTED, "a sequence may hold at most 2^31 - 1 positions");
+  if (n_batch > c->max_batch)
+    return fail(TPA_ERR_CAPACITY, "n_batch %lld exceeds the table's max_batch %lld", (long long)n_batch,
+                (long long)c->max_batch);
+  return TPA_OK;
+}
+
+tpa::PageMap page_map(const tpa_paged_cache* c) {
+  tpa::PageMap pm;
+  pm.block_table = c->block_table;
+  pm.page_tokens = (int32_t)c->page_tokens;
+  pm.max_pages = (int32_t)c->max_pages;
+  pm.n_pages = (int32_t)c->n_pages;
+  return pm;
+}
+
 tpa_status check_query(const tpa_dims* d, const tpa_factors* q) {
   if (!q) return fail(TPA_ERR_INVALID_ARGUMENT, "query factors are NULL");
   if (!q->b_q) return fail(TPA_ERR_INVALID_ARGUMENT, "b_q (or plain Q) is NULL");
@@ -319,6 +343,78 @@ tpa_status tpa_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_ca
                 workspace ? "" : ", NULL");
   return hip_status(tpa::launch_decode(d->dtype, a, ctx_len, p, workspace, (hipStream_t)stream),
                     "tpa_decode_attn");
+}
+
+tpa_status tpa_paged_cache_append(const tpa_dims* d, const tpa_paged_cache* c, const tpa_factors* kv,
+                                  int64_t n_batch, int64_t seq_len, const int32_t* start_pos, void* stream) {
+  tpa_status st = check_dims(d);
+  if (st != TPA_OK) return st;
+  if (!kv || !kv->a_k || !kv->b_k || !kv->a_v || !kv->b_v)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "a key/value factor tensor is NULL");
+  if (!start_pos) return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos is NULL");
+  if (n_batch < 1 || seq_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and seq_len must be >= 1");
+  if (n_batch * seq_len >= kMaxTokens) return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
+  if ((st = check_paged(c, n_batch)) != TPA_OK) return st;
+  int64_t kvs;
+  if ((st = resolve_stride(kv->kv_batch_stride, seq_len, "kv_batch_stride", &kvs)) != TPA_OK) return st;
+  const int64_t es = (int64_t)elem_size(d);
+  const int64_t h = d->n_heads, dh = d->head_dim;
+  const int64_t width[4] = {h * d->rank_k * es, d->rank_k * dh * es, h * d->rank_v * es, d->rank_v * dh * es};
+  const void* src[4] = {kv->a_k, kv->b_k, kv->a_v, kv->b_v};
+  void* dst[4] = {c->a_k, c->b_k, c->a_v, c->b_v};
+  tpa::PagedAppendArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int t = 0; t < 4; ++t) {
+    a.src[t] = src[t];
+    a.dst[t] = dst[t];
+    a.width_bytes[t] = width[t];
+    a.src_bstride[t] = kvs * width[t];
+  }
+  a.n_batch = n_batch;
+  a.S = seq_len;
+  a.start_pos = start_pos;
+  a.max_pos = c->max_pages * c->page_tokens;
+  a.pm = page_map(c);
+  return hip_status(tpa::launch_append_paged(a, (hipStream_t)stream), "tpa_paged_cache_append");
+}
+
+size_t tpa_paged_decode_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t max_ctx_len) {
+  return tpa_decode_workspace_bytes(d, n_batch, max_ctx_len);
+}
+
+tpa_status tpa_paged_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_paged_cache* c,
+                                 int64_t n_batch, const int32_t* ctx_lens, int64_t max_ctx_len, void* out,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  tpa_status st = check_dims(d);
+  if (st != TPA_OK) return st;
+  if ((st = check_query(d, q)) != TPA_OK) return st;
+  if (!out) return fail(TPA_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (!ctx_lens) return fail(TPA_ERR_INVALID_ARGUMENT, "ctx_lens is NULL");
+  if (n_batch < 1 || max_ctx_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and max_ctx_len must be >= 1");
+  if (n_batch > 65535) return fail(TPA_ERR_UNSUPPORTED, "n_batch must be <= 65535");
+  if ((st = check_paged(c, n_batch)) != TPA_OK) return st;
+  if (max_ctx_len > c->max_pages * c->page_tokens)
+    return fail(TPA_ERR_CAPACITY, "max_ctx_len %lld exceeds max_pages * page_tokens = %lld", (long long)max_ctx_len,
+                (long long)(c->max_pages * c->page_tokens));
+  int64_t qs;
+  if ((st = resolve_stride(q->q_batch_stride, 1, "q_batch_stride", &qs)) != TPA_OK) return st;
+  tpa_cache view;
+  view.a_k = c->a_k;
+  view.b_k = c->b_k;
+  view.a_v = c->a_v;
+  view.b_v = c->b_v;
+  view.max_batch = c->max_batch;
+  view.max_seq = c->max_pages * c->page_tokens;
+  tpa::AttnArgs a = attn_args(d, q, qs, &view, n_batch, 1, max_ctx_len - 1, 1, out);
+  a.pm = page_map(c);
+  a.ctx_lens = ctx_lens;
+  const tpa::DecodePlan p = tpa::plan_decode(d->dtype, a, max_ctx_len);
+  const size_t need = tpa::decode_workspace_bytes(p, a);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(TPA_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
+                workspace ? "" : ", NULL");
+  return hip_status(tpa::launch_decode(d->dtype, a, max_ctx_len, p, workspace, (hipStream_t)stream),
+                    "tpa_paged_decode_attn");
 }
 
 const char* tpa_status_string(tpa_status s) {

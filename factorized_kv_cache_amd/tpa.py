@@ -39,6 +39,12 @@ class tpa_cache(ctypes.Structure):
                 ("b_v", ctypes.c_void_p), ("max_batch", ctypes.c_int64), ("max_seq", ctypes.c_int64)]
 
 
+class tpa_paged_cache(ctypes.Structure):
+    _fields_ = [("a_k", ctypes.c_void_p), ("b_k", ctypes.c_void_p), ("a_v", ctypes.c_void_p),
+                ("b_v", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("n_pages", ctypes.c_int64),
+                ("page_tokens", ctypes.c_int64), ("max_pages", ctypes.c_int64), ("max_batch", ctypes.c_int64)]
+
+
 class tpa_factors(ctypes.Structure):
     _fields_ = [("a_q", ctypes.c_void_p), ("b_q", ctypes.c_void_p), ("a_k", ctypes.c_void_p),
                 ("b_k", ctypes.c_void_p), ("a_v", ctypes.c_void_p), ("b_v", ctypes.c_void_p),
@@ -61,6 +67,11 @@ def _load():
         "tpa_decode_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64]),
         "tpa_decode_attn": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_cache), i64, i64, vp, vp,
                                            ctypes.c_size_t, vp]),
+        "tpa_paged_cache_append": (ctypes.c_int, [P(tpa_dims), P(tpa_paged_cache), P(tpa_factors), i64, i64, vp,
+                                                  vp]),
+        "tpa_paged_decode_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64]),
+        "tpa_paged_decode_attn": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_paged_cache), i64, vp, i64,
+                                                 vp, vp, ctypes.c_size_t, vp]),
         "tpa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tpa_last_error": (ctypes.c_char_p, []),
     }
@@ -74,6 +85,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("tpa_packed_weight_rows", "tpa_cache_elems_per_token", "tpa_factor_proj", "tpa_rope_b",
             "tpa_cache_append", "tpa_prefill_attn", "tpa_decode_workspace_bytes", "tpa_decode_attn",
+            "tpa_paged_cache_append", "tpa_paged_decode_workspace_bytes", "tpa_paged_decode_attn",
             "tpa_status_string", "tpa_last_error")
 
 
@@ -174,6 +186,42 @@ class Cache:
                        self.b_v[:, start_pos], 0, self.max_seq)
 
 
+@dataclasses.dataclass
+class PagedCache:
+    """Page pools [n_pages, page_tokens, ...] and an int32 block table
+    [max_batch, max_pages] on the device (see include/tpa.h)."""
+    a_k: torch.Tensor
+    b_k: torch.Tensor
+    a_v: torch.Tensor
+    b_v: torch.Tensor
+    block_table: torch.Tensor
+
+    @property
+    def n_pages(self) -> int:
+        return self.a_k.shape[0]
+
+    @property
+    def page_tokens(self) -> int:
+        return self.a_k.shape[1]
+
+    def c(self) -> tpa_paged_cache:
+        mb, mp = self.block_table.shape
+        return tpa_paged_cache(_ptr(self.a_k), _ptr(self.b_k), _ptr(self.a_v), _ptr(self.b_v),
+                               _ptr(self.block_table), self.n_pages, self.page_tokens, mp, mb)
+
+
+def new_paged_cache(dims: Dims, n_pages: int, page_tokens: int, block_table: torch.Tensor,
+                    device="cuda") -> PagedCache:
+    dt = dims.torch_dtype
+    h, d = dims.n_heads, dims.head_dim
+    assert block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous()
+    return PagedCache(torch.zeros(n_pages, page_tokens, h, dims.rank_k, dtype=dt, device=device),
+                      torch.zeros(n_pages, page_tokens, dims.rank_k, d, dtype=dt, device=device),
+                      torch.zeros(n_pages, page_tokens, h, dims.rank_v, dtype=dt, device=device),
+                      torch.zeros(n_pages, page_tokens, dims.rank_v, d, dtype=dt, device=device),
+                      block_table.to(device))
+
+
 def new_cache(dims: Dims, max_batch: int, max_seq: int, device="cuda") -> Cache:
     dt = dims.torch_dtype
     h, d = dims.n_heads, dims.head_dim
@@ -267,4 +315,29 @@ def tpa_decode_attn(dims: Dims, q: Factors, cache: Cache, ctx_len: int, workspac
     _check(_lib.tpa_decode_attn(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B, ctx_len,
                                 _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream)))
+    return out
+
+
+def tpa_paged_cache_append(dims: Dims, cache: PagedCache, kv: Factors, start_pos: torch.Tensor, stream=None):
+    """start_pos: int32 [B] on the device (position of each sequence's token 0)."""
+    B, S = kv.a_k.shape[0], kv.a_k.shape[1]
+    assert start_pos.dtype == torch.int32 and start_pos.numel() >= B
+    _check(_lib.tpa_paged_cache_append(ctypes.byref(dims.c()), ctypes.byref(cache.c()), ctypes.byref(kv.c()), B, S,
+                                       _ptr(start_pos), _stream(stream)))
+
+
+def tpa_paged_decode_workspace_bytes(dims: Dims, batch: int, max_ctx_len: int) -> int:
+    return int(_lib.tpa_paged_decode_workspace_bytes(ctypes.byref(dims.c()), batch, max_ctx_len))
+
+
+def tpa_paged_decode_attn(dims: Dims, q: Factors, cache: PagedCache, ctx_lens: torch.Tensor, max_ctx_len: int,
+                          workspace: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """ctx_lens: int32 [B] on the device, each in [0, max_ctx_len]."""
+    B = q.b_q.shape[0]
+    assert ctx_lens.dtype == torch.int32 and ctx_lens.numel() >= B
+    if out is None:
+        out = torch.empty(B, dims.n_heads * dims.head_dim, dtype=dims.torch_dtype, device=q.b_q.device)
+    _check(_lib.tpa_paged_decode_attn(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B,
+                                      _ptr(ctx_lens), max_ctx_len, _ptr(out), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)))
     return out

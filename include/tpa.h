@@ -186,14 +186,71 @@ size_t tpa_decode_workspace_bytes(const tpa_dims* dims, int64_t n_batch, int64_t
  * q: the new token's query factors, a_q [B,h,R_Q], b_q [B,R_Q,d_h]
  * (KV-only: b_q = Q [B,h,d_h]); out [B, h*d_h].
  * workspace: device memory of at least tpa_decode_workspace_bytes(dims, B,
- * ctx_len) bytes, zero-filled before its first use with this library; every
- * call leaves it ready for the next one.  Calls that may run at the same time
+ * ctx_len) bytes; it holds per-chunk partial results during the call only, so
+ * its contents on entry do not matter.  Calls that may run at the same time
  * must not share a workspace.
  * Errors: null pointers, ctx_len < 1, B > max_batch or ctx_len > max_seq
  * (TPA_ERR_CAPACITY), workspace too small (TPA_ERR_WORKSPACE). */
 tpa_status tpa_decode_attn(const tpa_dims* dims, const tpa_factors* q, const tpa_cache* cache,
                            int64_t n_batch, int64_t ctx_len, void* out, void* workspace, size_t ws_bytes,
                            void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Paged factor cache (serving layout: the pages do not describe one; the
+ * arithmetic is that of tpa_cache_append and tpa_decode_attn).
+ *
+ * The four factor tensors are pools of fixed-size pages,
+ *   a_k [n_pages, page_tokens, h, R_K]   b_k [n_pages, page_tokens, R_K, d_h]
+ *   a_v [n_pages, page_tokens, h, R_V]   b_v [n_pages, page_tokens, R_V, d_h],
+ * and block_table [max_batch, max_pages] (int32, device memory) names, for
+ * sequence b, the page holding its tokens i*page_tokens .. (i+1)*page_tokens-1
+ * in column i.  Pages may appear in any order (and be shared); columns past a
+ * sequence's length are never read.  The library does not read the table on
+ * the host: page ids outside [0, n_pages) are clamped into the pool, which
+ * gives wrong values but never an access outside it.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  void* a_k;
+  void* b_k;
+  void* a_v;
+  void* b_v;
+  const int32_t* block_table;
+  int64_t n_pages;
+  int64_t page_tokens;
+  int64_t max_pages;  /* table columns: a sequence holds up to max_pages*page_tokens tokens */
+  int64_t max_batch;  /* table rows */
+} tpa_paged_cache;
+
+/* Paged cache append: token s of sequence b of `kv` is written, bit for bit, to
+ * position start_pos[b] + s of sequence b (start_pos: int32 device array [B]).
+ * Positions outside [0, max_pages*page_tokens) are skipped.  kv->a_q / b_q are
+ * ignored.
+ *   Passage: the cache writes of the code walk-through (前向传播), with each
+ *   sequence's positions mapped through its page list.
+ * Errors: null pointers, B or S < 1, B > max_batch, n_pages, page_tokens or
+ * max_pages < 1, or more than 2^31 positions per sequence. */
+tpa_status tpa_paged_cache_append(const tpa_dims* dims, const tpa_paged_cache* cache, const tpa_factors* kv,
+                                  int64_t n_batch, int64_t seq_len, const int32_t* start_pos, void* stream);
+
+/* Bytes of device workspace tpa_paged_decode_attn needs (the same as
+ * tpa_decode_workspace_bytes for ctx_len = max_ctx_len). */
+size_t tpa_paged_decode_workspace_bytes(const tpa_dims* dims, int64_t n_batch, int64_t max_ctx_len);
+
+/* Decode attention over a paged cache, each sequence with its own key count:
+ * sequence b attends over its keys 0 .. ctx_lens[b] - 1 (ctx_lens: int32
+ * device array [B]; each value is clamped to [0, max_ctx_len], and a sequence
+ * with no keys gets a zero output).  Arithmetic, split and merge order are
+ * those of tpa_decode_attn with ctx_len = max_ctx_len, so with an identity
+ * table and every length equal to max_ctx_len the two give the same bits
+ * (when both run the same kernel: the matrix-core kernel needs page_tokens to
+ * be a multiple of 32).
+ *   Passage: as tpa_decode_attn.
+ * q, out, workspace: as tpa_decode_attn.
+ * Errors: null pointers, B or max_ctx_len < 1, B > max_batch, max_ctx_len >
+ * max_pages*page_tokens (TPA_ERR_CAPACITY), workspace too small. */
+tpa_status tpa_paged_decode_attn(const tpa_dims* dims, const tpa_factors* q, const tpa_paged_cache* cache,
+                                 int64_t n_batch, const int32_t* ctx_lens, int64_t max_ctx_len, void* out,
+                                 void* workspace, size_t ws_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* tpa_status_string(tpa_status status);

@@ -33,6 +33,10 @@ causal with the diagonal visible; the 1/R factors of the equations apply (not
 the unscaled sum of [jieyibu] Ⅱ.2); decode attends over the new token too (the
 forward code writes the cache before it reads it).
 
+Paged and ragged decode (paged_gather, decode_paged) serve a layout the pages
+do not describe: each sequence's tokens are gathered through its page list and
+run through the same decode; a sequence with no keys gets a zero output.
+
 Everything is float64.  Inputs given in bf16 arrive here as their exact values
 widened to float64.  Loops run over (batch, head) in Python; numpy's matmul is
 the only library primitive used for contractions.  No blocking, no online
@@ -258,6 +262,40 @@ def decode(fq: Dict[str, np.ndarray], cache: Dict[str, np.ndarray], dims: Dims, 
     Returns out [B, h*d_h].
     """
     return prefill(fq, cache, dims, batch, 1, ctx_len - 1, causal=True)[:, 0, :]
+
+
+def paged_gather(pools: Dict[str, np.ndarray], block_table: np.ndarray, b: int, n: int) -> Dict[str, np.ndarray]:
+    """Cache rows of tokens 0..n-1 of sequence b from page pools [n_pages, P, ...].
+
+    Serving layout, not on the pages: token t of sequence b lives in page
+    block_table[b, t // P] at row t % P.
+    """
+    P = pools["a_k"].shape[1]
+    t = np.arange(n, dtype=np.int64)
+    pages = np.asarray(block_table, dtype=np.int64)[b, t // P]
+    rows = t % P
+    return {k: np.asarray(pools[k], dtype=np.float64)[pages, rows] for k in ("a_k", "b_k", "a_v", "b_v")}
+
+
+def decode_paged(fq: Dict[str, np.ndarray], pools: Dict[str, np.ndarray], block_table: np.ndarray,
+                 ctx_lens, dims: Dims) -> np.ndarray:
+    """Decode with a key count per sequence over a paged cache: sequence b's new
+    query (position ctx_lens[b]-1) attends over its keys 0..ctx_lens[b]-1, exactly
+    as decode() does for one sequence.  A sequence with no keys gets zeros
+    (a convention: the pages never call attention over nothing).
+    Returns out [B, h*d_h].
+    """
+    B = len(ctx_lens)
+    out = np.zeros((B, dims.n_heads * dims.head_dim), dtype=np.float64)
+    for b in range(B):
+        L = int(ctx_lens[b])
+        if L == 0:
+            continue
+        rows = paged_gather(pools, block_table, b, L)
+        cache_b = {k: v[None] for k, v in rows.items()}
+        fq_b = {k: (None if v is None else np.asarray(v)[b:b + 1]) for k, v in fq.items()}
+        out[b] = decode(fq_b, cache_b, dims, 1, L)[0]
+    return out
 
 
 def layer_forward(x: np.ndarray, w: Dict[str, np.ndarray], dims: Dims, cache: Dict[str, np.ndarray],

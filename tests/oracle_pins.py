@@ -15,6 +15,8 @@ What pins what:
   softmax_rows         attention rows sum to 1, outputs lie in the hull of the values
   closed_form_*        hand-derived values and exact special cases
   incremental_*        chunked prefill and decode against one long prefill
+  paged_*              decode with a key count per sequence over a paged cache,
+                       against the brute force run on each sequence's own prefix
 """
 import math
 
@@ -386,9 +388,79 @@ def incremental_chunked_prefill():
     _close(np.concatenate(outs, axis=1), full, what="chunked prefill")
 
 
+# --------------------------------------------------------------------------
+# Paged cache, key count per sequence
+# --------------------------------------------------------------------------
+
+def _scatter_pages(f, table, P, n_pages):
+    """Inverse of a gather through the table: token t of sequence b goes to page
+    table[b, t // P], row t % P (unused rows hold a value no sequence reads)."""
+    pools = {}
+    for k in ("a_k", "b_k", "a_v", "b_v"):
+        B, T = f[k].shape[:2]
+        pool = np.full((n_pages, P) + f[k].shape[2:], 7.0e3)
+        for b in range(B):
+            for t in range(T):
+                pool[table[b, t // P], t % P] = f[k][b, t]
+        pools[k] = pool
+    return pools
+
+
+PAGED_CASES = [
+    # d_model, h, d_h, R_Q, R_K, R_V, base, page, lengths
+    (6, 3, 4, 2, 3, 1, 10000.0, 2, (5, 1, 0, 3)),
+    (5, 2, 6, 0, 2, 2, 7.0, 3, (4, 6)),
+]
+
+
+def _paged_case(ci, seed):
+    dm, h, d, rq, rk, rv, base, P, lens = PAGED_CASES[ci]
+    rng = np.random.default_rng(seed)
+    dims = O.Dims(dm, h, d, rq, rk, rv, base)
+    B, T = len(lens), max(lens)
+    x = rng.normal(0, 1, (B, T, dm))
+    w = _weights(rng, dims)
+    f = O.rotate_factors(O.project(x, w, dims), 0, dims)
+    pages_per_seq = (T + P - 1) // P
+    n_pages = B * pages_per_seq + 2
+    table = rng.permutation(n_pages)[:B * pages_per_seq].reshape(B, pages_per_seq)
+    # each sequence's query factors at its own last position
+    qkeys = ("q",) if dims.kv_only else ("a_q", "b_q")
+    fq = {k: np.stack([f[k][b, max(lens[b] - 1, 0)] for b in range(B)])[:, None] for k in qkeys}
+    return dims, x, w, f, fq, table, n_pages, P, lens
+
+
+def paged_ragged_brute_force():
+    """Decode with ctx_lens[b] keys for sequence b, through a shuffled page table,
+    equals the brute force's last row on that sequence's own prefix; a sequence
+    without keys gives zeros."""
+    for ci in range(len(PAGED_CASES)):
+        dims, x, w, f, fq, table, n_pages, P, lens = _paged_case(ci, 300 + ci)
+        pools = _scatter_pages(f, table, P, n_pages)
+        got = O.decode_paged(fq, pools, table, lens, dims)
+        for b, L in enumerate(lens):
+            if L == 0:
+                _close(got[b], np.zeros_like(got[b]), what=f"paged case {ci} empty sequence {b}")
+                continue
+            ref = brute_force.layer(x[b:b + 1, :L].tolist(), {k: v.tolist() for k, v in w.items()},
+                                    dims.d_model, dims.n_heads, dims.head_dim, dims.rank_q, dims.rank_k,
+                                    dims.rank_v, dims.rope_base, causal=True)
+            _close(got[b], ref[0][L - 1], what=f"paged case {ci} sequence {b}")
+
+
+def paged_permutation_invariance():
+    """Moving pages to other pool slots (with the table updated) changes nothing."""
+    dims, x, w, f, fq, table, n_pages, P, lens = _paged_case(0, 400)
+    a = O.decode_paged(fq, _scatter_pages(f, table, P, n_pages), table, lens, dims)
+    perm = np.random.default_rng(401).permutation(n_pages)
+    table2 = perm[table]
+    b = O.decode_paged(fq, _scatter_pages(f, table2, P, n_pages), table2, lens, dims)
+    assert np.array_equal(a, b), "paged decode depends on where the pages sit"
+
+
 ALL_PINS = [
     brute_force_causal, brute_force_noncausal, textbook_mha, textbook_mqa, textbook_gqa,
     rope_identities, rope_textbook, commute_rope_factor_sum, commute_code_order_attention,
     softmax_rows, closed_form_two_tokens, closed_form_special_cases, incremental_decode,
-    incremental_chunked_prefill,
+    incremental_chunked_prefill, paged_ragged_brute_force, paged_permutation_invariance,
 ]

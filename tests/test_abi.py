@@ -154,6 +154,35 @@ def test_decode_validation():
     assert lib.tpa_decode_workspace_bytes(ctypes.byref(dims(head_dim=5)), 16, 4097) == 0
 
 
+def test_paged_validation():
+    lib = T.library()
+    d = dims()
+    pc = T.tpa_paged_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 64, 65, 16)   # 65 pages of 64 = 4160 positions
+    q = T.tpa_factors(FAKE, FAKE, None, None, None, None, 0, 0)
+    kv = T.tpa_factors(None, None, FAKE, FAKE, FAKE, FAKE, 0, 0)
+    need = lib.tpa_paged_decode_workspace_bytes(ctypes.byref(d), 16, 4097)
+    assert need == lib.tpa_decode_workspace_bytes(ctypes.byref(d), 16, 4097) > 0
+    dec = lambda B, L, ws, n, c=pc, lens=FAKE: lib.tpa_paged_decode_attn(
+        ctypes.byref(d), ctypes.byref(q), ctypes.byref(c), B, lens, L, FAKE, ws, n, None)
+    assert dec(16, 4097, FAKE, need - 1) == WORKSPACE
+    assert dec(16, 4097, None, need) == WORKSPACE
+    assert dec(17, 4097, FAKE, need) == CAPACITY                     # more sequences than table rows
+    assert dec(16, 4161, FAKE, need * 2) == CAPACITY                 # past max_pages * page_tokens
+    assert dec(16, 0, FAKE, need) == INVALID
+    assert dec(16, 4097, FAKE, need, lens=None) == INVALID           # no lengths
+    assert dec(16, 4097, FAKE, need, c=T.tpa_paged_cache(FAKE, FAKE, FAKE, FAKE, None, 100, 64, 65, 16)) == INVALID
+    assert dec(16, 4097, FAKE, need, c=T.tpa_paged_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 65, 16)) == INVALID
+    assert dec(16, 4097, FAKE, need, c=T.tpa_paged_cache(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 1 << 20, 1 << 12,
+                                                         16)) == UNSUPPORTED   # 2^32 positions
+    app = lambda B, S, sp=FAKE, c=pc, k=kv: lib.tpa_paged_cache_append(ctypes.byref(d), ctypes.byref(c),
+                                                                        ctypes.byref(k), B, S, sp, None)
+    assert app(17, 1) == CAPACITY
+    assert app(1, 0) == INVALID
+    assert app(1, 1, sp=None) == INVALID
+    assert app(1, 1, k=T.tpa_factors(None, None, FAKE, None, FAKE, FAKE, 0, 0)) == INVALID
+    assert app(1, 1, c=T.tpa_paged_cache(None, FAKE, FAKE, FAKE, FAKE, 100, 64, 65, 16)) == INVALID
+
+
 def test_status_strings():
     lib = T.library()
     for s in range(6):

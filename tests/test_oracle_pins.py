@@ -23,7 +23,7 @@ def test_pin(pin):
 
 _orig = {name: getattr(O, name) for name in
          ("rope", "rope_angles", "reconstruct", "project", "attend_head", "cache_append", "rotate_factors",
-          "prefill", "positions")}
+          "prefill", "positions", "paged_gather", "decode_paged")}
 
 
 def _rope_sign(v, pos, base):
@@ -119,6 +119,24 @@ def _prefill_v_from_k(fq, cache, dims, batch, seq, start_pos, causal=True, rows=
     return _orig["prefill"](fq, c, dims, batch, seq, start_pos, causal, rows)
 
 
+def _gather_next_row(pools, block_table, b, n):
+    """Rows shifted by one within each page."""
+    P = pools["a_k"].shape[1]
+    t = np.arange(n, dtype=np.int64)
+    pages = np.asarray(block_table, dtype=np.int64)[b, t // P]
+    return {k: np.asarray(pools[k], dtype=np.float64)[pages, (t + 1) % P] for k in ("a_k", "b_k", "a_v", "b_v")}
+
+
+def _gather_first_table_row(pools, block_table, b, n):
+    return _orig["paged_gather"](pools, block_table, 0, n)
+
+
+def _decode_paged_max_len(fq, pools, block_table, ctx_lens, dims):
+    """Every sequence attends over the longest sequence's key count."""
+    m = max(int(v) for v in ctx_lens)
+    return _orig["decode_paged"](fq, pools, block_table, [m if int(v) else 0 for v in ctx_lens], dims)
+
+
 MUTATIONS = {
     "rope rotates the wrong way": ("rope", _rope_sign),
     "rope pairs (i, i+d/2)": ("rope", _rope_half_split),
@@ -132,6 +150,9 @@ MUTATIONS = {
     "query positions off by one": ("rotate_factors", _rotate_queries_shifted),
     "queries left unrotated": ("rotate_factors", _rotate_keys_only),
     "values built from the wrong factors": ("prefill", _prefill_v_from_k),
+    "paged rows shifted within a page": ("paged_gather", _gather_next_row),
+    "every sequence read through the first table row": ("paged_gather", _gather_first_table_row),
+    "ragged lengths ignored": ("decode_paged", _decode_paged_max_len),
 }
 
 
