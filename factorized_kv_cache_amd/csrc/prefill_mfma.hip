@@ -4,8 +4,10 @@
 // Arithmetic as the general prefill kernel ("Tensor Product Attention Is All
 // You Need" review on coreui.cn: Q_t/K_t/V_t equations of 核心机制总结 and the
 // masked softmax attention of the code walk-through 前向传播), mapped as follows.
-// A workgroup owns 128 queries of one head of one sequence; each of its four
-// waves owns 32 of them (two 16-query tiles).  For every block of 64 keys:
+// A workgroup owns BM queries of one head of one sequence and each of its four
+// waves QT 16-query tiles (d_h = 64: 256 queries, 64 per wave, against 32-key
+// blocks; d_h = 128: 128 queries, 32 per wave, against 64-key blocks).  For
+// every key block:
 //
 //  * rebuild: the whole workgroup forms k_t = sum_r A_K[t,h,r] B~_K[t,r,:] and
 //    v_t = sum_r A_V[t,h,r] B_V[t,r,:] for the block (rank pairs through
@@ -109,16 +111,25 @@ __device__ __forceinline__ void factor_combine(typename RankWordP<R>::type a, co
   }
 }
 
+// d_h = 64: 256 queries per workgroup (64 per wave) against 32-key blocks, so
+// every K / V^T element read from LDS serves 64 queries; d_h = 128: 128
+// queries (32 per wave) against 64-key blocks (wider rows leave registers for
+// fewer query tiles).  Either way a wave does 36 (d_h = 64) or 72 matrix ops per
+// block between barriers.
 template <int DH>
 struct PrefillMfmaCfg {
-  static constexpr int BM = 128;         // queries per workgroup
-  static constexpr int BN = 64;          // keys per block
-  static constexpr int QT = 2;           // 16-query tiles per wave
+  static constexpr int QT = DH == 64 ? 4 : 2;     // 16-query tiles per wave
+  static constexpr int BM = 4 * 16 * QT;          // queries per workgroup
+  static constexpr int BN = DH == 64 ? 32 : 64;   // keys per block
+  static constexpr int KT = BN / 16;              // 16-key tiles of the score product
+  static constexpr int KB = BN / 32;              // 32-key steps of the value product
   static constexpr int KS = DH / 32;     // k-steps of the score product
   static constexpr int DT = DH / 16;     // d tiles of the value product (one more holds the ones row)
   static constexpr int LDK = DH + 8;     // K row stride in LDS (bf16)
   static constexpr int LDV = BN + 4;     // V^T row stride in LDS (bf16), 8-byte aligned rows
-  static constexpr int IT = DH / 64;     // rebuild items (2 keys x 8 d's) per thread
+  // rebuild items: KPI consecutive keys x an 8-wide d slice, IT per thread
+  static constexpr int KPI = BN * (DH / 8) >= 512 ? 2 : 1;
+  static constexpr int IT = BN * (DH / 8) / KPI / 256;
   static constexpr int KTILE = BN * LDK;            // bf16 elements of one K buffer
   static constexpr int VTILE = (DH + 16) * LDV;     // bf16 elements of one V^T buffer
   static constexpr size_t kLds = (size_t)2 * (KTILE + VTILE) * sizeof(bf16_t);
@@ -135,23 +146,24 @@ constexpr int prefill_prefetch_depth() {
 }
 
 // The cached factors one thread needs for its rebuild items of one key block:
-// keys 2*kp and 2*kp+1, d slice d0 .. d0+7.
+// keys KPI*kg .. KPI*kg+KPI-1, d slice d0 .. d0+7.
 template <int DH, int R>
 struct RebuildRegs {
   static constexpr int IT = PrefillMfmaCfg<DH>::IT;
-  uint4 bk[IT][2][R];
-  uint4 bv[IT][2][R];
-  typename RankWordP<R>::type ak[IT][2];
-  typename RankWordP<R>::type av[IT][2];
+  static constexpr int KPI = PrefillMfmaCfg<DH>::KPI;
+  uint4 bk[IT][KPI][R];
+  uint4 bv[IT][KPI][R];
+  typename RankWordP<R>::type ak[IT][KPI];
+  typename RankWordP<R>::type av[IT][KPI];
 };
 
-// Item = (key pair kp, 8-wide d slice d0).  Consecutive lanes take consecutive
-// d slices of one key pair, so the DH/8 lanes of a key read each rank row of
+// Item = (key group kg, 8-wide d slice d0).  Consecutive lanes take consecutive
+// d slices of one key group, so the DH/8 lanes of a key read each rank row of
 // B~_K / B_V as whole, contiguous cache lines.
 template <int DH>
-__device__ __forceinline__ void rebuild_item(int it, int& kp, int& d0) {
+__device__ __forceinline__ void rebuild_item(int it, int& kg, int& d0) {
   const int item = threadIdx.x + 256 * it;
-  kp = item / (DH / 8);
+  kg = item / (DH / 8);
   d0 = (item % (DH / 8)) * 8;
 }
 
@@ -168,11 +180,11 @@ __device__ __forceinline__ void load_rebuild(RebuildRegs<DH, R>& g, const AttnAr
   const bf16_t* BV = reinterpret_cast<const bf16_t*>(a.c_bv);
 #pragma unroll
   for (int it = 0; it < C::IT; ++it) {
-    int kp, d0;
-    rebuild_item<DH>(it, kp, d0);
+    int kg, d0;
+    rebuild_item<DH>(it, kg, d0);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      int64_t t = k0 + 2 * kp + k;
+    for (int k = 0; k < C::KPI; ++k) {
+      int64_t t = k0 + C::KPI * kg + k;
       t = t < kend ? t : kend - 1;
       const int64_t row = seq0 + t;
       g.ak[it][k] = *reinterpret_cast<const W*>(AK + (row * a.h + hh) * R);
@@ -191,22 +203,27 @@ __device__ __forceinline__ void store_rebuild(const RebuildRegs<DH, R>& g, bf16_
   using C = PrefillMfmaCfg<DH>;
 #pragma unroll
   for (int it = 0; it < C::IT; ++it) {
-    int kp, d0;
-    rebuild_item<DH>(it, kp, d0);
-    float kv[2][8], vv[2][8];
+    int kg, d0;
+    rebuild_item<DH>(it, kg, d0);
+    float kv[C::KPI][8], vv[C::KPI][8];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < C::KPI; ++k) {
       factor_combine<R>(g.ak[it][k], g.bk[it][k], kv[k]);
       factor_combine<R>(g.av[it][k], g.bv[it][k], vv[k]);
-      *reinterpret_cast<bf16x8_t*>(ks_lds + (2 * kp + k) * C::LDK + d0) = pack8(kv[k]);
+      *reinterpret_cast<bf16x8_t*>(ks_lds + (C::KPI * kg + k) * C::LDK + d0) = pack8(kv[k]);
     }
+    if constexpr (C::KPI == 2) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<uint32_t*>(vt_lds + (d0 + j) * C::LDV + 2 * kp) = pack_bf16x2(vv[0][j], vv[1][j]);
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint32_t*>(vt_lds + (d0 + j) * C::LDV + 2 * kg) = pack_bf16x2(vv[0][j], vv[1][j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vt_lds[(d0 + j) * C::LDV + kg] = f32_to_bf16(vv[0][j]);
+    }
   }
 }
 
-// One key block of the online-softmax attention for this wave's 2 x 16 queries
+// One key block of the online-softmax attention for this wave's QT x 16 queries
 // (positions wpos0 ..), reading K and V^T of the block from LDS.
 template <int DH>
 __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t* vt_lds, int64_t k0, int64_t kend,
@@ -216,10 +233,11 @@ __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t*
                                              f32x4_t (&oacc)[PrefillMfmaCfg<DH>::QT][PrefillMfmaCfg<DH>::DT + 1]) {
   using C = PrefillMfmaCfg<DH>;
   constexpr int BN = C::BN, QT = C::QT, KS = C::KS, DT = C::DT, LDK = C::LDK, LDV = C::LDV;
-    // ---- scores S^T[key, query] for the block's 4 key tiles
-    f32x4_t sacc[4][QT];
+  constexpr int KT = C::KT, KB = C::KB;
+    // ---- scores S^T[key, query] for the block's key tiles
+    f32x4_t sacc[KT][QT];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       bf16x8_t kf[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
@@ -237,7 +255,7 @@ __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t*
     const bool need_mask = (causal && k0 + BN - 1 > wpos0) || (k0 + BN > kend);
     if (need_mask) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -250,12 +268,12 @@ __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t*
     }
 
     // ---- online softmax per query (lazy rescale), P^T operands
-    bf16x8_t pop[QT][2];
+    bf16x8_t pop[QT][KB];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       float bmax = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, sacc[kt][qt][i]);
       bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
@@ -271,7 +289,7 @@ __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t*
       // a query with no visible key yet keeps m = -inf; its probabilities are 0
       const float m_use = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         float pv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(sacc[2 * kb + (j >> 2)][qt][j & 3] - m_use);
@@ -283,7 +301,7 @@ __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t*
 #pragma unroll
     for (int dt = 0; dt <= DT; ++dt) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         const bf16_t* vrow = vt_lds + (dt * 16 + li) * LDV + kb * 32 + 4 * lg;
         const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
         const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
@@ -339,14 +357,14 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
     VT_BUF(1)[(DH + rr) * LDV + col] = v;
   }
 
-  // ---- query operand: lane (query q0 + 32*wave + 16*qt + li, slice lg)
+  // ---- query operand: lane (query q0 + 16*QT*wave + 16*qt + li, slice lg)
   bf16x8_t qop[QT][KS];
   {
     const bf16_t* AQ = reinterpret_cast<const bf16_t*>(a.a_q);
     const bf16_t* BQ = reinterpret_cast<const bf16_t*>(a.b_q);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const int64_t s = q0 + 32 * wave + 16 * qt + li;
+      const int64_t s = q0 + 16 * QT * wave + 16 * qt + li;
       const int64_t tok = b * a.q_bstride_tok + (s < a.S ? s : a.S - 1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -383,7 +401,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
   }
 
   constexpr int kDepth = prefill_prefetch_depth<DH, R>();
-  const int64_t wpos0 = a.start_pos + q0 + 32 * wave;   // first position of this wave's queries
+  const int64_t wpos0 = a.start_pos + q0 + 16 * QT * wave;   // first position of this wave's queries
   const bool causal = a.causal != 0;
   // Block i is rebuilt into buffer i & 1 while block i - 1 is attended to.
   store_rebuild<DH, R>(rg, KS_BUF(0), VT_BUF(0));
@@ -415,7 +433,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
   for (int qt = 0; qt < QT; ++qt) {
     const float l = __shfl(oacc[qt][DT][0], li);
     const float inv = a.v_scale / l;
-    const int64_t s = q0 + 32 * wave + 16 * qt + li;
+    const int64_t s = q0 + 16 * QT * wave + 16 * qt + li;
     if (s < a.S) {
       bf16_t* orow = out + ((b * a.S + s) * h + hh) * (int64_t)DH;
 #pragma unroll
@@ -440,7 +458,8 @@ bool prefill_mfma_supported(int dtype, const AttnArgs& a) {
   if (dtype != kBF16) return false;
   const size_t lds = a.d_h == 64 ? PrefillMfmaCfg<64>::kLds : PrefillMfmaCfg<128>::kLds;
   if (lds > device_lds_per_block()) return false;
-  if ((a.S + 127) / 128 * (int64_t)a.h * a.n_batch >= ((int64_t)1 << 31)) return false;
+  const int bm = a.d_h == 64 ? PrefillMfmaCfg<64>::BM : PrefillMfmaCfg<128>::BM;
+  if ((a.S + bm - 1) / bm * (int64_t)a.h * a.n_batch >= ((int64_t)1 << 31)) return false;
   if (!(a.d_h == 64 || a.d_h == 128)) return false;
   if (a.rk != a.rv || !(a.rk == 1 || a.rk == 2 || a.rk == 4)) return false;
   if (a.d_h == 128 && a.rk == 4) return false;   // its registers would spill
@@ -451,7 +470,8 @@ bool prefill_mfma_supported(int dtype, const AttnArgs& a) {
 }
 
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t st) {
-  const int nqb = (int)((a.S + 127) / 128);
+  const int bm = a.d_h == 64 ? PrefillMfmaCfg<64>::BM : PrefillMfmaCfg<128>::BM;
+  const int nqb = (int)((a.S + bm - 1) / bm);
   const dim3 grid((unsigned)((int64_t)nqb * a.h * a.n_batch));
 #define TPA_PREFILL_LAUNCH(DH_, R_)                                                               \
   hipLaunchKernelGGL((prefill_mfma_kernel<DH_, R_>), grid, dim3(256), PrefillMfmaCfg<DH_>::kLds, st, a, \
