@@ -14,7 +14,8 @@
 //    so the contraction is unchanged.
 //  * the head factor: every lane's 4 output rows of a tile are R whole tokens'
 //    ranks (R in {1,2,4}), so s_t = sum_r A_K[t,head,r] P[(t,r),head] is
-//    lane-local; the block maximum per head needs two cross-lane xor steps.
+//    lane-local; the block maximum per head crosses the four lane groups with
+//    two half-wave swaps.
 //  * values: O^T[d, head] += B_V^T[d, (t,r)] * C[(t,r), head] with
 //    C = p_t * A_V[t,head,r].  The score tiles' output registers already sit
 //    in the B-operand layout of this product (k-slot j of lane group g is row
@@ -218,8 +219,7 @@ __device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf1
         s[st][k] = valid ? v : -INFINITY;
         bmax = fmaxf(bmax, s[st][k]);
       }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    bmax = lane_group_max(bmax);
     const float m_new = fmaxf(m_run[ht], bmax);
     const float alpha = fast_exp2(m_run[ht] - m_new);
     m_run[ht] = m_new;
@@ -387,8 +387,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
   // ---- merge the four waves (fixed order) and write this chunk's partial
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
-    l_run[ht] += __shfl_xor(l_run[ht], 16);
-    l_run[ht] += __shfl_xor(l_run[ht], 32);
+    l_run[ht] = lane_group_sum(l_run[ht]);
   }
   __syncthreads();
   float* mbuf = reinterpret_cast<float*>(smem);  // [4][HP]

@@ -30,4 +30,23 @@ __device__ __forceinline__ bf16x8_t pack8(const float* v) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
+// Maximum / sum of x over the lanes l, l^16, l^32, l^48 (the four lane groups
+// that hold one column of a 16x16 tile), with the gfx950 half-wave swaps:
+// after permlane32_swap(x, x) lane l holds x[l] and x[l^32]; after
+// permlane16_swap(y, y) it holds y[l] and y[l^16].  The sum adds the pairs in
+// the same order in every lane, so all four lanes get the same bits.
+__device__ __forceinline__ float lane_group_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float lane_group_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace tpa

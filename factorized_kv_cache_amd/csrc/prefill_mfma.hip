@@ -22,7 +22,8 @@
 //    is folded into Q), masking only on blocks that reach past a query.  The
 //    running maximum moves only when a block's maximum exceeds it by more than
 //    8 (then every probability stays below 2^8), so most blocks skip the
-//    rescale; the result does not depend on the reference maximum;
+//    rescale; the result does not depend on the reference maximum.  The block
+//    maximum crosses lane groups by half-wave swaps, not through LDS;
 //  * values, transposed: O^T[d, q] += V^T[d, t] P^T[t, q]; the score tiles'
 //    output registers are already the B operand of this product (k-slot j of
 //    lane group g is key 4g+j of one 16-key tile for j<4, of the next for j>=4),
@@ -276,8 +277,7 @@ __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t*
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, sacc[kt][qt][i]);
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      bmax = lane_group_max(bmax);
       const bool grow = bmax > m_run[qt] + (TPA_PF_LAZY ? C::kRescaleSlack : 0.f);
       if (__any(grow)) {
         const float m_new = grow ? bmax : m_run[qt];
