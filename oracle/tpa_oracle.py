@@ -33,8 +33,11 @@ causal with the diagonal visible; the 1/R factors of the equations apply (not
 the unscaled sum of [jieyibu] Ⅱ.2); decode attends over the new token too (the
 forward code writes the cache before it reads it).
 
-Paged and ragged decode (paged_gather, decode_paged) serve a layout the pages
-do not describe: each sequence's tokens are gathered through its page list and
+The backward functions (reconstruct_backward, attend_head_backward,
+prefill_backward, rope_backward) are the chain rule through the same
+definitions, written out; they serve training, which the pages mention as
+context.  Paged and ragged decode (paged_gather, decode_paged) serve a layout
+the pages do not describe: each sequence's tokens are gathered through its page list and
 run through the same decode; a sequence with no keys gets a zero output.
 
 Everything is float64.  Inputs given in bf16 arrive here as their exact values
@@ -262,6 +265,94 @@ def decode(fq: Dict[str, np.ndarray], cache: Dict[str, np.ndarray], dims: Dims, 
     Returns out [B, h*d_h].
     """
     return prefill(fq, cache, dims, batch, 1, ctx_len - 1, causal=True)[:, 0, :]
+
+
+# --------------------------------------------------------------------------
+# Backward (training): gradients of prefill() by the chain rule, written out
+# --------------------------------------------------------------------------
+
+def reconstruct_backward(a: np.ndarray, b: np.ndarray, dx: np.ndarray):
+    """Gradients of X = (1/R) sum_r a_r (x) b_r given dX [..., h, d_h]:
+    dA[..., h, r] = (1/R) dX[..., h, :] . b[..., r, :] and
+    dB[..., r, :] = (1/R) sum_h a[..., h, r] dX[..., h, :].
+    """
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    R = a.shape[-1]
+    da = np.zeros(a.shape, dtype=np.float64)
+    db = np.zeros(b.shape, dtype=np.float64)
+    for r in range(R):
+        da[..., :, r] = (dx * b[..., None, r, :]).sum(-1) / R
+        db[..., r, :] = (a[..., :, r, None] * dx).sum(-2) / R
+    return da, db
+
+
+def attend_head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray, causal: bool,
+                         dout: np.ndarray):
+    """Gradients of attend_head given dO [Sq, d_h]: returns dq [Sq, d_h], dk, dv [T, d_h].
+
+    Per query row with visible keys n, scores s = k q / sqrt(d_h), p = softmax(s):
+    dv += p (x) dO, dp = v dO, ds = p * (dp - p . dp), dq = ds k / sqrt(d_h),
+    dk += ds (x) q / sqrt(d_h).
+    """
+    d_h = q.shape[-1]
+    rs = 1.0 / math.sqrt(d_h)
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for i in range(q.shape[0]):
+        n = int(q_pos[i]) + 1 if causal else k.shape[0]
+        scores = (k[:n] @ q[i]) * rs
+        e = np.exp(scores - scores.max())
+        p = e / e.sum()
+        dv[:n] += p[:, None] * dout[i][None, :]
+        dp = v[:n] @ dout[i]
+        ds = p * (dp - p @ dp)
+        dq[i] = (ds @ k[:n]) * rs
+        dk[:n] += ds[:, None] * q[i][None, :] * rs
+    return dq, dk, dv
+
+
+def prefill_backward(fq: Dict[str, np.ndarray], cache: Dict[str, np.ndarray], dims: Dims, batch: int, seq: int,
+                     start_pos: int, causal: bool, dout: np.ndarray):
+    """Gradients of sum(prefill(...) * dout) with respect to the query factors
+    (as passed: b_q rotated; KV-only: the rotated Q) and to the cached key/value
+    factors at positions 0..start_pos+seq-1.
+
+    Returns (dfq, dkv): dfq has the keys of fq; dkv has a_k, b_k, a_v, b_v
+    shaped [B, start_pos+seq, ...].
+    """
+    h, dh = dims.n_heads, dims.head_dim
+    T = start_pos + seq
+    Q = queries(fq, dims)
+    dQ = np.zeros((batch, seq, h, dh))
+    dK = np.zeros((batch, T, h, dh))
+    dV = np.zeros((batch, T, h, dh))
+    q_pos = positions(start_pos, seq)
+    dout = np.asarray(dout, np.float64).reshape(batch, seq, h, dh)
+    for b in range(batch):
+        for hh in range(h):
+            k = reconstruct(cache["a_k"][b, :T, hh:hh + 1, :], cache["b_k"][b, :T])[:, 0, :]
+            v = reconstruct(cache["a_v"][b, :T, hh:hh + 1, :], cache["b_v"][b, :T])[:, 0, :]
+            dq, dk, dv = attend_head_backward(Q[b, :, hh, :], k, v, q_pos, causal, dout[b, :, hh, :])
+            dQ[b, :, hh] = dq
+            dK[b, :, hh] = dk
+            dV[b, :, hh] = dv
+    if dims.kv_only:
+        dfq = {"q": dQ}
+    else:
+        da, db = reconstruct_backward(fq["a_q"], fq["b_q"], dQ)
+        dfq = {"a_q": da, "b_q": db}
+    da_k, db_k = reconstruct_backward(cache["a_k"][:batch, :T], cache["b_k"][:batch, :T], dK)
+    da_v, db_v = reconstruct_backward(cache["a_v"][:batch, :T], cache["b_v"][:batch, :T], dV)
+    return dfq, {"a_k": da_k, "b_k": db_k, "a_v": da_v, "b_v": db_v}
+
+
+def rope_backward(g: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Gradient with respect to the unrotated vectors of rope(v, pos, base), given
+    the gradient g of the rotated ones: each pair's rotation is orthogonal, so
+    the gradient is turned back by the same angle, rope(g, -pos)."""
+    return rope(g, -np.asarray(pos, dtype=np.float64), base)
 
 
 def paged_gather(pools: Dict[str, np.ndarray], block_table: np.ndarray, b: int, n: int) -> Dict[str, np.ndarray]:

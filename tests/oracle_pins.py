@@ -17,6 +17,9 @@ What pins what:
   incremental_*        chunked prefill and decode against one long prefill
   paged_*              decode with a key count per sequence over a paged cache,
                        against the brute force run on each sequence's own prefix
+  backward_*           the written-out gradients against central finite
+                       differences of the forward oracle; the inverse rotation
+                       against the adjoint identity
 """
 import math
 
@@ -458,9 +461,68 @@ def paged_permutation_invariance():
     assert np.array_equal(a, b), "paged decode depends on where the pages sit"
 
 
+# --------------------------------------------------------------------------
+# Backward
+# --------------------------------------------------------------------------
+
+def _fd_grad(f, x, eps=1e-6):
+    """Central differences of the scalar f() with respect to every element of x
+    (perturbed in place and restored)."""
+    g = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        old = x[idx]
+        x[idx] = old + eps
+        fp = f()
+        x[idx] = old - eps
+        fm = f()
+        x[idx] = old
+        g[idx] = (fp - fm) / (2 * eps)
+    return g
+
+
+BACKWARD_CASES = [
+    # h, d_h, R_Q, R_K, R_V, base, B, S, start_pos, causal
+    (2, 4, 2, 2, 3, 10000.0, 2, 3, 2, True),     # chunked: earlier keys get gradients too
+    (3, 2, 0, 1, 2, 5.0, 1, 4, 0, False),        # KV-only, every key visible
+    (2, 6, 3, 3, 1, 100.0, 1, 3, 0, True),
+]
+
+
+def backward_finite_differences():
+    for ci, (h, d, rq, rk, rv, base, B, S, sp, causal) in enumerate(BACKWARD_CASES):
+        rng = np.random.default_rng(500 + ci)
+        dims = O.Dims(8, h, d, rq, rk, rv, base)
+        T = sp + S
+        fq = {"q": rng.normal(0, 0.8, (B, S, h, d))} if dims.kv_only else \
+            {"a_q": rng.normal(0, 0.8, (B, S, h, rq)), "b_q": rng.normal(0, 0.8, (B, S, rq, d))}
+        cache = O.cache_new(dims, B, T)
+        for k, shape in (("a_k", (h, rk)), ("b_k", (rk, d)), ("a_v", (h, rv)), ("b_v", (rv, d))):
+            cache[k][:] = rng.normal(0, 0.8, (B, T) + shape)
+        dout = rng.normal(0, 1, (B, S, h * d))
+        loss = lambda: float(np.sum(O.prefill(fq, cache, dims, B, S, sp, causal) * dout))
+        dfq, dkv = O.prefill_backward(fq, cache, dims, B, S, sp, causal, dout)
+        for k in fq:
+            _close(dfq[k], _fd_grad(loss, fq[k]), tol=1e-6, what=f"backward case {ci} d{k}")
+        for k in ("a_k", "b_k", "a_v", "b_v"):
+            _close(dkv[k], _fd_grad(loss, cache[k]), tol=1e-6, what=f"backward case {ci} d{k}")
+
+
+def backward_rope_adjoint():
+    """<rope(v), g> = <v, rope_backward(g)> at positions up to 131,072."""
+    rng = np.random.default_rng(600)
+    for d, base in ((8, 10000.0), (64, 500000.0)):
+        pos = np.array([0, 3, 4095, 131071])
+        v = rng.normal(0, 1, (2, 4, 3, d))
+        g = rng.normal(0, 1, (2, 4, 3, d))
+        lhs = np.sum(O.rope(v, pos, base) * g)
+        rhs = np.sum(v * O.rope_backward(g, pos, base))
+        _close(lhs, rhs, tol=1e-12, what=f"rope adjoint d={d}")
+
+
 ALL_PINS = [
     brute_force_causal, brute_force_noncausal, textbook_mha, textbook_mqa, textbook_gqa,
     rope_identities, rope_textbook, commute_rope_factor_sum, commute_code_order_attention,
     softmax_rows, closed_form_two_tokens, closed_form_special_cases, incremental_decode,
     incremental_chunked_prefill, paged_ragged_brute_force, paged_permutation_invariance,
+    backward_finite_differences, backward_rope_adjoint,
 ]

@@ -23,7 +23,8 @@ def test_pin(pin):
 
 _orig = {name: getattr(O, name) for name in
          ("rope", "rope_angles", "reconstruct", "project", "attend_head", "cache_append", "rotate_factors",
-          "prefill", "positions", "paged_gather", "decode_paged")}
+          "prefill", "positions", "paged_gather", "decode_paged", "attend_head_backward",
+          "reconstruct_backward", "rope_backward")}
 
 
 def _rope_sign(v, pos, base):
@@ -137,6 +138,32 @@ def _decode_paged_max_len(fq, pools, block_table, ctx_lens, dims):
     return _orig["decode_paged"](fq, pools, block_table, [m if int(v) else 0 for v in ctx_lens], dims)
 
 
+def _attend_backward_no_d(q, k, v, q_pos, causal, dout):
+    """dS = P dP (the softmax Jacobian's -p (p . dp) term dropped)."""
+    d_h = q.shape[-1]
+    rs = 1.0 / math.sqrt(d_h)
+    dq, dk, dv = (np.zeros(x.shape) for x in (q, k, v))
+    for i in range(q.shape[0]):
+        n = int(q_pos[i]) + 1 if causal else k.shape[0]
+        sc = (k[:n] @ q[i]) * rs
+        p = np.exp(sc - sc.max())
+        p /= p.sum()
+        dv[:n] += p[:, None] * dout[i][None, :]
+        ds = p * (v[:n] @ dout[i])
+        dq[i] = (ds @ k[:n]) * rs
+        dk[:n] += ds[:, None] * q[i][None, :] * rs
+    return dq, dk, dv
+
+
+def _reconstruct_backward_no_scale(a, b, dx):
+    da, db = _orig["reconstruct_backward"](a, b, dx)
+    return da, db * a.shape[-1]
+
+
+def _rope_backward_forward_turn(g, pos, base):
+    return O.rope(g, pos, base)
+
+
 MUTATIONS = {
     "rope rotates the wrong way": ("rope", _rope_sign),
     "rope pairs (i, i+d/2)": ("rope", _rope_half_split),
@@ -153,6 +180,9 @@ MUTATIONS = {
     "paged rows shifted within a page": ("paged_gather", _gather_next_row),
     "every sequence read through the first table row": ("paged_gather", _gather_first_table_row),
     "ragged lengths ignored": ("decode_paged", _decode_paged_max_len),
+    "backward drops the softmax row term": ("attend_head_backward", _attend_backward_no_d),
+    "dim-factor gradient without 1/R": ("reconstruct_backward", _reconstruct_backward_no_scale),
+    "rope gradient turned the forward way": ("rope_backward", _rope_backward_forward_turn),
 }
 
 
