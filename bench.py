@@ -272,6 +272,46 @@ def run_prefill(reps: int = 5):
     }
 
 
+def run_prefill_backward(reps: int = 3):
+    """Backward of the prefill attention at prefill_b4_s4k: gradients of all six
+    factor tensors from a seeded dO.  Algorithmic work: the usual 2.5x the
+    forward's matrix-product flops (dV, dP, dQ, dK and the score recomputation)."""
+    wl = I.WORKLOADS["prefill_b4_s4k"]
+    d = dims_of(wl)
+    B, S = wl.batch, wl.seq
+    h, dh = d.n_heads, d.head_dim
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1004)
+    x = torch.randn(B, S, d.d_model, generator=g, device="cuda").to(torch.bfloat16)
+    w = I.weights(wl.shape, seed=1004, dtype="bf16")
+    wp = T.pack_weights({k: v.cuda() for k, v in w.items()}, d.kv_only)
+    cache = T.new_cache(d, B, S)
+    f = T.new_factors(d, B, S)
+    T.tpa_factor_proj(d, x, wp, f, start_pos=0)
+    T.tpa_cache_append(d, cache, f, 0)
+    out = T.tpa_prefill_attn(d, f, cache, 0, True)
+    dout = torch.randn(B, S, h * dh, generator=g, device="cuda").to(torch.bfloat16)
+    f32 = lambda *s: torch.zeros(*s, dtype=torch.float32, device="cuda")
+    dq = T.Factors(f32(B, S, h, d.rank_q), f32(B, S, d.rank_q, dh), None, None, None, None)
+    dkv = T.Cache(f32(B, S, h, d.rank_k), f32(B, S, d.rank_k, dh), f32(B, S, h, d.rank_v), f32(B, S, d.rank_v, dh))
+    ws = torch.empty(T.tpa_prefill_backward_workspace_bytes(d, B, S, 0), dtype=torch.uint8, device="cuda")
+    T.tpa_prefill_attn_backward(d, f, cache, 0, True, out, dout, dq, dkv, ws)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        T.tpa_prefill_attn_backward(d, f, cache, 0, True, out, dout, dq, dkv, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    flop = 2.5 * 4.0 * B * h * dh * S * (S + 1) / 2
+    return {"workload": wl.name, "ms": round(ms, 3), "tflops": round(flop / ms / 1e9, 2),
+            "frac_bf16_peak": round(flop / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+            "kernels": "general (vector ALU, fp32 arithmetic)"}
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on a bounded sample of the decode step
 # ---------------------------------------------------------------------------
@@ -369,6 +409,8 @@ def main():
     if not args.no_prefill:
         log("[bench] prefill workload")
         result["prefill"] = run_prefill()
+        log("[bench] prefill backward")
+        result["prefill_backward"] = run_prefill_backward()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(wl)

@@ -146,4 +146,27 @@ hipError_t launch_decode(int dtype, const AttnArgs& a, int64_t ctx_len, const De
 
 hipError_t launch_prefill(int dtype, const AttnArgs& a, hipStream_t st);
 
+// ---- prefill backward --------------------------------------------------------
+// AttnArgs as for the forward (a.out is the forward output, read); gradients
+// are float32.
+struct BwdArgs {
+  const void* dout;      // [B, S, h*d_h], the call's element type
+  float* lse;            // [B, S, h]  base-2 log-sum-exp of each query's scores
+  float* dvec;           // [B, S, h]  sum_d dO * O
+  float* dq;             // [B, S, h, d_h]       dQ  (workspace)
+  float* dk;             // [B, n_keys, h, d_h]  dK  (workspace)
+  float* dv;             // [B, n_keys, h, d_h]  dV  (workspace)
+  float* d_aq;           // [B, *, h, R_Q]   (unused for KV-only)
+  float* d_bq;           // [B, *, R_Q, d_h] (KV-only: dQ [B, *, h, d_h])
+  int64_t dq_bstride;    // tokens between sequences of d_aq / d_bq
+  float* d_ak;           // cache layout, capacity dkv_max_seq tokens per sequence
+  float* d_bk;
+  float* d_av;
+  float* d_bv;
+  int64_t dkv_max_seq;
+};
+size_t prefill_backward_workspace_bytes(const AttnArgs& a);
+void prefill_backward_carve(const AttnArgs& a, void* ws, BwdArgs& g);
+hipError_t launch_prefill_backward(int dtype, const AttnArgs& a, const BwdArgs& g, hipStream_t st);
+
 }  // namespace tpa

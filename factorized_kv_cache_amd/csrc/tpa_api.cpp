@@ -345,6 +345,84 @@ tpa_status tpa_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_ca
                     "tpa_decode_attn");
 }
 
+size_t tpa_prefill_backward_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t seq_len,
+                                            int64_t start_pos) {
+  if (check_dims(d) != TPA_OK || n_batch < 1 || seq_len < 1 || start_pos < 0) return 0;
+  tpa_factors q;
+  memset(&q, 0, sizeof(q));
+  tpa_cache c;
+  memset(&c, 0, sizeof(c));
+  c.max_seq = start_pos + seq_len;
+  tpa::AttnArgs a = attn_args(d, &q, seq_len, &c, n_batch, seq_len, start_pos, 1, nullptr);
+  return tpa::prefill_backward_workspace_bytes(a);
+}
+
+tpa_status tpa_prefill_attn_backward(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
+                                     int64_t seq_len, int64_t start_pos, int32_t causal, const void* out,
+                                     const void* dout, const tpa_factors* dq, const tpa_cache* dkv, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+  tpa_status st = check_dims(d);
+  if (st != TPA_OK) return st;
+  if ((st = check_query(d, q)) != TPA_OK) return st;
+  if ((st = check_cache(c)) != TPA_OK) return st;
+  if (!out || !dout) return fail(TPA_ERR_INVALID_ARGUMENT, "out or dout is NULL");
+  if (!dq || !dq->b_q || (d->rank_q > 0 && !dq->a_q))
+    return fail(TPA_ERR_INVALID_ARGUMENT, "a query-factor gradient tensor is NULL");
+  if ((st = check_cache(dkv)) != TPA_OK) return st;
+  if (n_batch < 1 || seq_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and seq_len must be >= 1");
+  if (n_batch > 65535) return fail(TPA_ERR_UNSUPPORTED, "n_batch must be <= 65535");
+  if (start_pos < 0) return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos must be >= 0");
+  if (n_batch > c->max_batch || n_batch > dkv->max_batch)
+    return fail(TPA_ERR_CAPACITY, "n_batch %lld exceeds max_batch", (long long)n_batch);
+  if (seq_len > c->max_seq || start_pos > c->max_seq - seq_len || start_pos + seq_len > dkv->max_seq)
+    return fail(TPA_ERR_CAPACITY, "start_pos + seq_len (%lld) exceeds max_seq", (long long)(start_pos + seq_len));
+  if ((start_pos + seq_len) + seq_len >= kMaxTokens) return fail(TPA_ERR_UNSUPPORTED, "sequence too long");
+  int64_t qs, dqs;
+  if ((st = resolve_stride(q->q_batch_stride, seq_len, "q_batch_stride", &qs)) != TPA_OK) return st;
+  if ((st = resolve_stride(dq->q_batch_stride, seq_len, "dq->q_batch_stride", &dqs)) != TPA_OK) return st;
+  tpa::AttnArgs a = attn_args(d, q, qs, c, n_batch, seq_len, start_pos, causal, const_cast<void*>(out));
+  const size_t need = tpa::prefill_backward_workspace_bytes(a);
+  if (!workspace || ws_bytes < need)
+    return fail(TPA_ERR_WORKSPACE, "backward workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
+                workspace ? "" : ", NULL");
+  tpa::BwdArgs g;
+  memset(&g, 0, sizeof(g));
+  tpa::prefill_backward_carve(a, workspace, g);
+  g.dout = dout;
+  g.d_aq = static_cast<float*>(dq->a_q);
+  g.d_bq = static_cast<float*>(dq->b_q);
+  g.dq_bstride = dqs;
+  g.d_ak = static_cast<float*>(dkv->a_k);
+  g.d_bk = static_cast<float*>(dkv->b_k);
+  g.d_av = static_cast<float*>(dkv->a_v);
+  g.d_bv = static_cast<float*>(dkv->b_v);
+  g.dkv_max_seq = dkv->max_seq;
+  return hip_status(tpa::launch_prefill_backward(d->dtype, a, g, (hipStream_t)stream), "tpa_prefill_attn_backward");
+}
+
+tpa_status tpa_rope_b_backward(const tpa_dims* d, float* g, int64_t n_batch, int64_t seq_len, int32_t rows,
+                               int64_t start_pos, void* stream) {
+  tpa_status st = check_dims(d);
+  if (st != TPA_OK) return st;
+  if (!g) return fail(TPA_ERR_INVALID_ARGUMENT, "g is NULL");
+  if (n_batch < 1 || seq_len < 1 || rows < 1)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch, seq_len and rows must be >= 1");
+  if (n_batch * seq_len >= kMaxTokens) return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
+  if (start_pos < 0 || start_pos + seq_len >= kMaxTokens)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos must be in 0 .. 2^31 - seq_len");
+  tpa::RopeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.b = g;
+  a.n_tok = n_batch * seq_len;
+  a.S = seq_len;
+  a.start_pos = start_pos;
+  a.rows = rows;
+  a.head_dim = d->head_dim;
+  a.rope = rope_table(d);
+  for (int i = 0; i < d->head_dim / 2; ++i) a.rope.rev[i] = -a.rope.rev[i];   // turn back
+  return hip_status(tpa::launch_rope(tpa::kF32, a, (hipStream_t)stream), "tpa_rope_b_backward");
+}
+
 tpa_status tpa_paged_cache_append(const tpa_dims* d, const tpa_paged_cache* c, const tpa_factors* kv,
                                   int64_t n_batch, int64_t seq_len, const int32_t* start_pos, void* stream) {
   tpa_status st = check_dims(d);

@@ -67,6 +67,11 @@ def _load():
         "tpa_decode_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64]),
         "tpa_decode_attn": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_cache), i64, i64, vp, vp,
                                            ctypes.c_size_t, vp]),
+        "tpa_prefill_backward_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64, i64]),
+        "tpa_prefill_attn_backward": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_cache), i64, i64, i64, i32,
+                                                     vp, vp, P(tpa_factors), P(tpa_cache), vp, ctypes.c_size_t,
+                                                     vp]),
+        "tpa_rope_b_backward": (ctypes.c_int, [P(tpa_dims), vp, i64, i64, i32, i64, vp]),
         "tpa_paged_cache_append": (ctypes.c_int, [P(tpa_dims), P(tpa_paged_cache), P(tpa_factors), i64, i64, vp,
                                                   vp]),
         "tpa_paged_decode_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64]),
@@ -85,6 +90,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("tpa_packed_weight_rows", "tpa_cache_elems_per_token", "tpa_factor_proj", "tpa_rope_b",
             "tpa_cache_append", "tpa_prefill_attn", "tpa_decode_workspace_bytes", "tpa_decode_attn",
+            "tpa_prefill_backward_workspace_bytes", "tpa_prefill_attn_backward", "tpa_rope_b_backward",
             "tpa_paged_cache_append", "tpa_paged_decode_workspace_bytes", "tpa_paged_decode_attn",
             "tpa_status_string", "tpa_last_error")
 
@@ -341,3 +347,25 @@ def tpa_paged_decode_attn(dims: Dims, q: Factors, cache: PagedCache, ctx_lens: t
                                       _ptr(ctx_lens), max_ctx_len, _ptr(out), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def tpa_prefill_backward_workspace_bytes(dims: Dims, batch: int, seq: int, start_pos: int) -> int:
+    return int(_lib.tpa_prefill_backward_workspace_bytes(ctypes.byref(dims.c()), batch, seq, start_pos))
+
+
+def tpa_prefill_attn_backward(dims: Dims, q: Factors, cache: Cache, start_pos: int, causal: bool, out: torch.Tensor,
+                              dout: torch.Tensor, dq: Factors, dkv: Cache, workspace: torch.Tensor, stream=None):
+    """Gradients into dq (a_q, b_q; KV-only b_q = dQ) and dkv (cache layout), all float32."""
+    B, S = q.b_q.shape[0], q.b_q.shape[1]
+    _check(_lib.tpa_prefill_attn_backward(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B,
+                                          S, start_pos, 1 if causal else 0, _ptr(out), _ptr(dout),
+                                          ctypes.byref(dq.c()), ctypes.byref(dkv.c()), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def tpa_rope_b_backward(dims: Dims, g: torch.Tensor, start_pos: int = 0, stream=None) -> torch.Tensor:
+    """In place on g [B, S, rows, d_h], float32."""
+    assert g.dtype == torch.float32
+    B, S, rows = g.shape[0], g.shape[1], g.shape[2]
+    _check(_lib.tpa_rope_b_backward(ctypes.byref(dims.c()), _ptr(g), B, S, rows, start_pos, _stream(stream)))
+    return g

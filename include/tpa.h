@@ -196,6 +196,48 @@ tpa_status tpa_decode_attn(const tpa_dims* dims, const tpa_factors* q, const tpa
                            void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Backward (training; the pages train TPA models, the arithmetic is the chain
+ * rule through tpa_prefill_attn and tpa_rope_b).  Gradients are float32
+ * whatever dims->dtype is.  The projection's own gradients are plain matrix
+ * products of the packed factor gradient dF [B*S, n_out]: dX = dF w_packed and
+ * dW = dF^T x; the library does not provide them.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of device workspace tpa_prefill_attn_backward needs: float32 dQ, dK,
+ * dV and two per-query statistics, (B*h*d_h*(S + 2*(start_pos+S)) + 2*B*S*h)*4. */
+size_t tpa_prefill_backward_workspace_bytes(const tpa_dims* dims, int64_t n_batch, int64_t seq_len,
+                                            int64_t start_pos);
+
+/* Gradients of the prefill attention: given the forward's inputs (q, cache,
+ * start_pos, causal), its output `out` [B,S,h*d_h] and the upstream gradient
+ * dout (same layout and element type), writes
+ *   dq->a_q [B,S,h,R_Q], dq->b_q [B,S,R_Q,d_h]  (KV-only: dq->b_q = dQ [B,S,h,d_h]),
+ *     gradients of the query factors as passed (b_q rotated), float32,
+ *     dq->q_batch_stride applies (0 = S);
+ *   dkv->a_k .. b_v, float32 tensors in the cache layout: positions
+ *     0 .. start_pos+S-1 of each sequence are overwritten with the gradients of
+ *     the cached factors there (b_k rotated); other positions are untouched.
+ * With P the softmax rows and s = q.k/sqrt(d_h): dV = P^T dO, dS = P*(dO V^T -
+ * rowsum(dO*O)), dQ = dS K/sqrt(d_h), dK = dS^T Q/sqrt(d_h), then
+ * dA[t,h,r] = (1/R) dX[t,h,:].B[t,r,:] and dB[t,r,:] = (1/R) sum_h A[t,h,r] dX[t,h,:].
+ * Deterministic: repeated calls give the same bits.
+ *   Passage: the Q_t/K_t/V_t equations and the attention of the code
+ *   walk-through (前向传播), differentiated.
+ * Errors: as tpa_prefill_attn; null gradient tensors; dkv smaller than the
+ * key range (TPA_ERR_CAPACITY); workspace too small (TPA_ERR_WORKSPACE). */
+tpa_status tpa_prefill_attn_backward(const tpa_dims* dims, const tpa_factors* q, const tpa_cache* cache,
+                                     int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal,
+                                     const void* out, const void* dout, const tpa_factors* dq,
+                                     const tpa_cache* dkv, void* workspace, size_t ws_bytes, void* stream);
+
+/* Gradient through the rotary embedding: in place on g [B,S,rows,d_h]
+ * (float32), turns each pair back by the angle tpa_rope_b turned it forward
+ * (the rotation is orthogonal), giving the gradient of the unrotated factor.
+ * Errors: as tpa_rope_b. */
+tpa_status tpa_rope_b_backward(const tpa_dims* dims, float* g, int64_t n_batch, int64_t seq_len, int32_t rows,
+                               int64_t start_pos, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Paged factor cache (serving layout: the pages do not describe one; the
  * arithmetic is that of tpa_cache_append and tpa_decode_attn).
  *
