@@ -46,22 +46,26 @@ __device__ __forceinline__ float bwd_query(const AttnArgs& a, int64_t b, int64_t
   return v * a.q_scale;
 }
 
-// ---- pass 1: log-sum-exp (base 2) and D = dO . O per (sequence, query, head)
+// ---- pass 1: log-sum-exp (base 2) and D = dO . O per (sequence, query, head),
+// O recomputed in fp32 (online softmax over the key blocks)
 template <typename T, int BM, int BN>
 __global__ void __launch_bounds__(kBwdThreads) bwd_stats_kernel(AttnArgs a, BwdArgs g) {
   extern __shared__ float smem[];
   const int h = a.h, dh = a.d_h;
-  float* qs = smem;              // [BM][d_h]
+  float* qs = smem;              // [BM][d_h]  q^, at the end O * dO
   float* ks = qs + BM * dh;      // [BN][d_h]
-  float* ss = ks + BN * dh;      // [BM][BN]
+  float* vs = ks + BN * dh;      // [BN][d_h]
+  float* ss = vs + BN * dh;      // [BM][BN]   scores, then p
   float* mrow = ss + BM * BN;    // [BM]
   float* lrow = mrow + BM;       // [BM]
+  float* arow = lrow + BM;       // [BM]  rescale of the running sums
   const int64_t q0 = (int64_t)blockIdx.x * BM;
   const int hh = blockIdx.y;
   const int64_t b = blockIdx.z;
   const T* AK = reinterpret_cast<const T*>(a.c_ak);
   const T* BK = reinterpret_cast<const T*>(a.c_bk);
-  const T* O = reinterpret_cast<const T*>(a.out);
+  const T* AV = reinterpret_cast<const T*>(a.c_av);
+  const T* BV = reinterpret_cast<const T*>(a.c_bv);
   const T* dO = reinterpret_cast<const T*>(g.dout);
   const int64_t seq0 = b * a.max_seq;
 
@@ -74,24 +78,28 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_stats_kernel(AttnArgs a, BwdA
     mrow[i] = -INFINITY;
     lrow[i] = 0.f;
   }
-  // D_i, one wave-strided sum per query (fixed order)
-  for (int i = threadIdx.x; i < BM; i += blockDim.x) {
-    const int64_t s = q0 + i;
-    if (s >= a.S) continue;
-    const int64_t base = ((b * a.S + s) * h + hh) * (int64_t)dh;
-    float acc = 0.f;
-    for (int d = 0; d < dh; ++d) acc = fmaf(ldf(dO, base + d), ldf(O, base + d), acc);
-    g.dvec[(b * a.S + s) * h + hh] = acc;
+  // this thread's O outputs jo: query oi[jo], element od[jo] (n_out of them)
+  float acc[kBwdOut];
+  int oi[kBwdOut], od[kBwdOut];
+  const int n_out = (BM * dh - (int)threadIdx.x + kBwdThreads - 1) / kBwdThreads;
+#pragma unroll
+  for (int jo = 0; jo < kBwdOut; ++jo) {
+    const int idx = threadIdx.x + jo * kBwdThreads;
+    oi[jo] = idx / dh;
+    od[jo] = idx - oi[jo] * dh;
+    acc[jo] = 0.f;
   }
-  __syncthreads();
 
   const int64_t last_q = (q0 + BM < a.S ? q0 + BM : a.S) - 1;
   const int64_t kend = a.causal ? a.start_pos + last_q + 1 : a.start_pos + a.S;
   for (int64_t k0 = 0; k0 < kend; k0 += BN) {
+    __syncthreads();
     for (int idx = threadIdx.x; idx < BN * dh; idx += blockDim.x) {
       const int j = idx / dh, d = idx - j * dh;
       const int64_t t = k0 + j;
-      ks[idx] = t < kend ? bwd_rebuild(AK, BK, seq0 + t, hh, h, a.rk, dh, d) : 0.f;
+      const bool ok = t < kend;
+      ks[idx] = ok ? bwd_rebuild(AK, BK, seq0 + t, hh, h, a.rk, dh, d) : 0.f;
+      vs[idx] = ok ? bwd_rebuild(AV, BV, seq0 + t, hh, h, a.rv, dh, d) : 0.f;
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < BM * BN; idx += blockDim.x) {
@@ -111,16 +119,49 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_stats_kernel(AttnArgs a, BwdA
       for (int j = 0; j < BN; ++j) mx = fmaxf(mx, ss[i * BN + j]);
       if (mx != -INFINITY) {
         float sum = 0.f;
-        for (int j = 0; j < BN; ++j) sum += fast_exp2(ss[i * BN + j] - mx);
-        lrow[i] = lrow[i] * fast_exp2(mrow[i] - mx) + sum;
+        for (int j = 0; j < BN; ++j) {
+          const float p = fast_exp2(ss[i * BN + j] - mx);
+          ss[i * BN + j] = p;
+          sum += p;
+        }
+        const float alpha = fast_exp2(mrow[i] - mx);   // 0 while nothing was seen
+        lrow[i] = lrow[i] * alpha + sum;
         mrow[i] = mx;
+        arow[i] = alpha;
+      } else {
+        for (int j = 0; j < BN; ++j) ss[i * BN + j] = 0.f;
+        arow[i] = 1.f;
       }
     }
     __syncthreads();
+#pragma unroll 1
+    for (int j = 0; j < BN; ++j) {
+#pragma unroll
+      for (int jo = 0; jo < kBwdOut; ++jo) {
+        if (jo >= n_out) break;
+        const float a0 = j == 0 ? arow[oi[jo]] : 1.f;
+        acc[jo] = fmaf(ss[oi[jo] * BN + j], vs[j * dh + od[jo]], acc[jo] * a0);
+      }
+    }
   }
+  __syncthreads();
+  // O = acc / l / R_V; each row's dO . O summed in a fixed order
+  const float inv_rv = 1.f / (float)a.rv;
+#pragma unroll
+  for (int jo = 0; jo < kBwdOut; ++jo) {
+    if (jo >= n_out) break;
+    const int64_t s = q0 + oi[jo];
+    const float o = acc[jo] / lrow[oi[jo]] * inv_rv;
+    qs[oi[jo] * dh + od[jo]] = s < a.S ? o * ldf(dO, ((b * a.S + s) * h + hh) * (int64_t)dh + od[jo]) : 0.f;
+  }
+  __syncthreads();
   for (int i = threadIdx.x; i < BM; i += blockDim.x) {
     const int64_t s = q0 + i;
-    if (s < a.S) g.lse[(b * a.S + s) * h + hh] = mrow[i] + __log2f(lrow[i]);
+    if (s >= a.S) continue;
+    float dsum = 0.f;
+    for (int d = 0; d < dh; ++d) dsum += qs[i * dh + d];
+    g.lse[(b * a.S + s) * h + hh] = mrow[i] + __log2f(lrow[i]);
+    g.dvec[(b * a.S + s) * h + hh] = dsum;
   }
 }
 
@@ -384,7 +425,7 @@ template <typename T, int BM, int BN>
 static hipError_t launch_bwd_t(const AttnArgs& a, const BwdArgs& g, hipStream_t st) {
   const int dh = a.d_h;
   const int64_t n_keys = a.start_pos + a.S;
-  const size_t lds1 = sizeof(float) * ((size_t)(BM + BN) * dh + (size_t)BM * BN + 2 * BM);
+  const size_t lds1 = sizeof(float) * ((size_t)(BM + 2 * BN) * dh + (size_t)BM * BN + 3 * BM);
   const size_t lds2 = sizeof(float) * ((size_t)(2 * BN + 2 * BM) * dh + 2 * (size_t)BM * BN + 2 * BM);
   const size_t lds3 = sizeof(float) * ((size_t)(2 * BM + 2 * BN) * dh + (size_t)BM * BN + 2 * BM);
   const dim3 gq((unsigned)((a.S + BM - 1) / BM), (unsigned)a.h, (unsigned)a.n_batch);
@@ -399,26 +440,51 @@ static hipError_t launch_bwd_t(const AttnArgs& a, const BwdArgs& g, hipStream_t 
 
 size_t prefill_backward_workspace_bytes(const AttnArgs& a) {
   const int64_t n_keys = a.start_pos + a.S;
-  const size_t per = (size_t)a.n_batch * a.h * a.d_h * sizeof(float);
-  return per * (size_t)(a.S + 2 * n_keys) + 2 * (size_t)a.n_batch * a.S * a.h * sizeof(float);
+  const size_t per = (size_t)a.n_batch * a.h * a.d_h;
+  // dQ, dK, dV in float32; q^ (hi, lo), k^ (hi, lo), v^ in bf16; lse and D
+  return per * (size_t)(a.S + 2 * n_keys) * sizeof(float) + per * (size_t)(2 * a.S + 3 * n_keys) * sizeof(bf16_t) +
+         2 * (size_t)a.n_batch * a.S * a.h * sizeof(float);
 }
 
 void prefill_backward_carve(const AttnArgs& a, void* ws, BwdArgs& g) {
   const int64_t n_keys = a.start_pos + a.S;
-  float* p = reinterpret_cast<float*>(ws);
   const int64_t per = a.n_batch * a.h * (int64_t)a.d_h;
+  float* p = reinterpret_cast<float*>(ws);
   g.dq = p;
   p += per * a.S;
   g.dk = p;
   p += per * n_keys;
   g.dv = p;
   p += per * n_keys;
+  bf16_t* q = reinterpret_cast<bf16_t*>(p);
+  g.q_hi = q;
+  q += per * a.S;
+  g.q_lo = q;
+  q += per * a.S;
+  g.k_hi = q;
+  q += per * n_keys;
+  g.k_lo = q;
+  q += per * n_keys;
+  g.v_hat = q;
+  q += per * n_keys;
+  p = reinterpret_cast<float*>(q);
   g.lse = p;
   p += a.n_batch * a.S * a.h;
   g.dvec = p;
 }
 
+bool backward_mfma_supported(int dtype, const AttnArgs& a, const BwdArgs& g);
+hipError_t launch_backward_mfma(const AttnArgs& a, const BwdArgs& g, hipStream_t st);
+
 hipError_t launch_prefill_backward(int dtype, const AttnArgs& a, const BwdArgs& g, hipStream_t st) {
+  if (backward_mfma_supported(dtype, a, g)) {
+    const hipError_t e = launch_backward_mfma(a, g, st);
+    if (e != hipSuccess) return e;
+    const int64_t n_keys = a.start_pos + a.S;
+    hipLaunchKernelGGL((bwd_factor_kernel<bf16_t>), dim3((unsigned)(a.S + n_keys), (unsigned)a.n_batch),
+                       dim3(kBwdThreads), 0, st, a, g);
+    return hipGetLastError();
+  }
   if (a.d_h <= 128) {
     return dtype == kF32 ? launch_bwd_t<float, 32, 32>(a, g, st) : launch_bwd_t<bf16_t, 32, 32>(a, g, st);
   }

@@ -147,15 +147,19 @@ hipError_t launch_decode(int dtype, const AttnArgs& a, int64_t ctx_len, const De
 hipError_t launch_prefill(int dtype, const AttnArgs& a, hipStream_t st);
 
 // ---- prefill backward --------------------------------------------------------
-// AttnArgs as for the forward (a.out is the forward output, read); gradients
-// are float32.
+// AttnArgs as for the forward (a.out unused); gradients are float32.
 struct BwdArgs {
   const void* dout;      // [B, S, h*d_h], the call's element type
   float* lse;            // [B, S, h]  base-2 log-sum-exp of each query's scores
-  float* dvec;           // [B, S, h]  sum_d dO * O
+  float* dvec;           // [B, S, h]  D = sum_d dO * O, O recomputed in fp32
   float* dq;             // [B, S, h, d_h]       dQ  (workspace)
   float* dk;             // [B, n_keys, h, d_h]  dK  (workspace)
   float* dv;             // [B, n_keys, h, d_h]  dV  (workspace)
+  bf16_t* q_hi;          // [B, S, h, d_h]       scaled q^ as bf16 hi + lo (workspace, matrix-core path)
+  bf16_t* q_lo;
+  bf16_t* k_hi;          // [B, n_keys, h, d_h]  k^ as bf16 hi + lo (workspace, matrix-core path)
+  bf16_t* k_lo;
+  bf16_t* v_hat;         // [B, n_keys, h, d_h]  v^ (workspace, matrix-core path)
   float* d_aq;           // [B, *, h, R_Q]   (unused for KV-only)
   float* d_bq;           // [B, *, R_Q, d_h] (KV-only: dQ [B, *, h, d_h])
   int64_t dq_bstride;    // tokens between sequences of d_aq / d_bq

@@ -358,14 +358,14 @@ size_t tpa_prefill_backward_workspace_bytes(const tpa_dims* d, int64_t n_batch, 
 }
 
 tpa_status tpa_prefill_attn_backward(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
-                                     int64_t seq_len, int64_t start_pos, int32_t causal, const void* out,
-                                     const void* dout, const tpa_factors* dq, const tpa_cache* dkv, void* workspace,
-                                     size_t ws_bytes, void* stream) {
+                                     int64_t seq_len, int64_t start_pos, int32_t causal, const void* dout,
+                                     const tpa_factors* dq, const tpa_cache* dkv, void* workspace, size_t ws_bytes,
+                                     void* stream) {
   tpa_status st = check_dims(d);
   if (st != TPA_OK) return st;
   if ((st = check_query(d, q)) != TPA_OK) return st;
   if ((st = check_cache(c)) != TPA_OK) return st;
-  if (!out || !dout) return fail(TPA_ERR_INVALID_ARGUMENT, "out or dout is NULL");
+  if (!dout) return fail(TPA_ERR_INVALID_ARGUMENT, "dout is NULL");
   if (!dq || !dq->b_q || (d->rank_q > 0 && !dq->a_q))
     return fail(TPA_ERR_INVALID_ARGUMENT, "a query-factor gradient tensor is NULL");
   if ((st = check_cache(dkv)) != TPA_OK) return st;
@@ -380,7 +380,7 @@ tpa_status tpa_prefill_attn_backward(const tpa_dims* d, const tpa_factors* q, co
   int64_t qs, dqs;
   if ((st = resolve_stride(q->q_batch_stride, seq_len, "q_batch_stride", &qs)) != TPA_OK) return st;
   if ((st = resolve_stride(dq->q_batch_stride, seq_len, "dq->q_batch_stride", &dqs)) != TPA_OK) return st;
-  tpa::AttnArgs a = attn_args(d, q, qs, c, n_batch, seq_len, start_pos, causal, const_cast<void*>(out));
+  tpa::AttnArgs a = attn_args(d, q, qs, c, n_batch, seq_len, start_pos, causal, nullptr);
   const size_t need = tpa::prefill_backward_workspace_bytes(a);
   if (!workspace || ws_bytes < need)
     return fail(TPA_ERR_WORKSPACE, "backward workspace needs %zu bytes (got %zu%s)", need, ws_bytes,

@@ -69,8 +69,7 @@ def _load():
                                            ctypes.c_size_t, vp]),
         "tpa_prefill_backward_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64, i64]),
         "tpa_prefill_attn_backward": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_cache), i64, i64, i64, i32,
-                                                     vp, vp, P(tpa_factors), P(tpa_cache), vp, ctypes.c_size_t,
-                                                     vp]),
+                                                     vp, P(tpa_factors), P(tpa_cache), vp, ctypes.c_size_t, vp]),
         "tpa_rope_b_backward": (ctypes.c_int, [P(tpa_dims), vp, i64, i64, i32, i64, vp]),
         "tpa_paged_cache_append": (ctypes.c_int, [P(tpa_dims), P(tpa_paged_cache), P(tpa_factors), i64, i64, vp,
                                                   vp]),
@@ -353,12 +352,12 @@ def tpa_prefill_backward_workspace_bytes(dims: Dims, batch: int, seq: int, start
     return int(_lib.tpa_prefill_backward_workspace_bytes(ctypes.byref(dims.c()), batch, seq, start_pos))
 
 
-def tpa_prefill_attn_backward(dims: Dims, q: Factors, cache: Cache, start_pos: int, causal: bool, out: torch.Tensor,
+def tpa_prefill_attn_backward(dims: Dims, q: Factors, cache: Cache, start_pos: int, causal: bool,
                               dout: torch.Tensor, dq: Factors, dkv: Cache, workspace: torch.Tensor, stream=None):
     """Gradients into dq (a_q, b_q; KV-only b_q = dQ) and dkv (cache layout), all float32."""
     B, S = q.b_q.shape[0], q.b_q.shape[1]
     _check(_lib.tpa_prefill_attn_backward(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B,
-                                          S, start_pos, 1 if causal else 0, _ptr(out), _ptr(dout),
+                                          S, start_pos, 1 if causal else 0, _ptr(dout),
                                           ctypes.byref(dq.c()), ctypes.byref(dkv.c()), _ptr(workspace),
                                           workspace.numel() * workspace.element_size(), _stream(stream)))
 

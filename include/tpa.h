@@ -203,14 +203,17 @@ tpa_status tpa_decode_attn(const tpa_dims* dims, const tpa_factors* q, const tpa
  * dW = dF^T x; the library does not provide them.
  * ------------------------------------------------------------------------- */
 
-/* Bytes of device workspace tpa_prefill_attn_backward needs: float32 dQ, dK,
- * dV and two per-query statistics, (B*h*d_h*(S + 2*(start_pos+S)) + 2*B*S*h)*4. */
+/* Bytes of device workspace tpa_prefill_attn_backward needs, with N = B*h*d_h
+ * and T = start_pos+S: float32 dQ, dK, dV (N*(S + 2T)*4), the bf16 operands of
+ * the matrix-core kernels (N*(2S + 3T)*2) and two float32 statistics per
+ * query and head (2*B*S*h*4).  The base address must be 16-byte aligned for
+ * the matrix-core path (otherwise the general kernels run). */
 size_t tpa_prefill_backward_workspace_bytes(const tpa_dims* dims, int64_t n_batch, int64_t seq_len,
                                             int64_t start_pos);
 
 /* Gradients of the prefill attention: given the forward's inputs (q, cache,
- * start_pos, causal), its output `out` [B,S,h*d_h] and the upstream gradient
- * dout (same layout and element type), writes
+ * start_pos, causal) and the upstream gradient dout [B,S,h*d_h] (the element
+ * type of dims->dtype), writes
  *   dq->a_q [B,S,h,R_Q], dq->b_q [B,S,R_Q,d_h]  (KV-only: dq->b_q = dQ [B,S,h,d_h]),
  *     gradients of the query factors as passed (b_q rotated), float32,
  *     dq->q_batch_stride applies (0 = S);
@@ -220,6 +223,9 @@ size_t tpa_prefill_backward_workspace_bytes(const tpa_dims* dims, int64_t n_batc
  * With P the softmax rows and s = q.k/sqrt(d_h): dV = P^T dO, dS = P*(dO V^T -
  * rowsum(dO*O)), dQ = dS K/sqrt(d_h), dK = dS^T Q/sqrt(d_h), then
  * dA[t,h,r] = (1/R) dX[t,h,:].B[t,r,:] and dB[t,r,:] = (1/R) sum_h A[t,h,r] dX[t,h,:].
+ * The forward output is not an argument: the row sums rowsum(dO*O) take O as
+ * recomputed in fp32 (a stored bf16 output would perturb every dS by its
+ * rounding, which the cancelling rows of dS magnify).
  * Deterministic: repeated calls give the same bits.
  *   Passage: the Q_t/K_t/V_t equations and the attention of the code
  *   walk-through (前向传播), differentiated.
@@ -227,8 +233,8 @@ size_t tpa_prefill_backward_workspace_bytes(const tpa_dims* dims, int64_t n_batc
  * key range (TPA_ERR_CAPACITY); workspace too small (TPA_ERR_WORKSPACE). */
 tpa_status tpa_prefill_attn_backward(const tpa_dims* dims, const tpa_factors* q, const tpa_cache* cache,
                                      int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal,
-                                     const void* out, const void* dout, const tpa_factors* dq,
-                                     const tpa_cache* dkv, void* workspace, size_t ws_bytes, void* stream);
+                                     const void* dout, const tpa_factors* dq, const tpa_cache* dkv,
+                                     void* workspace, size_t ws_bytes, void* stream);
 
 /* Gradient through the rotary embedding: in place on g [B,S,rows,d_h]
  * (float32), turns each pair back by the angle tpa_rope_b turned it forward

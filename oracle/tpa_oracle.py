@@ -314,13 +314,18 @@ def attend_head_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.
 
 
 def prefill_backward(fq: Dict[str, np.ndarray], cache: Dict[str, np.ndarray], dims: Dims, batch: int, seq: int,
-                     start_pos: int, causal: bool, dout: np.ndarray):
+                     start_pos: int, causal: bool, dout: np.ndarray, heads=None):
     """Gradients of sum(prefill(...) * dout) with respect to the query factors
     (as passed: b_q rotated; KV-only: the rotated Q) and to the cached key/value
     factors at positions 0..start_pos+seq-1.
 
     Returns (dfq, dkv): dfq has the keys of fq; dkv has a_k, b_k, a_v, b_v
     shaped [B, start_pos+seq, ...].
+
+    heads: if given, only these heads' attention gradients are formed (the rest
+    stay zero), so only those heads' entries of the head-factor gradients
+    (a_q, a_k, a_v) are complete; the dim-factor gradients, which sum over the
+    heads, are then partial.
     """
     h, dh = dims.n_heads, dims.head_dim
     T = start_pos + seq
@@ -331,7 +336,7 @@ def prefill_backward(fq: Dict[str, np.ndarray], cache: Dict[str, np.ndarray], di
     q_pos = positions(start_pos, seq)
     dout = np.asarray(dout, np.float64).reshape(batch, seq, h, dh)
     for b in range(batch):
-        for hh in range(h):
+        for hh in (range(h) if heads is None else heads):
             k = reconstruct(cache["a_k"][b, :T, hh:hh + 1, :], cache["b_k"][b, :T])[:, 0, :]
             v = reconstruct(cache["a_v"][b, :T, hh:hh + 1, :], cache["b_v"][b, :T])[:, 0, :]
             dq, dk, dv = attend_head_backward(Q[b, :, hh, :], k, v, q_pos, causal, dout[b, :, hh, :])
