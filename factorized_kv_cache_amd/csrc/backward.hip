@@ -149,10 +149,11 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_stats_kernel(AttnArgs a, BwdA
   const float inv_rv = 1.f / (float)a.rv;
 #pragma unroll
   for (int jo = 0; jo < kBwdOut; ++jo) {
-    if (jo >= n_out) break;
     const int64_t s = q0 + oi[jo];
-    const float o = acc[jo] / lrow[oi[jo]] * inv_rv;
-    qs[oi[jo] * dh + od[jo]] = s < a.S ? o * ldf(dO, ((b * a.S + s) * h + hh) * (int64_t)dh + od[jo]) : 0.f;
+    if (jo < n_out) {
+      const float o = acc[jo] / lrow[oi[jo]] * inv_rv;
+      qs[oi[jo] * dh + od[jo]] = s < a.S ? o * ldf(dO, ((b * a.S + s) * h + hh) * (int64_t)dh + od[jo]) : 0.f;
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < BM; i += blockDim.x) {
@@ -368,28 +369,59 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_dq_kernel(AttnArgs a, BwdArgs
 }
 
 // ---- pass 4: factor gradients of one token, dX [h, d_h] -> dA [h, R], dB [R, d_h]
-template <typename T>
+// With LDS: dX, A and B (rows padded by one float, so the R rows read
+// together fall on different banks) are staged first, each read from global
+// memory once.  Without (shapes too large for LDS): straight from memory.
+template <typename T, bool LDS>
 __device__ void bwd_factor_grads(const float* dX, const T* A, const T* Bm, int h, int R, int dh, float* dA,
-                                 float* dB) {
+                                 float* dB, float* lds) {
   const float inv_r = 1.f / (float)R;
-  for (int idx = threadIdx.x; idx < h * R; idx += blockDim.x) {
-    const int hh = idx / R, r = idx - hh * R;
-    float acc = 0.f;
-    for (int d = 0; d < dh; ++d) acc = fmaf(dX[hh * dh + d], ldf(Bm, r * dh + d), acc);
-    dA[idx] = acc * inv_r;
-  }
-  for (int idx = threadIdx.x; idx < R * dh; idx += blockDim.x) {
-    const int r = idx / dh, d = idx - r * dh;
-    float acc = 0.f;
-    for (int hh = 0; hh < h; ++hh) acc = fmaf(ldf(A, hh * R + r), dX[hh * dh + d], acc);
-    dB[idx] = acc * inv_r;
+  if constexpr (LDS) {
+    float* xs = lds;              // [h][d_h]
+    float* as = xs + h * dh;      // [h][R]
+    float* bs = as + h * R;       // [R][d_h + 1]
+    const int ldb = dh + 1;
+    __syncthreads();              // the previous tensor's reads are done
+    for (int idx = threadIdx.x; idx < h * dh; idx += blockDim.x) xs[idx] = dX[idx];
+    for (int idx = threadIdx.x; idx < h * R; idx += blockDim.x) as[idx] = ldf(A, idx);
+    for (int idx = threadIdx.x; idx < R * dh; idx += blockDim.x) {
+      const int r = idx / dh, d = idx - r * dh;
+      bs[r * ldb + d] = ldf(Bm, idx);
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < h * R; idx += blockDim.x) {
+      const int hh = idx / R, r = idx - hh * R;
+      float acc = 0.f;
+      for (int d = 0; d < dh; ++d) acc = fmaf(xs[hh * dh + d], bs[r * ldb + d], acc);
+      dA[idx] = acc * inv_r;
+    }
+    for (int idx = threadIdx.x; idx < R * dh; idx += blockDim.x) {
+      const int r = idx / dh, d = idx - r * dh;
+      float acc = 0.f;
+      for (int hh = 0; hh < h; ++hh) acc = fmaf(as[hh * R + r], xs[hh * dh + d], acc);
+      dB[idx] = acc * inv_r;
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < h * R; idx += blockDim.x) {
+      const int hh = idx / R, r = idx - hh * R;
+      float acc = 0.f;
+      for (int d = 0; d < dh; ++d) acc = fmaf(dX[hh * dh + d], ldf(Bm, r * dh + d), acc);
+      dA[idx] = acc * inv_r;
+    }
+    for (int idx = threadIdx.x; idx < R * dh; idx += blockDim.x) {
+      const int r = idx / dh, d = idx - r * dh;
+      float acc = 0.f;
+      for (int hh = 0; hh < h; ++hh) acc = fmaf(ldf(A, hh * R + r), dX[hh * dh + d], acc);
+      dB[idx] = acc * inv_r;
+    }
   }
 }
 
 // One workgroup per (sequence, token): blockIdx.x < S: query token (when the
 // query is factored); then the key/value tokens 0 .. n_keys-1.
-template <typename T>
+template <typename T, bool LDS>
 __global__ void __launch_bounds__(kBwdThreads) bwd_factor_kernel(AttnArgs a, BwdArgs g) {
+  extern __shared__ float fsmem[];
   const int h = a.h, dh = a.d_h;
   const int64_t b = blockIdx.y;
   const int64_t n_keys = a.start_pos + a.S;
@@ -401,9 +433,10 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_factor_kernel(AttnArgs a, Bwd
       float* out = g.d_bq + (b * g.dq_bstride + u) * h * (int64_t)dh;
       for (int idx = threadIdx.x; idx < h * dh; idx += blockDim.x) out[idx] = dX[idx];
     } else {
-      bwd_factor_grads<T>(dX, reinterpret_cast<const T*>(a.a_q) + tok * h * a.rq,
-                          reinterpret_cast<const T*>(a.b_q) + tok * a.rq * dh, h, a.rq, dh,
-                          g.d_aq + (b * g.dq_bstride + u) * h * a.rq, g.d_bq + (b * g.dq_bstride + u) * a.rq * dh);
+      bwd_factor_grads<T, LDS>(dX, reinterpret_cast<const T*>(a.a_q) + tok * h * a.rq,
+                               reinterpret_cast<const T*>(a.b_q) + tok * a.rq * dh, h, a.rq, dh,
+                               g.d_aq + (b * g.dq_bstride + u) * h * a.rq,
+                               g.d_bq + (b * g.dq_bstride + u) * a.rq * dh, fsmem);
     }
     return;
   }
@@ -413,12 +446,31 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_factor_kernel(AttnArgs a, Bwd
   const int64_t drow = b * g.dkv_max_seq + t;
   const float* dK = g.dk + (b * n_keys + t) * h * (int64_t)dh;
   const float* dV = g.dv + (b * n_keys + t) * h * (int64_t)dh;
-  bwd_factor_grads<T>(dK, reinterpret_cast<const T*>(a.c_ak) + row * h * a.rk,
-                      reinterpret_cast<const T*>(a.c_bk) + row * a.rk * dh, h, a.rk, dh,
-                      g.d_ak + drow * h * a.rk, g.d_bk + drow * a.rk * dh);
-  bwd_factor_grads<T>(dV, reinterpret_cast<const T*>(a.c_av) + row * h * a.rv,
-                      reinterpret_cast<const T*>(a.c_bv) + row * a.rv * dh, h, a.rv, dh,
-                      g.d_av + drow * h * a.rv, g.d_bv + drow * a.rv * dh);
+  bwd_factor_grads<T, LDS>(dK, reinterpret_cast<const T*>(a.c_ak) + row * h * a.rk,
+                           reinterpret_cast<const T*>(a.c_bk) + row * a.rk * dh, h, a.rk, dh,
+                           g.d_ak + drow * h * a.rk, g.d_bk + drow * a.rk * dh, fsmem);
+  bwd_factor_grads<T, LDS>(dV, reinterpret_cast<const T*>(a.c_av) + row * h * a.rv,
+                           reinterpret_cast<const T*>(a.c_bv) + row * a.rv * dh, h, a.rv, dh,
+                           g.d_av + drow * h * a.rv, g.d_bv + drow * a.rv * dh, fsmem);
+}
+
+static size_t bwd_lds_limit() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 0;
+  return (size_t)v;
+}
+
+template <typename T>
+static void launch_bwd_factor(const AttnArgs& a, const BwdArgs& g, hipStream_t st) {
+  const int64_t n_keys = a.start_pos + a.S;
+  const int R = a.rq > a.rk ? (a.rq > a.rv ? a.rq : a.rv) : (a.rk > a.rv ? a.rk : a.rv);
+  const size_t lds = sizeof(float) * ((size_t)a.h * a.d_h + (size_t)a.h * R + (size_t)R * (a.d_h + 1));
+  const dim3 grid((unsigned)(a.S + n_keys), (unsigned)a.n_batch);
+  if (lds <= bwd_lds_limit())
+    hipLaunchKernelGGL((bwd_factor_kernel<T, true>), grid, dim3(kBwdThreads), lds, st, a, g);
+  else
+    hipLaunchKernelGGL((bwd_factor_kernel<T, false>), grid, dim3(kBwdThreads), 0, st, a, g);
 }
 
 template <typename T, int BM, int BN>
@@ -433,8 +485,7 @@ static hipError_t launch_bwd_t(const AttnArgs& a, const BwdArgs& g, hipStream_t 
   hipLaunchKernelGGL((bwd_stats_kernel<T, BM, BN>), gq, dim3(kBwdThreads), lds1, st, a, g);
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, BM, BN>), gk, dim3(kBwdThreads), lds2, st, a, g);
   hipLaunchKernelGGL((bwd_dq_kernel<T, BM, BN>), gq, dim3(kBwdThreads), lds3, st, a, g);
-  hipLaunchKernelGGL((bwd_factor_kernel<T>), dim3((unsigned)(a.S + n_keys), (unsigned)a.n_batch),
-                     dim3(kBwdThreads), 0, st, a, g);
+  launch_bwd_factor<T>(a, g, st);
   return hipGetLastError();
 }
 
@@ -478,12 +529,7 @@ hipError_t launch_backward_mfma(const AttnArgs& a, const BwdArgs& g, hipStream_t
 
 hipError_t launch_prefill_backward(int dtype, const AttnArgs& a, const BwdArgs& g, hipStream_t st) {
   if (backward_mfma_supported(dtype, a, g)) {
-    const hipError_t e = launch_backward_mfma(a, g, st);
-    if (e != hipSuccess) return e;
-    const int64_t n_keys = a.start_pos + a.S;
-    hipLaunchKernelGGL((bwd_factor_kernel<bf16_t>), dim3((unsigned)(a.S + n_keys), (unsigned)a.n_batch),
-                       dim3(kBwdThreads), 0, st, a, g);
-    return hipGetLastError();
+    return launch_backward_mfma(a, g, st);
   }
   if (a.d_h <= 128) {
     return dtype == kF32 ? launch_bwd_t<float, 32, 32>(a, g, st) : launch_bwd_t<bf16_t, 32, 32>(a, g, st);

@@ -31,7 +31,9 @@
 //     tiles stream through LDS as k^, v^ row-major and k^ transposed; S^T and
 //     dP^T put one query per lane, and dQ^T += k^T dS^T takes the dS^T
 //     registers as its B operand.
-// The factor gradients then follow from dQ, dK, dV per token (general kernel).
+// The epilogues of 3 and 4 also form each head's factor gradients
+// dA[t, h, r] = (1/R) dX[t, h, :] . B[t, r, :] from the registers; pass 5 forms
+// the dim-factor gradients, which sum over the heads, per token.
 #include "kernels.h"
 #include "mfma.h"
 
@@ -167,6 +169,28 @@ __device__ __forceinline__ void bwd_item(int64_t hb, int h, int& blk, int& hh, i
   if (hb % 8 == 0) u = (u & 7) * (hb >> 3) + (u >> 3);
   hh = (int)(u % h);
   b = u / h;
+}
+
+// dA[r] = (1/R) sum_d x[d] Bm[r][d] for the row whose d = 16dt + 4lg + i values
+// (i < 4, dt < DH/16) this lane holds in acc[dt][col] (the lane's 16-lane
+// column); the four lane groups are summed, lane group 0 stores when ok.
+template <int DH, int NC>
+__device__ __forceinline__ void head_factor_grad(const f32x4_t (&acc)[DH / 16][NC], int col, const bf16_t* Bm, int R,
+                                                 int lg, bool ok, float* dA) {
+  const float inv_r = 1.f / (float)R;
+  for (int r = 0; r < R; ++r) {
+    float part = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) {
+      const uint2 w = *reinterpret_cast<const uint2*>(Bm + r * DH + 16 * dt + 4 * lg);
+      part = fmaf(acc[dt][col][0], __uint_as_float(w.x << 16), part);
+      part = fmaf(acc[dt][col][1], __uint_as_float(w.x & 0xffff0000u), part);
+      part = fmaf(acc[dt][col][2], __uint_as_float(w.y << 16), part);
+      part = fmaf(acc[dt][col][3], __uint_as_float(w.y & 0xffff0000u), part);
+    }
+    part = lane_group_sum(part);
+    if (ok && lg == 0) dA[r] = part * inv_r;
+  }
 }
 
 // ---- pass 3: dK and dV --------------------------------------------------------------
@@ -380,13 +404,22 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_mfma_kernel(AttnArgs a, BwdAr
   const float kscale = (float)a.rk / kLog2e;
 #pragma unroll
   for (int kt = 0; kt < KW; ++kt) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dk[dt][kt] *= kscale;
     const int64_t t = kw0 + 16 * kt + li;
-    if (t >= n_keys) continue;
+    const bool ok = t < n_keys;
+    const int64_t tc = ok ? t : n_keys - 1;
+    // this head's factor gradients dA[t, h, r] = (1/R) dX[t, h, :] . B[t, r, :]
+    head_factor_grad<DH>(dk, kt, reinterpret_cast<const bf16_t*>(a.c_bk) + (b * a.max_seq + tc) * a.rk * DH, a.rk,
+                         lg, ok, g.d_ak + ((b * g.dkv_max_seq + tc) * h + hh) * a.rk);
+    head_factor_grad<DH>(dv, kt, reinterpret_cast<const bf16_t*>(a.c_bv) + (b * a.max_seq + tc) * a.rv * DH, a.rv,
+                         lg, ok, g.d_av + ((b * g.dkv_max_seq + tc) * h + hh) * a.rv);
+    if (!ok) continue;
     const int64_t o = ((b * n_keys + t) * h + hh) * (int64_t)DH + 4 * lg;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const f32x4_t k4 = dk[dt][kt] * kscale;
-      *reinterpret_cast<float4*>(g.dk + o + 16 * dt) = make_float4(k4[0], k4[1], k4[2], k4[3]);
+      *reinterpret_cast<float4*>(g.dk + o + 16 * dt) =
+          make_float4(dk[dt][kt][0], dk[dt][kt][1], dk[dt][kt][2], dk[dt][kt][3]);
       *reinterpret_cast<float4*>(g.dv + o + 16 * dt) =
           make_float4(dv[dt][kt][0], dv[dt][kt][1], dv[dt][kt][2], dv[dt][kt][3]);
     }
@@ -665,18 +698,97 @@ __global__ void __launch_bounds__(256, 2) bwd_query_mfma_kernel(AttnArgs a, BwdA
     }
   } else {
     // lane holds d = 16dt + 4lg + i of query 16qt + li.  dQ = dS K / sqrt(d_h)
-    // with K = k^ / R_K.
+    // with K = k^ / R_K.  KV-only: dQ is the query gradient itself; factored:
+    // this head's dA_Q here, dQ to the workspace for dB_Q.
     const float qscale = 1.f / ((float)a.rk * sqrtf((float)DH));
+    f32x4_t dqt[DT][QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dqt[dt][qt] = acc[qt][dt] * qscale;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const int64_t s = sw0 + 16 * qt + li;
-      if (s >= a.S) continue;
-      float* o = g.dq + ((b * a.S + s) * h + hh) * (int64_t)DH + 4 * lg;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f32x4_t v = acc[qt][dt] * qscale;
-        *reinterpret_cast<float4*>(o + 16 * dt) = make_float4(v[0], v[1], v[2], v[3]);
+      const bool ok = s < a.S;
+      const int64_t sc = ok ? s : a.S - 1;
+      float* o;
+      if (a.rq == 0) {
+        o = g.d_bq + ((b * g.dq_bstride + sc) * h + hh) * (int64_t)DH + 4 * lg;
+      } else {
+        const int64_t tok = b * a.q_bstride_tok + sc;
+        head_factor_grad<DH>(dqt, qt, reinterpret_cast<const bf16_t*>(a.b_q) + tok * a.rq * DH, a.rq, lg, ok,
+                             g.d_aq + ((b * g.dq_bstride + sc) * h + hh) * a.rq);
+        o = g.dq + ((b * a.S + sc) * h + hh) * (int64_t)DH + 4 * lg;
       }
+      if (!ok) continue;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(o + 16 * dt) = make_float4(dqt[dt][qt][0], dqt[dt][qt][1], dqt[dt][qt][2],
+                                                              dqt[dt][qt][3]);
+    }
+  }
+}
+
+// ---- pass 5: dim-factor gradients dB[t, r, :] = (1/R) sum_h A[t, h, r] dX[t, h, :]
+// One wave per (token, tensor): the query tokens (factored queries only), then
+// each key token's K and V.  The wave stages its A [h, R] in its own LDS
+// slice (read back as broadcasts); lanes run over d, reading dX coalesced,
+// and the rank goes in chunks of 8.
+constexpr int kMaxHR = 1024;   // h * R this pass takes (larger: general kernel)
+
+template <int DH>
+__global__ void __launch_bounds__(256) bwd_dim_factor_kernel(AttnArgs a, BwdArgs g, int64_t n_items) {
+  __shared__ float a_lds[4][kMaxHR + 8];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+  const int h = a.h;
+  const int64_t n_keys = a.start_pos + a.S;
+  const int64_t nq = a.rq > 0 ? a.n_batch * a.S : 0;
+  const float* dX = nullptr;
+  const bf16_t* A = nullptr;
+  float* dB = nullptr;
+  int R = 1;
+  if (item < nq) {
+    const int64_t b = item / a.S, s = item - b * a.S;
+    const int64_t tok = b * a.q_bstride_tok + s;
+    R = a.rq;
+    dX = g.dq + (b * a.S + s) * h * (int64_t)DH;
+    A = reinterpret_cast<const bf16_t*>(a.a_q) + tok * h * R;
+    dB = g.d_bq + (b * g.dq_bstride + s) * R * (int64_t)DH;
+  } else if (item < n_items) {
+    const int64_t k = (item - nq) >> 1;
+    const bool is_v = (item - nq) & 1;
+    const int64_t b = k / n_keys, t = k - b * n_keys;
+    const int64_t row = b * a.max_seq + t, drow = b * g.dkv_max_seq + t;
+    R = is_v ? a.rv : a.rk;
+    dX = (is_v ? g.dv : g.dk) + (b * n_keys + t) * h * (int64_t)DH;
+    A = reinterpret_cast<const bf16_t*>(is_v ? a.c_av : a.c_ak) + row * h * R;
+    dB = (is_v ? g.d_bv : g.d_bk) + drow * R * (int64_t)DH;
+  }
+  float* as = a_lds[wave];
+  if (A) {
+    for (int e = lane; e < h * R; e += 64) as[e] = bf16_to_f32(A[e]);
+    if (lane < 8) as[h * R + lane] = 0.f;   // read past the last rank chunk, never stored
+  }
+  __syncthreads();
+  if (!A) return;
+  const float inv_r = 1.f / (float)R;
+#pragma unroll
+  for (int c = lane; c < DH; c += 64) {
+    for (int r0 = 0; r0 < R; r0 += 8) {
+      float acc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+      for (int hh = 0; hh < h; ++hh) {
+        const float x = dX[hh * DH + c];
+        const float* ar = as + hh * R + r0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(ar[j], x, acc[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r0 + j < R) dB[(r0 + j) * DH + c] = acc[j] * inv_r;
     }
   }
 }
@@ -699,15 +811,18 @@ static size_t bwd_max_lds() {
 
 bool backward_mfma_supported(int dtype, const AttnArgs& a, const BwdArgs& g) {
   if (dtype != kBF16 || !(a.d_h == 64 || a.d_h == 128)) return false;
+  const int r_max = a.rq > a.rk ? (a.rq > a.rv ? a.rq : a.rv) : (a.rk > a.rv ? a.rk : a.rv);
+  if (a.h * r_max > kMaxHR) return false;
   if ((a.d_h == 64 ? bwd_max_lds<64>() : bwd_max_lds<128>()) > bwd_device_lds()) return false;
   const int64_t n_keys = a.start_pos + a.S;
   const int64_t hb = (int64_t)a.h * a.n_batch;
   if ((n_keys / 64 + 1) * hb >= ((int64_t)1 << 31) || (a.S / 64 + 1) * hb >= ((int64_t)1 << 31)) return false;
   // 16-byte loads and stores
-  const void* p16[11] = {a.b_q, a.c_bk, a.c_bv, g.dout, g.q_hi, g.q_lo, g.k_hi, g.k_lo, g.v_hat, g.dk, g.dv};
-  for (int i = 0; i < 11; ++i)
+  const void* p16[12] = {a.b_q, a.c_bk, a.c_bv, g.dout, g.q_hi, g.q_lo, g.k_hi, g.k_lo, g.v_hat, g.dk, g.dv, g.dq};
+  for (int i = 0; i < 12; ++i)
     if (((uintptr_t)p16[i]) % 16) return false;
-  return ((uintptr_t)g.dq) % 16 == 0;
+  // KV-only: dQ is written straight into the caller's tensor, 16 bytes at a time
+  return a.rq > 0 || (((uintptr_t)g.d_bq) % 16 == 0 && (g.dq_bstride * a.h * a.d_h) % 4 == 0);
 }
 
 template <int DH>
@@ -726,7 +841,7 @@ static void launch_bwd_mfma_dh(const AttnArgs& a, const BwdArgs& g, hipStream_t 
                      nqd);
 }
 
-// Passes 1-4; the caller runs the factor-gradient pass after them.
+// All five passes.
 hipError_t launch_backward_mfma(const AttnArgs& a, const BwdArgs& g, hipStream_t st) {
   const int64_t n_keys = a.start_pos + a.S;
   const int64_t items = a.n_batch * (a.S + n_keys) * a.h * (a.d_h / 8);
@@ -735,6 +850,10 @@ hipError_t launch_backward_mfma(const AttnArgs& a, const BwdArgs& g, hipStream_t
   hipLaunchKernelGGL(bwd_rebuild_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, g, n_keys);
   if (a.d_h == 64) launch_bwd_mfma_dh<64>(a, g, st);
   else launch_bwd_mfma_dh<128>(a, g, st);
+  const int64_t n_items = (a.rq > 0 ? a.n_batch * a.S : 0) + 2 * a.n_batch * n_keys;
+  const dim3 grid((unsigned)((n_items + 3) / 4));
+  if (a.d_h == 64) hipLaunchKernelGGL(bwd_dim_factor_kernel<64>, grid, dim3(256), 0, st, a, g, n_items);
+  else hipLaunchKernelGGL(bwd_dim_factor_kernel<128>, grid, dim3(256), 0, st, a, g, n_items);
   return hipGetLastError();
 }
 

@@ -316,7 +316,7 @@ __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t*
 template <int DH, int R>
 __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_qblocks) {
   using C = PrefillMfmaCfg<DH>;
-  constexpr int BM = C::BM, BN = C::BN, QT = C::QT, KS = C::KS, DT = C::DT, LDK = C::LDK, LDV = C::LDV;
+  constexpr int BM = C::BM, BN = C::BN, QT = C::QT, KS = C::KS, DT = C::DT, LDV = C::LDV;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16_t* const lds = reinterpret_cast<bf16_t*>(smem);
   // buffer i: K at lds + i*KTILE, V^T at lds + 2*KTILE + i*VTILE
