@@ -39,6 +39,9 @@ definitions, written out; they serve training, which the pages mention as
 context.  Paged and ragged decode (paged_gather, decode_paged) serve a layout
 the pages do not describe: each sequence's tokens are gathered through its page list and
 run through the same decode; a sequence with no keys gets a zero output.
+The shared-basis variant (shared_keys_values, decode_shared) takes the dim
+factors of K and V as parameters common to every token, so a cache holds only
+the head factors; each key is rotated at its own position.
 
 Everything is float64.  Inputs given in bf16 arrive here as their exact values
 widened to float64.  Loops run over (batch, head) in Python; numpy's matmul is
@@ -391,6 +394,49 @@ def decode_paged(fq: Dict[str, np.ndarray], pools: Dict[str, np.ndarray], block_
         cache_b = {k: v[None] for k, v in rows.items()}
         fq_b = {k: (None if v is None else np.asarray(v)[b:b + 1]) for k, v in fq.items()}
         out[b] = decode(fq_b, cache_b, dims, 1, L)[0]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Shared-basis variant: dim factors shared by every token
+# ---------------------------------------------------------------------------
+
+def shared_keys_values(a_k: np.ndarray, a_v: np.ndarray, b_k: np.ndarray, b_v: np.ndarray, base: float,
+                       n: int):
+    """Keys and values 0..n-1 of one sequence in the shared-basis variant ([coreui]
+    "优点与创新", item 5, names a variant that shares the basis vectors across
+    tokens; it gives no formula, the reading is in the design notes): the dim
+    factors b_k [R_K, d_h] and b_v [R_V, d_h] are parameters common to all tokens,
+    the head factors a_k [n, h, R_K] and a_v [n, h, R_V] stay per token, and each
+    key is rotated at its own position:
+        k[t, h] = rope((1/R_K) sum_r a_k[t, h, r] b_k[r], t),
+        v[t, h] = (1/R_V) sum_r a_v[t, h, r] b_v[r].
+    Returns k, v [n, h, d_h]."""
+    a_k = np.asarray(a_k, np.float64)[:n]
+    a_v = np.asarray(a_v, np.float64)[:n]
+    b_k = np.asarray(b_k, np.float64)
+    b_v = np.asarray(b_v, np.float64)
+    k = reconstruct(a_k, np.broadcast_to(b_k, (n,) + b_k.shape))
+    k = rope(k[None], positions(0, n), base)[0]
+    v = reconstruct(a_v, np.broadcast_to(b_v, (n,) + b_v.shape))
+    return k, v
+
+
+def decode_shared(fq: Dict[str, np.ndarray], cache_a: Dict[str, np.ndarray], basis: Dict[str, np.ndarray],
+                  dims: Dims, batch: int, ctx_len: int) -> np.ndarray:
+    """One new query per sequence, at position ctx_len-1, over keys 0..ctx_len-1 of
+    a shared-basis cache (cache_a: a_k [B, max_seq, h, R_K], a_v [B, max_seq, h, R_V];
+    basis: b_k [R_K, d_h], b_v [R_V, d_h], b_k unrotated).  fq as for decode().
+    Returns out [B, h*d_h]."""
+    h, dh = dims.n_heads, dims.head_dim
+    Q = queries(fq, dims)                                           # [B, 1, h, d_h]
+    out = np.empty((batch, h * dh), dtype=np.float64)
+    q_pos = np.array([ctx_len - 1], dtype=np.int64)
+    for b in range(batch):
+        k, v = shared_keys_values(cache_a["a_k"][b], cache_a["a_v"][b], basis["b_k"], basis["b_v"],
+                                  dims.rope_base, ctx_len)
+        for hh in range(h):
+            out[b, hh * dh:(hh + 1) * dh] = attend_head(Q[b, :, hh, :], k[:, hh, :], v[:, hh, :], q_pos, True)[0]
     return out
 
 

@@ -79,3 +79,27 @@ def layer(x, w, d_model, h, d, rq, rk, rv, base, causal=True):
             rows.append(row)
         out.append(rows)
     return out
+
+
+def shared_decode(q, a_k, a_v, b_k, b_v, base):
+    """Shared-basis decode of one sequence: q [h][d] (already rotated at its
+    position), a_k [T][h][R_K], a_v [T][h][R_V] per token, b_k [R_K][d] and
+    b_v [R_V][d] common to all tokens.  Key t is (1/R_K) sum_r a_k[t][h][r] b_k[r]
+    turned by exp(i t theta) pairwise; value t is (1/R_V) sum_r a_v[t][h][r] b_v[r].
+    Returns [h*d] for the query attending over all T keys."""
+    T, h, d = len(a_k), len(q), len(q[0])
+    rk, rv = len(b_k), len(b_v)
+    out = []
+    for hh in range(h):
+        keys, vals = [], []
+        for t in range(T):
+            k = [sum(a_k[t][hh][r] * b_k[r][j] for r in range(rk)) / rk for j in range(d)]
+            keys.append(_rotate(k, t, base))
+            vals.append([sum(a_v[t][hh][r] * b_v[r][j] for r in range(rv)) / rv for j in range(d)])
+        sc = [sum(q[hh][j] * keys[t][j] for j in range(d)) / math.sqrt(d) for t in range(T)]
+        mx = max(sc)
+        e = [math.exp(v - mx) for v in sc]
+        z = sum(e)
+        for j in range(d):
+            out.append(sum(e[t] / z * vals[t][j] for t in range(T)))
+    return out

@@ -20,6 +20,9 @@ What pins what:
   backward_*           the written-out gradients against central finite
                        differences of the forward oracle; the inverse rotation
                        against the adjoint identity
+  shared_*             the shared-basis decode against its own scalar brute force,
+                       against the standard decode over per-token rotated copies
+                       of the basis, and with constant values
 """
 import math
 
@@ -519,10 +522,74 @@ def backward_rope_adjoint():
         _close(lhs, rhs, tol=1e-12, what=f"rope adjoint d={d}")
 
 
+# ---------------------------------------------------------------------------
+# Shared-basis variant
+# ---------------------------------------------------------------------------
+
+SHARED_CASES = [
+    # h, d, rq, rk, rv, base, B, ctx
+    (2, 4, 2, 2, 1, 10000.0, 2, 5),
+    (3, 6, 0, 1, 3, 100.0, 1, 7),      # KV-only query
+    (1, 8, 1, 3, 2, 10.0, 2, 9),       # large angles
+]
+
+
+def _shared_case(ci, seed, std=0.8):
+    h, d, rq, rk, rv, base, B, ctx = SHARED_CASES[ci]
+    rng = np.random.default_rng(seed)
+    dims = O.Dims(8, h, d, rq, rk, rv, base)
+    fq = {"q": rng.normal(0, std, (B, 1, h, d))} if dims.kv_only else \
+        {"a_q": rng.normal(0, std, (B, 1, h, rq)), "b_q": rng.normal(0, std, (B, 1, rq, d))}
+    cache_a = {"a_k": rng.normal(0, std, (B, ctx + 2, h, rk)), "a_v": rng.normal(0, std, (B, ctx + 2, h, rv))}
+    basis = {"b_k": rng.normal(0, std, (rk, d)), "b_v": rng.normal(0, std, (rv, d))}
+    return dims, fq, cache_a, basis, B, ctx
+
+
+def shared_brute_force():
+    """Shared-basis decode against the scalar brute force (complex rotation)."""
+    for ci in range(len(SHARED_CASES)):
+        dims, fq, cache_a, basis, B, ctx = _shared_case(ci, 700 + ci)
+        got = O.decode_shared(fq, cache_a, basis, dims, B, ctx)
+        Q = O.queries(fq, dims)
+        for b in range(B):
+            want = brute_force.shared_decode(Q[b, 0].tolist(), cache_a["a_k"][b, :ctx].tolist(),
+                                             cache_a["a_v"][b, :ctx].tolist(), basis["b_k"].tolist(),
+                                             basis["b_v"].tolist(), dims.rope_base)
+            _close(got[b], np.array(want), what=f"shared case {ci} seq {b}")
+
+
+def shared_equals_standard_with_rotated_copies():
+    """A standard factor cache holding, for every token t, the shared basis
+    pre-rotated at t (b_k[t] = rope(b_k, t)) and b_v itself gives the same decode."""
+    for ci in range(len(SHARED_CASES)):
+        dims, fq, cache_a, basis, B, ctx = _shared_case(ci, 720 + ci)
+        n = ctx + 2
+        cache = O.cache_new(dims, B, n)
+        cache["a_k"][:] = cache_a["a_k"]
+        cache["a_v"][:] = cache_a["a_v"]
+        bk = np.broadcast_to(basis["b_k"], (B, n) + basis["b_k"].shape)
+        cache["b_k"][:] = O.rope(bk, O.positions(0, n), dims.rope_base)
+        cache["b_v"][:] = basis["b_v"]
+        _close(O.decode_shared(fq, cache_a, basis, dims, B, ctx), O.decode(fq, cache, dims, B, ctx),
+               what=f"shared vs standard case {ci}")
+
+
+def shared_constant_values():
+    """With R_V = 1 and a constant value head factor c, every value is c * b_v,
+    so every head returns exactly c * b_v whatever the scores."""
+    dims, fq, cache_a, basis, B, ctx = _shared_case(0, 740)
+    cache_a["a_v"][:] = 0.6
+    out = O.decode_shared(fq, cache_a, basis, dims, B, ctx)
+    want = np.tile(0.6 * basis["b_v"][0], dims.n_heads)
+    for b in range(B):
+        _close(out[b], want, what="constant shared values")
+
+
 ALL_PINS = [
     brute_force_causal, brute_force_noncausal, textbook_mha, textbook_mqa, textbook_gqa,
     rope_identities, rope_textbook, commute_rope_factor_sum, commute_code_order_attention,
     softmax_rows, closed_form_two_tokens, closed_form_special_cases, incremental_decode,
     incremental_chunked_prefill, paged_ragged_brute_force, paged_permutation_invariance,
-    backward_finite_differences, backward_rope_adjoint,
+    backward_finite_differences, backward_rope_adjoint, shared_brute_force,
+    shared_equals_standard_with_rotated_copies, shared_constant_values,
 ]

@@ -164,6 +164,17 @@ def _rope_backward_forward_turn(g, pos, base):
     return O.rope(g, pos, base)
 
 
+def _shared_unrotated(a_k, a_v, b_k, b_v, base, n):
+    k = O.reconstruct(np.asarray(a_k, np.float64)[:n], np.broadcast_to(np.asarray(b_k, np.float64), (n,) + b_k.shape))
+    v = O.reconstruct(np.asarray(a_v, np.float64)[:n], np.broadcast_to(np.asarray(b_v, np.float64), (n,) + b_v.shape))
+    return k, v
+
+
+def _shared_rotated_at_last(a_k, a_v, b_k, b_v, base, n):
+    k, v = _shared_unrotated(a_k, a_v, b_k, b_v, base, n)
+    return O.rope(k[None], np.full(n, n - 1), base)[0], v
+
+
 MUTATIONS = {
     "rope rotates the wrong way": ("rope", _rope_sign),
     "rope pairs (i, i+d/2)": ("rope", _rope_half_split),
@@ -183,6 +194,8 @@ MUTATIONS = {
     "backward drops the softmax row term": ("attend_head_backward", _attend_backward_no_d),
     "dim-factor gradient without 1/R": ("reconstruct_backward", _reconstruct_backward_no_scale),
     "rope gradient turned the forward way": ("rope_backward", _rope_backward_forward_turn),
+    "shared keys left unrotated": ("shared_keys_values", _shared_unrotated),
+    "shared keys rotated at the query's position": ("shared_keys_values", _shared_rotated_at_last),
 }
 
 
