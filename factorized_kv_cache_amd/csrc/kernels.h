@@ -146,6 +146,20 @@ hipError_t launch_decode(int dtype, const AttnArgs& a, int64_t ctx_len, const De
 
 hipError_t launch_prefill(int dtype, const AttnArgs& a, hipStream_t st);
 
+// ---- shared-basis variant: decode over a cache of head factors ------------------
+// AttnArgs as for the decode, except c_bk / c_bv are the bases shared by every
+// token, B_K [R_K, d_h] (unrotated) and B_V [R_V, d_h]; c_ak / c_av are the
+// cache of head factors.  The rotation table gives the keys' angles.
+struct SharedPlan {
+  int64_t chunk_tokens;
+  int64_t n_chunks;
+};
+bool shared_decode_supported(const AttnArgs& a);
+SharedPlan plan_shared_decode(const AttnArgs& a, int64_t ctx_len);
+size_t shared_decode_workspace_bytes(const SharedPlan& p, const AttnArgs& a);
+hipError_t launch_shared_decode(int dtype, const AttnArgs& a, const RopeTable& tab, int64_t ctx_len,
+                                const SharedPlan& p, void* ws, hipStream_t st);
+
 // ---- prefill backward --------------------------------------------------------
 // AttnArgs as for the forward (a.out unused); gradients are float32.
 struct BwdArgs {

@@ -93,6 +93,29 @@ tpa_status check_paged(const tpa_paged_cache* c, int64_t n_batch) {
   return TPA_OK;
 }
 
+tpa_status check_shared(const tpa_shared_cache* c) {
+  if (!c) return fail(TPA_ERR_INVALID_ARGUMENT, "shared cache is NULL");
+  if (!c->a_k || !c->a_v || !c->b_k || !c->b_v)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "a shared-cache tensor or basis is NULL");
+  if (c->max_batch < 1 || c->max_seq < 1)
+    return fail(TPA_ERR_INVALID_ARGUMENT, "cache capacity must be at least 1 x 1");
+  if (c->max_seq >= kMaxTokens) return fail(TPA_ERR_UNSUPPORTED, "max_seq must be < 2^31");
+  return TPA_OK;
+}
+
+// The shared-basis cache seen through the attention arguments: the head
+// factors in the cache slots, the shared bases in place of the dim factors.
+tpa_cache shared_as_cache(const tpa_shared_cache* c) {
+  tpa_cache v;
+  v.a_k = c->a_k;
+  v.b_k = const_cast<void*>(c->b_k);
+  v.a_v = c->a_v;
+  v.b_v = const_cast<void*>(c->b_v);
+  v.max_batch = c->max_batch;
+  v.max_seq = c->max_seq;
+  return v;
+}
+
 tpa::PageMap page_map(const tpa_paged_cache* c) {
   tpa::PageMap pm;
   pm.block_table = c->block_table;
@@ -493,6 +516,84 @@ tpa_status tpa_paged_decode_attn(const tpa_dims* d, const tpa_factors* q, const 
                 workspace ? "" : ", NULL");
   return hip_status(tpa::launch_decode(d->dtype, a, max_ctx_len, p, workspace, (hipStream_t)stream),
                     "tpa_paged_decode_attn");
+}
+
+tpa_status tpa_shared_cache_append(const tpa_dims* d, const tpa_shared_cache* c, const tpa_factors* kv,
+                                   int64_t n_batch, int64_t seq_len, int64_t start_pos, void* stream) {
+  tpa_status st = check_dims(d);
+  if (st != TPA_OK) return st;
+  if ((st = check_shared(c)) != TPA_OK) return st;
+  if (!kv || !kv->a_k || !kv->a_v) return fail(TPA_ERR_INVALID_ARGUMENT, "a head-factor tensor is NULL");
+  if (n_batch < 1 || seq_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and seq_len must be >= 1");
+  if (start_pos < 0) return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos must be >= 0");
+  if (n_batch > c->max_batch)
+    return fail(TPA_ERR_CAPACITY, "n_batch %lld exceeds max_batch %lld", (long long)n_batch,
+                (long long)c->max_batch);
+  if (seq_len > c->max_seq || start_pos > c->max_seq - seq_len)
+    return fail(TPA_ERR_CAPACITY, "start_pos + seq_len (%lld) exceeds max_seq %lld",
+                (long long)(start_pos + seq_len), (long long)c->max_seq);
+  int64_t kvs;
+  if ((st = resolve_stride(kv->kv_batch_stride, seq_len, "kv_batch_stride", &kvs)) != TPA_OK) return st;
+  const int64_t es = (int64_t)elem_size(d);
+  const int64_t width[2] = {d->n_heads * d->rank_k * es, d->n_heads * d->rank_v * es};
+  const void* src[2] = {kv->a_k, kv->a_v};
+  void* dst[2] = {c->a_k, c->a_v};
+  tpa::AppendArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int t = 0; t < 4; ++t) {   // slots 2 and 3 copy nothing (width 0)
+    a.src[t] = src[t & 1];
+    a.dst[t] = dst[t & 1];
+    a.width_bytes[t] = t < 2 ? width[t] : 0;
+    a.src_bstride[t] = kvs * a.width_bytes[t];
+    a.dst_bstride[t] = c->max_seq * a.width_bytes[t];
+  }
+  a.n_batch = n_batch;
+  a.S = seq_len;
+  a.start_pos = start_pos;
+  return hip_status(tpa::launch_append(a, (hipStream_t)stream), "tpa_shared_cache_append");
+}
+
+size_t tpa_shared_decode_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t ctx_len) {
+  if (check_dims(d) != TPA_OK || n_batch < 1 || ctx_len < 1) return 0;
+  tpa_factors q;
+  memset(&q, 0, sizeof(q));
+  tpa_cache c;
+  memset(&c, 0, sizeof(c));
+  c.max_seq = ctx_len;
+  const tpa::AttnArgs a = attn_args(d, &q, 1, &c, n_batch, 1, ctx_len - 1, 1, nullptr);
+  return tpa::shared_decode_workspace_bytes(tpa::plan_shared_decode(a, ctx_len), a);
+}
+
+tpa_status tpa_shared_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_shared_cache* c,
+                                  int64_t n_batch, int64_t ctx_len, void* out, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+  tpa_status st = check_dims(d);
+  if (st != TPA_OK) return st;
+  if ((st = check_query(d, q)) != TPA_OK) return st;
+  if ((st = check_shared(c)) != TPA_OK) return st;
+  if (!out) return fail(TPA_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (n_batch < 1 || ctx_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and ctx_len must be >= 1");
+  if (n_batch > 65535) return fail(TPA_ERR_UNSUPPORTED, "n_batch must be <= 65535");
+  if (n_batch > c->max_batch)
+    return fail(TPA_ERR_CAPACITY, "n_batch %lld exceeds max_batch %lld", (long long)n_batch,
+                (long long)c->max_batch);
+  if (ctx_len > c->max_seq)
+    return fail(TPA_ERR_CAPACITY, "ctx_len %lld exceeds max_seq %lld", (long long)ctx_len, (long long)c->max_seq);
+  int64_t qs;
+  if ((st = resolve_stride(q->q_batch_stride, 1, "q_batch_stride", &qs)) != TPA_OK) return st;
+  const tpa_cache cc = shared_as_cache(c);
+  const tpa::AttnArgs a = attn_args(d, q, qs, &cc, n_batch, 1, ctx_len - 1, 1, out);
+  if (!tpa::shared_decode_supported(a))
+    return fail(TPA_ERR_UNSUPPORTED, "shared-basis decode takes up to 64 heads, R_K and R_V up to 4, and "
+                                     "per-query tables that fit the device's LDS");
+  const tpa::SharedPlan p = tpa::plan_shared_decode(a, ctx_len);
+  const size_t need = tpa::shared_decode_workspace_bytes(p, a);
+  if (!workspace || ws_bytes < need)
+    return fail(TPA_ERR_WORKSPACE, "shared decode workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
+                workspace ? "" : ", NULL");
+  return hip_status(tpa::launch_shared_decode(d->dtype, a, rope_table(d), ctx_len, p, workspace,
+                                              (hipStream_t)stream),
+                    "tpa_shared_decode_attn");
 }
 
 const char* tpa_status_string(tpa_status s) {

@@ -45,6 +45,11 @@ class tpa_paged_cache(ctypes.Structure):
                 ("page_tokens", ctypes.c_int64), ("max_pages", ctypes.c_int64), ("max_batch", ctypes.c_int64)]
 
 
+class tpa_shared_cache(ctypes.Structure):
+    _fields_ = [("a_k", ctypes.c_void_p), ("a_v", ctypes.c_void_p), ("b_k", ctypes.c_void_p),
+                ("b_v", ctypes.c_void_p), ("max_batch", ctypes.c_int64), ("max_seq", ctypes.c_int64)]
+
+
 class tpa_factors(ctypes.Structure):
     _fields_ = [("a_q", ctypes.c_void_p), ("b_q", ctypes.c_void_p), ("a_k", ctypes.c_void_p),
                 ("b_k", ctypes.c_void_p), ("a_v", ctypes.c_void_p), ("b_v", ctypes.c_void_p),
@@ -76,6 +81,11 @@ def _load():
         "tpa_paged_decode_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64]),
         "tpa_paged_decode_attn": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_paged_cache), i64, vp, i64,
                                                  vp, vp, ctypes.c_size_t, vp]),
+        "tpa_shared_cache_append": (ctypes.c_int, [P(tpa_dims), P(tpa_shared_cache), P(tpa_factors), i64, i64, i64,
+                                                   vp]),
+        "tpa_shared_decode_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64]),
+        "tpa_shared_decode_attn": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_shared_cache), i64, i64, vp, vp,
+                                                  ctypes.c_size_t, vp]),
         "tpa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tpa_last_error": (ctypes.c_char_p, []),
     }
@@ -91,6 +101,7 @@ EXPORTED = ("tpa_packed_weight_rows", "tpa_cache_elems_per_token", "tpa_factor_p
             "tpa_cache_append", "tpa_prefill_attn", "tpa_decode_workspace_bytes", "tpa_decode_attn",
             "tpa_prefill_backward_workspace_bytes", "tpa_prefill_attn_backward", "tpa_rope_b_backward",
             "tpa_paged_cache_append", "tpa_paged_decode_workspace_bytes", "tpa_paged_decode_attn",
+            "tpa_shared_cache_append", "tpa_shared_decode_workspace_bytes", "tpa_shared_decode_attn",
             "tpa_status_string", "tpa_last_error")
 
 
@@ -213,6 +224,39 @@ class PagedCache:
         mb, mp = self.block_table.shape
         return tpa_paged_cache(_ptr(self.a_k), _ptr(self.b_k), _ptr(self.a_v), _ptr(self.b_v),
                                _ptr(self.block_table), self.n_pages, self.page_tokens, mp, mb)
+
+
+@dataclasses.dataclass
+class SharedCache:
+    """Shared-basis cache: head factors a_k [max_batch, max_seq, h, R_K], a_v
+    [.., h, R_V], and the bases b_k [R_K, d_h] (unrotated), b_v [R_V, d_h]
+    common to every token (see include/tpa.h)."""
+    a_k: torch.Tensor
+    a_v: torch.Tensor
+    b_k: torch.Tensor
+    b_v: torch.Tensor
+
+    @property
+    def max_batch(self) -> int:
+        return self.a_k.shape[0]
+
+    @property
+    def max_seq(self) -> int:
+        return self.a_k.shape[1]
+
+    def c(self) -> tpa_shared_cache:
+        return tpa_shared_cache(_ptr(self.a_k), _ptr(self.a_v), _ptr(self.b_k), _ptr(self.b_v), self.max_batch,
+                                self.max_seq)
+
+
+def new_shared_cache(dims: Dims, max_batch: int, max_seq: int, b_k: torch.Tensor, b_v: torch.Tensor,
+                     device="cuda") -> SharedCache:
+    dt = dims.torch_dtype
+    h = dims.n_heads
+    assert b_k.shape == (dims.rank_k, dims.head_dim) and b_v.shape == (dims.rank_v, dims.head_dim)
+    return SharedCache(torch.zeros(max_batch, max_seq, h, dims.rank_k, dtype=dt, device=device),
+                       torch.zeros(max_batch, max_seq, h, dims.rank_v, dtype=dt, device=device),
+                       b_k.to(device=device, dtype=dt).contiguous(), b_v.to(device=device, dtype=dt).contiguous())
 
 
 def new_paged_cache(dims: Dims, n_pages: int, page_tokens: int, block_table: torch.Tensor,
@@ -345,6 +389,28 @@ def tpa_paged_decode_attn(dims: Dims, q: Factors, cache: PagedCache, ctx_lens: t
     _check(_lib.tpa_paged_decode_attn(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B,
                                       _ptr(ctx_lens), max_ctx_len, _ptr(out), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def tpa_shared_cache_append(dims: Dims, cache: SharedCache, kv: Factors, start_pos: int, stream=None):
+    """Writes kv.a_k, kv.a_v (the head factors) at positions start_pos.. of each sequence."""
+    B, S = kv.a_k.shape[0], kv.a_k.shape[1]
+    _check(_lib.tpa_shared_cache_append(ctypes.byref(dims.c()), ctypes.byref(cache.c()), ctypes.byref(kv.c()), B, S,
+                                        start_pos, _stream(stream)))
+
+
+def tpa_shared_decode_workspace_bytes(dims: Dims, batch: int, ctx_len: int) -> int:
+    return int(_lib.tpa_shared_decode_workspace_bytes(ctypes.byref(dims.c()), batch, ctx_len))
+
+
+def tpa_shared_decode_attn(dims: Dims, q: Factors, cache: SharedCache, ctx_len: int, workspace: torch.Tensor,
+                           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    B = q.b_q.shape[0]
+    if out is None:
+        out = torch.empty(B, dims.n_heads * dims.head_dim, dtype=dims.torch_dtype, device=q.b_q.device)
+    _check(_lib.tpa_shared_decode_attn(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B,
+                                       ctx_len, _ptr(out), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

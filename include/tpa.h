@@ -300,6 +300,57 @@ tpa_status tpa_paged_decode_attn(const tpa_dims* dims, const tpa_factors* q, con
                                  int64_t n_batch, const int32_t* ctx_lens, int64_t max_ctx_len, void* out,
                                  void* workspace, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Shared-basis variant.  The pages list, among TPA's variants, one that shares
+ * the basis vectors across tokens (coreui.cn review, 优点与创新 item 5) and give
+ * no formula; this library reads it as: the dim factors of K and V are
+ * parameters common to every token, B_K [R_K, d_h] (unrotated) and B_V
+ * [R_V, d_h], while the head factors stay per token, and key t is rotated at
+ * its own position:
+ *   K_t[h] = RoPE_t((1/R_K) sum_r A_K[t,h,r] B_K[r]),  V_t[h] = (1/R_V) sum_r A_V[t,h,r] B_V[r].
+ * The cache therefore holds only a_k [max_batch, max_seq, h, R_K] and
+ * a_v [max_batch, max_seq, h, R_V]: h*(R_K+R_V) elements per token.  The query
+ * is the same as for tpa_decode_attn.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  void* a_k;          /* [max_batch, max_seq, h, R_K], caller-owned device memory */
+  void* a_v;          /* [max_batch, max_seq, h, R_V] */
+  const void* b_k;    /* [R_K, d_h], shared by every token, unrotated */
+  const void* b_v;    /* [R_V, d_h] */
+  int64_t max_batch;
+  int64_t max_seq;
+} tpa_shared_cache;
+
+/* Shared-basis cache append: kv->a_k [B,S,h,R_K] and kv->a_v [B,S,h,R_V] are
+ * written, bit for bit, to positions start_pos .. start_pos+S-1 of each
+ * sequence (kv->kv_batch_stride applies; the other kv fields are ignored).
+ *   Passage: the cache writes of the code walk-through (前向传播), for the
+ *   head factors only.
+ * Errors: null pointers, B or S < 1, start_pos < 0, B > max_batch,
+ * start_pos+S > max_seq (TPA_ERR_CAPACITY). */
+tpa_status tpa_shared_cache_append(const tpa_dims* dims, const tpa_shared_cache* cache, const tpa_factors* kv,
+                                   int64_t n_batch, int64_t seq_len, int64_t start_pos, void* stream);
+
+/* Device workspace for tpa_shared_decode_attn: float32 partials
+ * (max, sum, R_V weights) per sequence, key chunk and head. */
+size_t tpa_shared_decode_workspace_bytes(const tpa_dims* dims, int64_t n_batch, int64_t ctx_len);
+
+/* Decode attention over a shared-basis cache: each sequence's new query
+ * (position ctx_len-1, q as for tpa_decode_attn) attends over its keys
+ * 0 .. ctx_len-1; out [B, h*d_h] in dims->dtype.  The score of key t is
+ * sum_r A_K[t,h,r] (q . RoPE_t(B_K[r])) / (R_K sqrt(d_h)), formed from per-query
+ * products of q with B_K and the key's rotation angles, so only the head
+ * factors are read per key; each head accumulates sum_t p_t A_V[t,h,r] and the
+ * merge applies B_V.  fp32 arithmetic throughout.  Deterministic.
+ *   Passage: the Q_t/K_t/V_t equations (核心机制总结) with the dim factors of
+ *   K and V shared, and the decode of the code walk-through (前向传播).
+ * Errors: as tpa_decode_attn; TPA_ERR_UNSUPPORTED for more than 64 heads,
+ * R_K or R_V above 4, or shapes whose per-query tables exceed the device's
+ * LDS. */
+tpa_status tpa_shared_decode_attn(const tpa_dims* dims, const tpa_factors* q, const tpa_shared_cache* cache,
+                                  int64_t n_batch, int64_t ctx_len, void* out, void* workspace, size_t ws_bytes,
+                                  void* stream);
+
 /* Static text for a status code. */
 const char* tpa_status_string(tpa_status status);
 

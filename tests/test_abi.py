@@ -183,6 +183,32 @@ def test_paged_validation():
     assert app(1, 1, c=T.tpa_paged_cache(None, FAKE, FAKE, FAKE, FAKE, 100, 64, 65, 16)) == INVALID
 
 
+def test_shared_validation():
+    lib = T.library()
+    d = dims()
+    sc = T.tpa_shared_cache(FAKE, FAKE, FAKE, FAKE, 16, 4097)
+    q = T.tpa_factors(FAKE, FAKE, None, None, None, None, 0, 0)
+    kv = T.tpa_factors(None, None, FAKE, None, FAKE, None, 0, 0)
+    need = lib.tpa_shared_decode_workspace_bytes(ctypes.byref(d), 16, 4097)
+    assert need > 0 and need % (4 * 16 * 16 * (2 + 2)) == 0      # (max, sum, R_V weights) per chunk and head
+    assert lib.tpa_shared_decode_workspace_bytes(ctypes.byref(d), 0, 4097) == 0
+    dec = lambda B, L, c=sc, qq=q: lib.tpa_shared_decode_attn(ctypes.byref(d), ctypes.byref(qq), ctypes.byref(c), B,
+                                                               L, FAKE, FAKE, need, None)
+    assert dec(17, 4097) == CAPACITY
+    assert dec(16, 4098) == CAPACITY
+    assert dec(16, 0) == INVALID
+    assert dec(16, 4097, c=T.tpa_shared_cache(FAKE, FAKE, None, FAKE, 16, 4097)) == INVALID    # no basis
+    assert dec(16, 4097, c=T.tpa_shared_cache(FAKE, None, FAKE, FAKE, 16, 4097)) == INVALID    # no a_v
+    assert dec(16, 4097, qq=T.tpa_factors(None, FAKE, None, None, None, None, 0, 0)) == INVALID   # a_q missing
+    app = lambda B, S, sp, c=sc, k=kv: lib.tpa_shared_cache_append(ctypes.byref(d), ctypes.byref(c), ctypes.byref(k),
+                                                                   B, S, sp, None)
+    assert app(17, 1, 0) == CAPACITY
+    assert app(1, 1, 4097) == CAPACITY
+    assert app(1, 0, 0) == INVALID
+    assert app(1, 1, -1) == INVALID
+    assert app(1, 1, 0, k=T.tpa_factors(None, None, None, None, FAKE, None, 0, 0)) == INVALID
+
+
 def test_status_strings():
     lib = T.library()
     for s in range(6):

@@ -74,6 +74,7 @@ _STREAMS = {
     "x": 0, "w_a_q": 1, "w_b_q": 2, "w_a_k": 3, "w_b_k": 4, "w_a_v": 5, "w_b_v": 6,
     "w_q": 7, "x_new": 8,
     "f_a_q": 10, "f_b_q": 11, "f_a_k": 12, "f_b_k": 13, "f_a_v": 14, "f_b_v": 15, "f_q": 16,
+    "basis_k": 20, "basis_v": 21,
 }
 
 
@@ -151,6 +152,14 @@ def factors(shape: Shape, batch: int, seq: int, seed: int, dtype: str, std: Opti
     out["a_v"] = normal((batch, seq, h, shape.rank_v), s, seed, "f_a_v", dtype, salt)
     out["b_v"] = normal((batch, seq, shape.rank_v, dh), s, seed, "f_b_v", dtype, salt)
     return out
+
+
+def shared_basis(shape: Shape, seed: int, dtype: str, std: Optional[float] = None) -> Dict[str, torch.Tensor]:
+    """Bases of the shared-basis variant, common to every token: b_k [R_K, d_h]
+    (unrotated) and b_v [R_V, d_h], i.i.d. normal with the factors' spread."""
+    s = factor_std(shape) if std is None else std
+    return {"b_k": normal((shape.rank_k, shape.head_dim), s, seed, "basis_k", dtype),
+            "b_v": normal((shape.rank_v, shape.head_dim), s, seed, "basis_v", dtype)}
 
 
 def to_f64(t: torch.Tensor):
