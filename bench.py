@@ -227,6 +227,45 @@ def run_paged(db, reps: int = 64):
             "ragged_GBps": round(ragged_bytes / (ragged_ms * 1e-3) / 1e9, 1)}
 
 
+def run_shared(db, reps: int = 64):
+    """Decode-call time of the shared-basis variant on the benchmark's shapes:
+    each layer's head factors (A_K, A_V of its dense cache) with seeded bases
+    B_K, B_V common to every token; layers visited in turn.  Bytes per call:
+    only the head factors, B*ctx*h*(R_K+R_V)*2; work: the per-key rotated
+    products h*R_K*d_h fused multiply-adds (fp32 vector ALU)."""
+    d, B, ctx = db.dims, db.B, db.ctx
+    s = db.wl.shape
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4343)
+    std = I.factor_std(s)
+    layers = []
+    for L in db.layers:
+        b_k = (torch.randn(s.rank_k, s.head_dim, generator=g, device="cuda") * std).to(torch.bfloat16)
+        b_v = (torch.randn(s.rank_v, s.head_dim, generator=g, device="cuda") * std).to(torch.bfloat16)
+        sc = T.SharedCache(L["cache"].a_k, L["cache"].a_v, b_k, b_v)
+        layers.append(sc)
+    ws = torch.empty(T.tpa_shared_decode_workspace_bytes(d, B, ctx), dtype=torch.uint8, device="cuda")
+    for i in range(2 * LAYERS):
+        L = db.layers[i % LAYERS]
+        T.tpa_shared_decode_attn(d, L["q"], layers[i % LAYERS], ctx, ws, out=L["out"])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        L = db.layers[i % LAYERS]
+        evs[i][0].record()
+        T.tpa_shared_decode_attn(d, L["q"], layers[i % LAYERS], ctx, ws, out=L["out"])
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+    nbytes = B * ctx * s.n_heads * (s.rank_k + s.rank_v) * 2
+    flop = 2.0 * B * ctx * s.n_heads * s.rank_k * s.head_dim
+    return {"call_us": round(ms * 1e3, 2), "bytes_per_call": nbytes,
+            "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "valu_TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2), "valu_frac": round(flop / (ms * 1e-3) / 1e12 / 157.3, 4),
+            "cache_bytes_per_token": s.n_heads * (s.rank_k + s.rank_v) * 2,
+            "standard_cache_bytes_per_token": T.tpa_cache_elems_per_token(d) * 2}
+
+
 # ---------------------------------------------------------------------------
 # Prefill workload (reported alongside)
 # ---------------------------------------------------------------------------
@@ -405,6 +444,8 @@ def main():
     }
     log("[bench] paged decode")
     result["paged_decode"] = run_paged(db)
+    log("[bench] shared-basis decode")
+    result["shared_decode"] = run_shared(db)
     if not args.no_prefill:
         log("[bench] prefill workload")
         result["prefill"] = run_prefill()

@@ -49,4 +49,36 @@ __device__ __forceinline__ float lane_group_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Maximum / sum of x over the whole wave: DPP quad permutations and row
+// mirrors combine each 16-lane row, the half-wave swaps combine the rows.
+// Every lane ends with the result; the pairing order is fixed.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Maximum / sum over the 16 lanes of a row (lanes 16k .. 16k + 15): pairs,
+// then quads, then the mirrored halves of 8 and of 16.  Each step combines two
+// partial results that every lane of the pair holds with the same bits, so all
+// 16 lanes end with the same value.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));    // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_mov<0x4E>(x));    // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_mov<0x141>(x));   // row_half_mirror
+  x = fmaxf(x, dpp_mov<0x140>(x));   // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) { return lane_group_max(row16_max(x)); }
+
+__device__ __forceinline__ float wave_sum(float x) { return lane_group_sum(row16_sum(x)); }
+
 }  // namespace tpa

@@ -16,198 +16,406 @@
 // Values never need B_V inside the loop: each head accumulates
 // w[r] = sum_t p_t A_V[t,h,r], and the combine forms (1/R_V) sum_r w[r] B_V[r].
 //
-// One workgroup per (sequence, chunk of keys) covers every head.  A block of
-// 32 keys: the angle pairs go to LDS (fp64 angles as in every rotation here);
-// lane l of each half-wave takes key l of the block and the heads g, g+8, ...
-// of its half-wave g, with an online softmax of its own; the 32 lanes merge
-// at the end of the chunk, and a second pass merges the chunks in order.
+// One workgroup per (sequence, chunk of keys) covers every head.  It forms
+// alpha/beta of every (head, rank) once, as bf16 hi + lo rows in LDS, and then
+// walks the chunk in blocks of 64 keys with no barrier: wave w takes keys
+// 16 (w % 4) .. + 15 of each block and a group of 16-column tiles (w / 4).
+// The products run transposed on the matrix cores,
+//   G^T[(h, r), t] = sum_i alpha[h,r,i] cos(t th_i) + beta[h,r,i] sin(t th_i),
+// with each lane forming its key's angle features in registers (fp64 angles,
+// as in every rotation here; features and alpha/beta both as hi + lo, three
+// products: fp32-level accuracy).  Lane (li, lg) then holds key li and the four
+// consecutive columns 16 n0 + 4 lg .. + 3 of tile n0.  Columns are numbered
+// head * RKP + rank, RKP in {1, 2, 4} the smallest power of two >= R_K (ranks
+// past R_K are zero), so the lane holds whole heads (HPL = 4 / RKP per tile):
+// the rank sum of a score stays in the lane, and the head factors it needs are
+// contiguous in its key's cache row, loaded straight into registers ahead of
+// the products.  Each lane keeps an online softmax per head over its own keys; the 16
+// keys of a wave merge through DPP, the four waves of a tile group through LDS,
+// and a second pass merges the chunks over a fixed tree.
 #include "kernels.h"
+#include "mfma.h"
 
 namespace tpa {
 
-constexpr int kShT = 32;   // keys per block: one per lane of a half-wave
+constexpr int kShB = 64;      // keys per block: 16 per wave of a tile group
+constexpr int kShMaxKS = 4;   // d_h / 32 k-steps of the products, d_h up to 128
+constexpr int kShMaxG = 4;    // tile groups (waves / 4) per workgroup
 
-template <typename T, int MJ, int MR>
-__global__ void __launch_bounds__(256) shared_decode_kernel(AttnArgs a, RopeTable tab, int64_t ctx_len,
-                                                            int64_t chunk, int n_chunks, float* ws) {
-  extern __shared__ __align__(16) float sh[];
-  const int h = a.h, dh = a.d_h, np = dh / 2, rk = a.rk, rv = a.rv;
-  const int ldf2 = np + 1;                              // angle rows, padded (float2 units)
-  float* qs = sh;                                       // [h][d_h] scaled query
-  float2* ab = reinterpret_cast<float2*>(qs + h * dh);  // [h * R_K][d_h/2] (alpha, beta)
-  float2* fb = ab + h * rk * np;                        // 2 x [kShT][d_h/2 + 1] (cos, sin)
+typedef uint32_t sh_u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t sh_u32x4 __attribute__((ext_vector_type(4)));
+
+// LDS carve of the decode kernel (in bytes from the start).
+struct SharedLds {
+  size_t rev, stage, bhi, blo, end;
+  int np, nt, ldb;
+};
+
+__host__ __device__ inline int shared_rkp(int rk) { return rk <= 1 ? 1 : (rk <= 2 ? 2 : 4); }
+
+__host__ __device__ inline SharedLds shared_carve(int h, int dh, int rq, int rk) {
+  SharedLds c;
+  c.np = dh / 2;
+  c.nt = (h * shared_rkp(rk) + 15) / 16;   // 16-column tiles of G^T
+  c.ldb = dh + 8;                          // alpha/beta rows (bf16), padded
+  const int rqq = rq > 0 ? rq : 1;
+  size_t o = 0;
+  c.rev = o; o += sizeof(double) * c.np;
+  // the query factors and B_K in the prologue, the four waves' per-head
+  // partials [4][h][2 + 4] at the end
+  const size_t st_in = (size_t)h * rqq + (rq > 0 ? (size_t)rqq * dh : 0) + (size_t)rk * dh;
+  const size_t st_out = (size_t)4 * h * 6;
+  c.stage = o; o += sizeof(float) * (st_in > st_out ? st_in : st_out);
+  o = (o + 15) / 16 * 16;
+  c.bhi = o; o += sizeof(bf16_t) * c.nt * 16 * c.ldb;
+  c.blo = o; o += sizeof(bf16_t) * c.nt * 16 * c.ldb;
+  c.end = o;
+  return c;
+}
+
+// Element e of a run of head factors held as raw words (bf16 pairs or fp32).
+template <typename T>
+__device__ __forceinline__ float raw_elem(const uint32_t* w, int e) {
+  if constexpr (sizeof(T) == 4) return __uint_as_float(w[e]);
+  else return __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+}
+
+template <typename T>
+__device__ __forceinline__ void raw_put(uint32_t* w, int e, const T* p, int64_t i) {
+  if constexpr (sizeof(T) == 4) {
+    w[e] = __float_as_uint(p[i]);
+  } else {
+    const uint32_t bits = reinterpret_cast<const uint16_t*>(p)[i];
+    w[e >> 1] |= (e & 1) ? bits << 16 : bits;
+  }
+}
+
+// W contiguous, W*4-byte aligned words.
+template <int W>
+__device__ __forceinline__ void load_words(uint32_t (&r)[W], const void* p) {
+  if constexpr (W == 1) {
+    r[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (W == 2) {
+    const sh_u32x2 v = *reinterpret_cast<const sh_u32x2*>(p);
+    r[0] = v.x;
+    r[1] = v.y;
+  } else {
+    static_assert(W % 4 == 0, "runs of 1, 2 or 4k words");
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const sh_u32x4 v = reinterpret_cast<const sh_u32x4*>(p)[i];
+      r[4 * i] = v.x;
+      r[4 * i + 1] = v.y;
+      r[4 * i + 2] = v.z;
+      r[4 * i + 3] = v.w;
+    }
+  }
+}
+
+// The head factors one lane needs from one cache row for one tile: the HPL
+// heads hh0 .. hh0 + HPL - 1, A_K as [HPL][RKP] and A_V as [HPL][MRV] (zeros
+// past R_K, R_V and past the last head).  Runs that are whole and aligned go
+// as one vector load each.
+template <typename T, int HPL, int MRV>
+struct TileFactors {
+  static constexpr int RKP = 4 / HPL;
+  static constexpr int KW = (4 * (int)sizeof(T) + 3) / 4;
+  static constexpr int VW = (HPL * MRV * (int)sizeof(T) + 3) / 4;
+  uint32_t k[KW];
+  uint32_t v[VW];
+
+  __device__ __forceinline__ void load(const T* AK, const T* AV, int64_t row, int hh0, int h, int rk, int rv,
+                                       bool vk, bool vv) {
+    const bool whole = hh0 + HPL <= h;
+    if (vk && whole) {
+      load_words<KW>(k, AK + row * h * rk + (int64_t)hh0 * rk);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KW; ++i) k[i] = 0u;
+#pragma unroll
+      for (int j = 0; j < HPL; ++j)
+#pragma unroll
+        for (int r = 0; r < RKP; ++r)
+          if (hh0 + j < h && r < rk) raw_put<T>(k, j * RKP + r, AK, row * h * rk + (int64_t)(hh0 + j) * rk + r);
+    }
+    if (vv && whole) {
+      load_words<VW>(v, AV + row * h * rv + (int64_t)hh0 * rv);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VW; ++i) v[i] = 0u;
+#pragma unroll
+      for (int j = 0; j < HPL; ++j)
+#pragma unroll
+        for (int r = 0; r < MRV; ++r)
+          if (hh0 + j < h && r < rv) raw_put<T>(v, j * MRV + r, AV, row * h * rv + (int64_t)(hh0 + j) * rv + r);
+    }
+  }
+};
+
+// x = hi + lo as bf16 pairs (round to nearest even each).
+__device__ __forceinline__ void split_pair8(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
+  float h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = bf16_to_f32(f32_to_bf16(x[e]));
+    l[e] = x[e] - h[e];
+  }
+  hi = pack8(h);
+  lo = pack8(l);
+}
+
+// NT tiles per wave at most, HPL heads per lane per tile (RKP = 4 / HPL
+// columns each), MRV >= R_V value ranks.  blockDim = 256 x tile groups.
+template <typename T, int NT, int HPL, int MRV>
+__global__ void __launch_bounds__(64 * 4 * kShMaxG) shared_decode_kernel(AttnArgs a, RopeTable tab,
+                                                                        int64_t ctx_len, int64_t chunk,
+                                                                        int n_chunks, float* part) {
+  constexpr int RKP = 4 / HPL;
+  using TF = TileFactors<T, HPL, MRV>;
+  extern __shared__ __align__(16) unsigned char shb[];
+  const int h = a.h, dh = a.d_h, rk = a.rk, rv = a.rv, rq = a.rq > 0 ? a.rq : 1;
+  const SharedLds L = shared_carve(h, dh, a.rq, rk);
+  const int np = L.np, nt = L.nt, ldb = L.ldb;
+  double* s_rev = reinterpret_cast<double*>(shb + L.rev);
+  float* s_aq = reinterpret_cast<float*>(shb + L.stage);     // [h][R_Q]
+  float* s_bq = s_aq + h * rq;                                 // [R_Q][d_h]
+  float* s_bk = s_bq + (a.rq > 0 ? rq * dh : 0);               // [R_K][d_h]
+  float* s_red = reinterpret_cast<float*>(shb + L.stage);      // [4][h][2 + MRV] after the loop
+  bf16_t* bhi = reinterpret_cast<bf16_t*>(shb + L.bhi);        // [nt*16][d_h + 8] alpha/beta rows, hi
+  bf16_t* blo = reinterpret_cast<bf16_t*>(shb + L.blo);        //                                  lo
   const int c = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int64_t t0 = (int64_t)c * chunk;
   const int64_t t1 = t0 + chunk < ctx_len ? t0 + chunk : ctx_len;
+  const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int mt = wave & 3, grp = wave >> 2, n_grp = blockDim.x >> 8;
   const T* AQ = reinterpret_cast<const T*>(a.a_q);
   const T* BQ = reinterpret_cast<const T*>(a.b_q);
   const T* BK = reinterpret_cast<const T*>(a.c_bk);
   const T* AK = reinterpret_cast<const T*>(a.c_ak);
   const T* AV = reinterpret_cast<const T*>(a.c_av);
+  const int64_t row0 = b * a.max_seq;
 
-  // ---- query (one token per sequence), scaled by log2(e) / (R_Q R_K sqrt(d_h))
+  // whole runs go as vector loads when the rows and the base keep them aligned
+  const bool vk = rk == RKP && (h * rk) % 4 == 0 && ((uintptr_t)AK % (4 * sizeof(T) < 16 ? 4 * sizeof(T) : 16)) == 0;
+  constexpr int VB = HPL * MRV * (int)sizeof(T);
+  const bool vv = VB >= 4 && rv == MRV && (h * rv) % (HPL * MRV) == 0 && ((uintptr_t)AV % (VB < 16 ? VB : 16)) == 0;
+
+  for (int i = threadIdx.x; i < np; i += blockDim.x) s_rev[i] = tab.rev[i];
   const int64_t tok = b * a.q_bstride_tok;
-  for (int idx = threadIdx.x; idx < h * dh; idx += blockDim.x) {
-    const int hh = idx / dh, d = idx - hh * dh;
-    float v = 0.f;
-    if (a.rq == 0) {
-      v = ldf(BQ, (tok * h + hh) * dh + d);
-    } else {
-      for (int r = 0; r < a.rq; ++r) v = fmaf(ldf(AQ, (tok * h + hh) * a.rq + r), ldf(BQ, (tok * a.rq + r) * dh + d), v);
+  if (a.rq > 0) {
+    for (int idx = threadIdx.x; idx < h * rq; idx += blockDim.x) s_aq[idx] = ldf(AQ, tok * h * rq + idx);
+    for (int idx = threadIdx.x; idx < rq * dh; idx += blockDim.x) s_bq[idx] = ldf(BQ, tok * rq * dh + idx);
+  }
+  for (int idx = threadIdx.x; idx < rk * dh; idx += blockDim.x) s_bk[idx] = ldf(BK, idx);
+  __syncthreads();
+  // ---- alpha/beta rows, column n = head RKP + r, feature 2i (alpha_i) and
+  //      2i+1 (beta_i), as bf16 hi + lo; columns with r >= R_K or past the last
+  //      head are zero.  The query pair (scaled by log2(e) / (R_Q R_K sqrt(d_h)))
+  //      is formed on the way.
+  for (int idx = threadIdx.x; idx < nt * 16 * np; idx += blockDim.x) {
+    const int n = idx / np, i = idx - n * np;
+    const int hh = n / RKP, r = n - hh * RKP;
+    float al = 0.f, be = 0.f;
+    if (hh < h && r < rk) {
+      float q0 = 0.f, q1 = 0.f;
+      if (a.rq == 0) {
+        q0 = ldf(BQ, (tok * h + hh) * dh + 2 * i);
+        q1 = ldf(BQ, (tok * h + hh) * dh + 2 * i + 1);
+      } else {
+        for (int rr = 0; rr < rq; ++rr) {
+          const float aq = s_aq[hh * rq + rr];
+          q0 = fmaf(aq, s_bq[rr * dh + 2 * i], q0);
+          q1 = fmaf(aq, s_bq[rr * dh + 2 * i + 1], q1);
+        }
+      }
+      q0 *= a.q_scale;
+      q1 *= a.q_scale;
+      const float b0 = s_bk[r * dh + 2 * i], b1 = s_bk[r * dh + 2 * i + 1];
+      al = fmaf(q0, b0, q1 * b1);
+      be = fmaf(q1, b0, -q0 * b1);
     }
-    qs[idx] = v * a.q_scale;
+    const float ah = bf16_to_f32(f32_to_bf16(al)), bh = bf16_to_f32(f32_to_bf16(be));
+    *reinterpret_cast<uint32_t*>(bhi + n * ldb + 2 * i) = pack_bf16x2(ah, bh);
+    *reinterpret_cast<uint32_t*>(blo + n * ldb + 2 * i) = pack_bf16x2(al - ah, be - bh);
   }
   __syncthreads();
-  // ---- alpha, beta of every (head, rank, pair)
-  for (int idx = threadIdx.x; idx < h * rk * np; idx += blockDim.x) {
-    const int i = idx % np, hr = idx / np;
-    const int hh = hr / rk, r = hr - hh * rk;
-    const float q0 = qs[hh * dh + 2 * i], q1 = qs[hh * dh + 2 * i + 1];
-    const float b0 = ldf(BK, (int64_t)r * dh + 2 * i), b1 = ldf(BK, (int64_t)r * dh + 2 * i + 1);
-    ab[idx] = make_float2(fmaf(q0, b0, q1 * b1), fmaf(q1, b0, -q0 * b1));
-  }
 
-  const int tt = threadIdx.x % kShT, hg = threadIdx.x / kShT;   // key slot, head group (half-wave)
-  const int n_heads = hg < h ? (h - hg + 7) / 8 : 0;            // heads hg, hg+8, ... of this lane
-  float m[MJ], l[MJ], w[MJ][MR];
+  float m[NT][HPL], l[NT][HPL], w[NT][HPL][MRV];
 #pragma unroll
-  for (int j = 0; j < MJ; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
+  for (int k = 0; k < NT; ++k)
 #pragma unroll
-    for (int r = 0; r < MR; ++r) w[j][r] = 0.f;
-  }
-
-  // angle pairs of the first block
-  auto angles = [&](int64_t blk0, float2* f) {
-    for (int idx = threadIdx.x; idx < kShT * np; idx += blockDim.x) {
-      const int ti = idx / np, i = idx - ti * np;
-      float cs, sn;
-      rope_cos_sin(tab, blk0 + ti, i, cs, sn);
-      f[ti * ldf2 + i] = make_float2(cs, sn);
+    for (int j = 0; j < HPL; ++j) {
+      m[k][j] = -INFINITY;
+      l[k][j] = 0.f;
+#pragma unroll
+      for (int r = 0; r < MRV; ++r) w[k][j][r] = 0.f;
     }
-  };
-  angles(t0, fb);
-  __syncthreads();
-  int buf = 0;
-  for (int64_t blk0 = t0; blk0 < t1; blk0 += kShT) {
-    const float2* f = fb + buf * kShT * ldf2;
-    // the next block's angles into the other buffer (read after the barrier below)
-    if (blk0 + kShT < t1) angles(blk0 + kShT, fb + (buf ^ 1) * kShT * ldf2);
-    const int64_t t = blk0 + tt;
-    const bool valid = t < t1;
-    const int64_t row = b * a.max_seq + (valid ? t : t1 - 1);
-    // g[j][r] = q_h . RoPE_t(B_K[r]) for this lane's key and heads
-    float g[MJ][MR];
+  const int ksn = dh / 32;
+  for (int64_t blk0 = t0; blk0 < t1; blk0 += kShB) {
+    const int64_t key = blk0 + 16 * mt + li;
+    const bool valid = key < t1;
+    // the head factors of the lane's key go out first; the products hide them
+    TF cur[NT];
 #pragma unroll
-    for (int j = 0; j < MJ; ++j)
+    for (int k = 0; k < NT; ++k) {
+      const int n0 = grp + n_grp * k;
+      if (n0 < nt && valid) cur[k].load(AK, AV, row0 + key, (16 * n0 + 4 * lg) / RKP, h, rk, rv, vk, vv);
+    }
+    // ---- per k-step: the features of key li, 32 ks + 8 lg .. + 7 = (cos, sin)
+    //      of pairs 16 ks + 4 lg .. + 3, then that step of every tile's product
+    const double pos = (double)key;
+    f32x4_t acc[NT];
 #pragma unroll
-      for (int r = 0; r < MR; ++r) g[j][r] = 0.f;
-    for (int i = 0; i < np; ++i) {
-      const float2 fv = f[tt * ldf2 + i];
+    for (int k = 0; k < NT; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < MJ; ++j) {
-        if (j < n_heads) {
-          const float2* abh = ab + (hg + 8 * j) * rk * np + i;
+    for (int ks = 0; ks < kShMaxKS; ++ks) {
+      if (ks >= ksn) break;
+      float x[8];
 #pragma unroll
-          for (int r = 0; r < MR; ++r) {
-            if (r < rk) {
-              const float2 av = abh[r * np];
-              g[j][r] = fmaf(fv.x, av.x, fmaf(fv.y, av.y, g[j][r]));
-            }
-          }
+      for (int e = 0; e < 4; ++e) {
+        double turns = pos * s_rev[16 * ks + 4 * lg + e];
+        turns -= rint(turns);
+        const float ang = (float)turns;
+        x[2 * e] = __builtin_amdgcn_cosf(ang);
+        x[2 * e + 1] = __builtin_amdgcn_sinf(ang);
+      }
+      bf16x8_t fh, fl;
+      split_pair8(x, fh, fl);
+#pragma unroll
+      for (int k = 0; k < NT; ++k) {
+        const int n0 = grp + n_grp * k;
+        if (n0 >= nt) break;
+        const int boff = (16 * n0 + li) * ldb + 32 * ks + 8 * lg;
+        const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(bhi + boff);
+        const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(blo + boff);
+        acc[k] = mfma_bf16(bh, fh, acc[k]);
+        acc[k] = mfma_bf16(bl, fh, acc[k]);
+        acc[k] = mfma_bf16(bh, fl, acc[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+      const int n0 = grp + n_grp * k;
+      if (n0 >= nt) break;
+      // acc[k][i] = G^T[column 16 n0 + 4 lg + i][key li]
+      if (valid) {
+#pragma unroll
+        for (int j = 0; j < HPL; ++j) {
+          float s = 0.f;
+#pragma unroll
+          for (int r = 0; r < RKP; ++r) s = fmaf(raw_elem<T>(cur[k].k, j * RKP + r), acc[k][j * RKP + r], s);
+          // one exponential per key: exp2(-|s - m|) is the old terms' factor
+          // when s is the new maximum, else the new term's weight
+          const float d = s - m[k][j];
+          const float e2 = fast_exp2(-fabsf(d));
+          const bool up = d > 0.f;
+          const float alpha = up ? e2 : 1.f, p = up ? 1.f : e2;
+          m[k][j] = up ? s : m[k][j];
+          l[k][j] = fmaf(l[k][j], alpha, p);
+#pragma unroll
+          for (int r = 0; r < MRV; ++r)
+            w[k][j][r] = fmaf(w[k][j][r], alpha, p * raw_elem<T>(cur[k].v, j * MRV + r));
         }
       }
     }
-    // scores and the lane's online softmax per head
-#pragma unroll
-    for (int j = 0; j < MJ; ++j) {
-      if (j < n_heads && valid) {
-        const int hh = hg + 8 * j;
-        float s = 0.f;
-#pragma unroll
-        for (int r = 0; r < MR; ++r)
-          if (r < rk) s = fmaf(ldf(AK, (row * h + hh) * rk + r), g[j][r], s);
-        const float mn = fmaxf(m[j], s);
-        const float alpha = fast_exp2(m[j] - mn);   // 0 for the lane's first key
-        const float p = fast_exp2(s - mn);
-        m[j] = mn;
-        l[j] = fmaf(l[j], alpha, p);
-#pragma unroll
-        for (int r = 0; r < MR; ++r)
-          if (r < rv) w[j][r] = fmaf(w[j][r], alpha, p * ldf(AV, (row * h + hh) * rv + r));
-      }
-    }
-    __syncthreads();
-    buf ^= 1;
   }
 
-  // ---- merge the 32 key slots of each head (a half-wave), in a fixed order
+  // ---- merge the wave's 16 keys per head (DPP), then the four waves of the
+  //      tile group through LDS, in a fixed order
 #pragma unroll
-  for (int j = 0; j < MJ; ++j) {
-    float mx = m[j];
+  for (int k = 0; k < NT; ++k) {
+    const int n0 = grp + n_grp * k;
+    if (n0 >= nt) break;
 #pragma unroll
-    for (int k = 1; k < kShT; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k, kShT));
-    const float sc = mx == -INFINITY ? 0.f : fast_exp2(m[j] - mx);
-    float lt = l[j] * sc;
+    for (int j = 0; j < HPL; ++j) {
+      const float mx = row16_max(m[k][j]);
+      const float sc = m[k][j] == -INFINITY ? 0.f : fast_exp2(m[k][j] - mx);
+      const float lt = row16_sum(l[k][j] * sc);
+      float wt[MRV];
 #pragma unroll
-    for (int k = 1; k < kShT; k <<= 1) lt += __shfl_xor(lt, k, kShT);
-    float wt[MR];
+      for (int r = 0; r < MRV; ++r) wt[r] = row16_sum(w[k][j][r] * sc);
+      const int hh = (16 * n0 + 4 * lg) / RKP + j;
+      if (li == 0 && hh < h) {
+        float* q = s_red + ((int64_t)mt * h + hh) * (2 + MRV);
+        q[0] = mx;
+        q[1] = lt;
 #pragma unroll
-    for (int r = 0; r < MR; ++r) {
-      wt[r] = w[j][r] * sc;
-#pragma unroll
-      for (int k = 1; k < kShT; k <<= 1) wt[r] += __shfl_xor(wt[r], k, kShT);
+        for (int r = 0; r < MRV; ++r) q[2 + r] = wt[r];
+      }
     }
-    if (tt == 0 && j < n_heads) {
-      const int hh = hg + 8 * j;
-      float* p = ws + ((b * n_chunks + c) * h + hh) * (int64_t)(2 + rv);
-      p[0] = mx;
-      p[1] = lt;
+  }
+  __syncthreads();
+  for (int hh = threadIdx.x; hh < h; hh += blockDim.x) {
+    float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < MR; ++r)
-        if (r < rv) p[2 + r] = wt[r];
+    for (int q = 0; q < 4; ++q) mx = fmaxf(mx, s_red[((int64_t)q * h + hh) * (2 + MRV)]);
+    float lt = 0.f, wt[MRV];
+#pragma unroll
+    for (int r = 0; r < MRV; ++r) wt[r] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float* e = s_red + ((int64_t)q * h + hh) * (2 + MRV);
+      const float sc = e[0] == -INFINITY ? 0.f : fast_exp2(e[0] - mx);
+      lt = fmaf(e[1], sc, lt);
+#pragma unroll
+      for (int r = 0; r < MRV; ++r) wt[r] = fmaf(e[2 + r], sc, wt[r]);
     }
+    float* p = part + ((b * n_chunks + c) * h + hh) * (int64_t)(2 + rv);
+    p[0] = mx;
+    p[1] = lt;
+#pragma unroll
+    for (int r = 0; r < MRV; ++r)
+      if (r < rv) p[2 + r] = wt[r];
   }
 }
 
-// Chunks merged in order per (sequence, head); out = (1/R_V) sum_r W[r] B_V[r] / L.
+// Chunks merged per (sequence, head), one wave each: lane l merges chunks
+// l, l + 64, ... in order, then the 64 lanes merge over DPP and the half-wave
+// swaps, a fixed order; out = (1/R_V) sum_r W[r] B_V[r] / L.
+constexpr int kShCombWaves = 4;
+
 template <typename T, int MR>
-__global__ void __launch_bounds__(64) shared_combine_kernel(AttnArgs a, int n_chunks, const float* ws) {
-  const int hh = blockIdx.x;
+__global__ void __launch_bounds__(64 * kShCombWaves) shared_combine_kernel(AttnArgs a, int n_chunks,
+                                                                          const float* ws) {
+  const int lane = threadIdx.x & 63;
+  const int hh = blockIdx.x * kShCombWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t b = blockIdx.y;
   const int h = a.h, dh = a.d_h, rv = a.rv;
+  if (hh >= h) return;   // a whole wave
   const float* p = ws + (b * n_chunks * h + hh) * (int64_t)(2 + rv);
   const int64_t cstride = (int64_t)h * (2 + rv);
-  float M = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, p[c * cstride]);
-  float L = 0.f, W[MR];
+  float mt = -INFINITY, lt = 0.f, wt[MR];
 #pragma unroll
-  for (int r = 0; r < MR; ++r) W[r] = 0.f;
-  for (int c = 0; c < n_chunks; ++c) {
+  for (int r = 0; r < MR; ++r) wt[r] = 0.f;
+  for (int c = lane; c < n_chunks; c += 64) {
     const float* q = p + c * cstride;
-    const float s = q[0] == -INFINITY ? 0.f : fast_exp2(q[0] - M);
-    L = fmaf(q[1], s, L);
+    const float mc = q[0], lc = q[1];
+    const float mn = fmaxf(mt, mc);
+    const float sa = mt == -INFINITY ? 0.f : fast_exp2(mt - mn);
+    const float sb = mc == -INFINITY ? 0.f : fast_exp2(mc - mn);
+    mt = mn;
+    lt = lt * sa + lc * sb;
 #pragma unroll
-    for (int r = 0; r < MR; ++r)
-      if (r < rv) W[r] = fmaf(q[2 + r], s, W[r]);
+    for (int r = 0; r < MR; ++r) wt[r] = wt[r] * sa + (r < rv ? q[2 + r] : 0.f) * sb;
   }
+  const float M = wave_max(mt);
+  const float sc = mt == -INFINITY ? 0.f : fast_exp2(mt - M);
+  const float L = wave_sum(lt * sc);
+  float W[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) W[r] = wave_sum(wt[r] * sc);
   const float inv = a.v_scale / L;
   const T* BV = reinterpret_cast<const T*>(a.c_bv);
   T* out = reinterpret_cast<T*>(a.out);
-  for (int d = threadIdx.x; d < dh; d += blockDim.x) {
+  for (int d = lane; d < dh; d += 64) {
     float o = 0.f;
 #pragma unroll
     for (int r = 0; r < MR; ++r)
       if (r < rv) o = fmaf(W[r], ldf(BV, (int64_t)r * dh + d), o);
     stf(out, (b * h + hh) * (int64_t)dh + d, o * inv);
   }
-}
-
-static size_t shared_lds_bytes(const AttnArgs& a) {
-  const size_t np = a.d_h / 2;
-  return sizeof(float) * ((size_t)a.h * a.d_h + (size_t)a.h * a.rk * a.d_h + 2 * kShT * (np + 1) * 2);
 }
 
 static size_t shared_device_lds() {
@@ -217,48 +425,118 @@ static size_t shared_device_lds() {
   return (size_t)v;
 }
 
-// Heads per lane and ranks the kernel instances hold in registers.
-bool shared_decode_supported(const AttnArgs& a) {
-  const int hpl = (a.h + 7) / 8;
-  if (hpl > 8 || a.rk > 4 || a.rv > 4) return false;
-  return shared_lds_bytes(a) <= shared_device_lds();
+// The kernel's shape for a layer: heads per lane per tile, value ranks, tile
+// groups and tiles per wave.  A wave keeps, per tile, HPL (2 + MRV) softmax
+// registers, one key's head factors, four accumulators and about eight
+// registers of alpha/beta operands in flight.  The tile groups grow until the
+// instance's tiles (a power of two) cost at most 76 such registers, or 88 for
+// four tiles of one head per lane: the bounds under which every instance fits
+// the 128 registers of four resident waves per SIMD without spills.
+struct SharedShape {
+  int hpl, mrv, groups, ntw, nt_max;
+};
+
+__host__ __device__ constexpr bool shared_fits(int es, int nt_max, int hpl, int mrv) {
+  const int per_tile = hpl * (2 + mrv) + (4 * es + 3) / 4 + (hpl * mrv * es + 3) / 4 + 12;
+  return (nt_max >= 1 && nt_max <= 2 && nt_max * per_tile <= 76) ||
+         (nt_max == 4 && hpl == 1 && nt_max * per_tile <= 88);
 }
 
+static SharedShape shared_shape(int dtype, const AttnArgs& a) {
+  SharedShape s;
+  const int es = dtype == kF32 ? 4 : 2;
+  const int rkp = shared_rkp(a.rk);
+  s.hpl = 4 / rkp;
+  s.mrv = a.rv <= 1 ? 1 : (a.rv <= 2 ? 2 : 4);
+  const int nt = (a.h * rkp + 15) / 16;
+  s.groups = 0;
+  s.ntw = 0;
+  s.nt_max = 0;
+  for (int g = 1; g <= kShMaxG; g *= 2) {
+    const int ntw = (nt + g - 1) / g;
+    const int ntm = ntw <= 1 ? 1 : (ntw <= 2 ? 2 : (ntw <= 4 ? 4 : 0));
+    if (shared_fits(es, ntm, s.hpl, s.mrv)) {
+      s.groups = g;
+      s.ntw = ntw;
+      s.nt_max = ntm;
+      break;
+    }
+  }
+  return s;
+}
+
+#ifndef TPA_SHARED_WGS
+#define TPA_SHARED_WGS 1024
+#endif
+
+// Chunks of whole 64-key blocks, about TPA_SHARED_WGS workgroups in all.
 SharedPlan plan_shared_decode(const AttnArgs& a, int64_t ctx_len) {
   SharedPlan p;
-  int64_t n = (512 + a.n_batch - 1) / a.n_batch;   // about two workgroups per CU in all
-  const int64_t max_n = (ctx_len + kShT - 1) / kShT;
+  int64_t n = (TPA_SHARED_WGS + a.n_batch - 1) / a.n_batch;
+  const int64_t max_n = (ctx_len + kShB - 1) / kShB;
   n = n < 1 ? 1 : (n > max_n ? max_n : n);
-  p.chunk_tokens = ((ctx_len + n - 1) / n + kShT - 1) / kShT * kShT;
+  p.chunk_tokens = ((ctx_len + n - 1) / n + kShB - 1) / kShB * kShB;
   p.n_chunks = (ctx_len + p.chunk_tokens - 1) / p.chunk_tokens;
   return p;
+}
+
+// The matrix-core products take d_h a multiple of 32, up to 128; R_K and R_V
+// up to 4; the per-query alpha/beta rows must fit the device's LDS.
+bool shared_decode_supported(int dtype, const AttnArgs& a) {
+  if (a.d_h % 32 || a.d_h > 32 * kShMaxKS || a.rk < 1 || a.rk > 4 || a.rv < 1 || a.rv > 4) return false;
+  if (shared_shape(dtype, a).groups == 0) return false;
+  return shared_carve(a.h, a.d_h, a.rq, a.rk).end <= shared_device_lds();
 }
 
 size_t shared_decode_workspace_bytes(const SharedPlan& p, const AttnArgs& a) {
   return sizeof(float) * (size_t)a.n_batch * p.n_chunks * a.h * (2 + a.rv);
 }
 
-template <typename T, int MJ>
+template <typename T, int NT, int HPL, int MRV>
 static void launch_shared_t(const AttnArgs& a, const RopeTable& tab, int64_t ctx_len, const SharedPlan& p,
-                            float* ws, hipStream_t st) {
-  const dim3 grid((unsigned)p.n_chunks, (unsigned)a.n_batch);
-  hipLaunchKernelGGL((shared_decode_kernel<T, MJ, 4>), grid, dim3(256), shared_lds_bytes(a), st, a, tab, ctx_len,
-                     p.chunk_tokens, (int)p.n_chunks, ws);
-  hipLaunchKernelGGL((shared_combine_kernel<T, 4>), dim3((unsigned)a.h, (unsigned)a.n_batch), dim3(64), 0, st, a,
-                     (int)p.n_chunks, ws);
+                            int groups, float* ws, hipStream_t st) {
+  // only the instances the shape rule can pick are built
+  if constexpr (shared_fits((int)sizeof(T), NT, HPL, MRV)) {
+    const dim3 grid((unsigned)p.n_chunks, (unsigned)a.n_batch);
+    hipLaunchKernelGGL((shared_decode_kernel<T, NT, HPL, MRV>), grid, dim3(256 * groups),
+                       shared_carve(a.h, a.d_h, a.rq, a.rk).end, st, a, tab, ctx_len, p.chunk_tokens,
+                       (int)p.n_chunks, ws);
+    hipLaunchKernelGGL((shared_combine_kernel<T, MRV>),
+                       dim3((unsigned)((a.h + kShCombWaves - 1) / kShCombWaves), (unsigned)a.n_batch),
+                       dim3(64 * kShCombWaves), 0, st, a, (int)p.n_chunks, ws);
+  }
+}
+
+template <typename T, int NT, int HPL>
+static void launch_shared_v(const AttnArgs& a, const RopeTable& tab, int64_t ctx_len, const SharedPlan& p,
+                            const SharedShape& s, float* ws, hipStream_t st) {
+  if (s.mrv == 1) launch_shared_t<T, NT, HPL, 1>(a, tab, ctx_len, p, s.groups, ws, st);
+  else if (s.mrv == 2) launch_shared_t<T, NT, HPL, 2>(a, tab, ctx_len, p, s.groups, ws, st);
+  else launch_shared_t<T, NT, HPL, 4>(a, tab, ctx_len, p, s.groups, ws, st);
+}
+
+template <typename T, int NT>
+static void launch_shared_h(const AttnArgs& a, const RopeTable& tab, int64_t ctx_len, const SharedPlan& p,
+                            const SharedShape& s, float* ws, hipStream_t st) {
+  if (s.hpl == 4) launch_shared_v<T, NT, 4>(a, tab, ctx_len, p, s, ws, st);
+  else if (s.hpl == 2) launch_shared_v<T, NT, 2>(a, tab, ctx_len, p, s, ws, st);
+  else launch_shared_v<T, NT, 1>(a, tab, ctx_len, p, s, ws, st);
+}
+
+template <typename T>
+static void launch_shared_dt(const AttnArgs& a, const RopeTable& tab, int64_t ctx_len, const SharedPlan& p,
+                             const SharedShape& s, float* ws, hipStream_t st) {
+  if (s.nt_max == 1) launch_shared_h<T, 1>(a, tab, ctx_len, p, s, ws, st);
+  else if (s.nt_max == 2) launch_shared_h<T, 2>(a, tab, ctx_len, p, s, ws, st);
+  else launch_shared_v<T, 4, 1>(a, tab, ctx_len, p, s, ws, st);   // four tiles only at one head per lane
 }
 
 hipError_t launch_shared_decode(int dtype, const AttnArgs& a, const RopeTable& tab, int64_t ctx_len,
                                 const SharedPlan& p, void* ws, hipStream_t st) {
+  const SharedShape s = shared_shape(dtype, a);
   float* w = reinterpret_cast<float*>(ws);
-  const int hpl = (a.h + 7) / 8;
-  if (dtype == kF32) {
-    if (hpl <= 4) launch_shared_t<float, 4>(a, tab, ctx_len, p, w, st);
-    else launch_shared_t<float, 8>(a, tab, ctx_len, p, w, st);
-  } else {
-    if (hpl <= 4) launch_shared_t<bf16_t, 4>(a, tab, ctx_len, p, w, st);
-    else launch_shared_t<bf16_t, 8>(a, tab, ctx_len, p, w, st);
-  }
+  if (dtype == kF32) launch_shared_dt<float>(a, tab, ctx_len, p, s, w, st);
+  else launch_shared_dt<bf16_t>(a, tab, ctx_len, p, s, w, st);
   return hipGetLastError();
 }
 

@@ -583,7 +583,7 @@ tpa_status tpa_shared_decode_attn(const tpa_dims* d, const tpa_factors* q, const
   if ((st = resolve_stride(q->q_batch_stride, 1, "q_batch_stride", &qs)) != TPA_OK) return st;
   const tpa_cache cc = shared_as_cache(c);
   const tpa::AttnArgs a = attn_args(d, q, qs, &cc, n_batch, 1, ctx_len - 1, 1, out);
-  if (!tpa::shared_decode_supported(a))
+  if (!tpa::shared_decode_supported(d->dtype, a))
     return fail(TPA_ERR_UNSUPPORTED, "shared-basis decode takes up to 64 heads, R_K and R_V up to 4, and "
                                      "per-query tables that fit the device's LDS");
   const tpa::SharedPlan p = tpa::plan_shared_decode(a, ctx_len);

@@ -62,7 +62,8 @@ SHARED_CASES = [
     ("bf16_h32_dh128", "bf16", 2, 777, 4096, 32, 128, 6, 2, 2, None),
     ("bf16_kvonly_h24_r4", "bf16", 2, 300, 1536, 24, 64, 0, 4, 4, None),
     ("f32_h5_rk3_rv1", "f32", 3, 45, 64, 5, 32, 3, 3, 1, 1.0),
-    ("f32_h64_wide", "f32", 1, 70, 256, 64, 16, 2, 1, 4, 1.0),
+    ("f32_h64_wide", "f32", 1, 70, 256, 64, 32, 2, 1, 4, 1.0),
+    ("bf16_h40_r2", "bf16", 2, 200, 640, 40, 64, 2, 2, 1, None),
     ("bf16_one_key", "bf16", 2, 1, 256, 8, 64, 2, 2, 2, None),
     ("bf16_33_keys_sharp", "bf16", 2, 33, 256, 8, 64, 2, 2, 2, 1.5),
     ("f32_long_131072", "f32", 1, 131072, 256, 4, 64, 2, 2, 2, 1.0),
