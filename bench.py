@@ -232,7 +232,8 @@ def run_shared(db, reps: int = 64):
     each layer's head factors (A_K, A_V of its dense cache) with seeded bases
     B_K, B_V common to every token; layers visited in turn.  Bytes per call:
     only the head factors, B*ctx*h*(R_K+R_V)*2; work: the per-key rotated
-    products h*R_K*d_h fused multiply-adds (fp32 vector ALU)."""
+    products, h*R_K*d_h multiply-adds per key (run on the matrix cores as
+    three bf16 products of hi/lo splits)."""
     d, B, ctx = db.dims, db.B, db.ctx
     s = db.wl.shape
     g = torch.Generator(device="cuda")
@@ -261,9 +262,44 @@ def run_shared(db, reps: int = 64):
     flop = 2.0 * B * ctx * s.n_heads * s.rank_k * s.head_dim
     return {"call_us": round(ms * 1e3, 2), "bytes_per_call": nbytes,
             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "valu_TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2), "valu_frac": round(flop / (ms * 1e-3) / 1e12 / 157.3, 4),
+            "products_TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2),
             "cache_bytes_per_token": s.n_heads * (s.rank_k + s.rank_v) * 2,
             "standard_cache_bytes_per_token": T.tpa_cache_elems_per_token(d) * 2}
+
+
+def run_shared_long(reps: int = 20):
+    """The shared-basis decode at the long-context decode workload's shape
+    (8 sequences x 131072 cached keys + the new one, h 32, d_h 128, R 2): the
+    head factors are seeded draws with the factors' spread, bases likewise."""
+    wl = I.WORKLOADS["decode_b8_ctx128k"]
+    d = dims_of(wl)
+    s = wl.shape
+    B, ctx = wl.batch, wl.seq + 1
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4747)
+    std = I.factor_std(s)
+    rnd = lambda *shape: (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+    sc = T.SharedCache(rnd(B, ctx, s.n_heads, s.rank_k), rnd(B, ctx, s.n_heads, s.rank_v),
+                       rnd(s.rank_k, s.head_dim), rnd(s.rank_v, s.head_dim))
+    q = T.Factors(rnd(B, s.n_heads, s.rank_q), rnd(B, s.rank_q, s.head_dim), None, None, None, None)
+    ws = torch.empty(T.tpa_shared_decode_workspace_bytes(d, B, ctx), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, s.n_heads * s.head_dim, dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        T.tpa_shared_decode_attn(d, q, sc, ctx, ws, out=out)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        evs[i][0].record()
+        T.tpa_shared_decode_attn(d, q, sc, ctx, ws, out=out)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+    nbytes = B * ctx * s.n_heads * (s.rank_k + s.rank_v) * 2
+    flop = 2.0 * B * ctx * s.n_heads * s.rank_k * s.head_dim
+    return {"workload": wl.name, "batch": B, "context": ctx, "call_us": round(ms * 1e3, 2),
+            "bytes_per_call": nbytes, "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "products_TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2)}
 
 
 # ---------------------------------------------------------------------------
@@ -409,6 +445,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain copy of known size (for profiler byte counters)")
+    ap.add_argument("--shared-long-only", action="store_true",
+                    help="only time the shared-basis decode at the long-context shape (for a kernel trace of it)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "
@@ -418,6 +456,9 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.shared_long_only:
+        print(json.dumps({"shared_decode_long": run_shared_long()}), flush=True)
         return
 
     db, wl, ms_per_step, eager_ms, dec_avg_ms, dec_med_ms, graph_steps = run_decode(args)
@@ -446,6 +487,8 @@ def main():
     result["paged_decode"] = run_paged(db)
     log("[bench] shared-basis decode")
     result["shared_decode"] = run_shared(db)
+    log("[bench] shared-basis decode, long context")
+    result["shared_decode_long"] = run_shared_long()
     if not args.no_prefill:
         log("[bench] prefill workload")
         result["prefill"] = run_prefill()

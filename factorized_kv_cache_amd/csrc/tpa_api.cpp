@@ -584,8 +584,9 @@ tpa_status tpa_shared_decode_attn(const tpa_dims* d, const tpa_factors* q, const
   const tpa_cache cc = shared_as_cache(c);
   const tpa::AttnArgs a = attn_args(d, q, qs, &cc, n_batch, 1, ctx_len - 1, 1, out);
   if (!tpa::shared_decode_supported(d->dtype, a))
-    return fail(TPA_ERR_UNSUPPORTED, "shared-basis decode takes up to 64 heads, R_K and R_V up to 4, and "
-                                     "per-query tables that fit the device's LDS");
+    return fail(TPA_ERR_UNSUPPORTED, "shared-basis decode takes d_h a multiple of 32 up to 128, R_K and R_V "
+                                     "up to 4, per-query tables that fit the device's LDS and per-lane state "
+                                     "that fits the registers");
   const tpa::SharedPlan p = tpa::plan_shared_decode(a, ctx_len);
   const size_t need = tpa::shared_decode_workspace_bytes(p, a);
   if (!workspace || ws_bytes < need)

@@ -341,12 +341,15 @@ size_t tpa_shared_decode_workspace_bytes(const tpa_dims* dims, int64_t n_batch, 
  * sum_r A_K[t,h,r] (q . RoPE_t(B_K[r])) / (R_K sqrt(d_h)), formed from per-query
  * products of q with B_K and the key's rotation angles, so only the head
  * factors are read per key; each head accumulates sum_t p_t A_V[t,h,r] and the
- * merge applies B_V.  fp32 arithmetic throughout.  Deterministic.
+ * merge applies B_V.  The score products run on the matrix cores with both
+ * operands split into bf16 hi + lo (fp32-level accuracy); angles are reduced
+ * in fp64; the rest is fp32.  Deterministic.
  *   Passage: the Q_t/K_t/V_t equations (核心机制总结) with the dim factors of
  *   K and V shared, and the decode of the code walk-through (前向传播).
- * Errors: as tpa_decode_attn; TPA_ERR_UNSUPPORTED for more than 64 heads,
- * R_K or R_V above 4, or shapes whose per-query tables exceed the device's
- * LDS. */
+ * Errors: as tpa_decode_attn; TPA_ERR_UNSUPPORTED unless d_h is a multiple of
+ * 32 up to 128 and R_K, R_V are at most 4, for head counts whose per-query
+ * alpha/beta rows exceed the device's LDS, and for layers whose per-lane
+ * softmax state would not fit the registers (about 64 heads at rank 4). */
 tpa_status tpa_shared_decode_attn(const tpa_dims* dims, const tpa_factors* q, const tpa_shared_cache* cache,
                                   int64_t n_batch, int64_t ctx_len, void* out, void* workspace, size_t ws_bytes,
                                   void* stream);
