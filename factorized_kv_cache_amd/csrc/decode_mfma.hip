@@ -9,9 +9,12 @@
 //
 //  * scores: P[(t,r), head] = B~_K[(t,r), :] . q[head, :] as two 16x16 tiles
 //    per block, A operand = 16 cache rows read straight from HBM, B operand =
-//    q^T held in registers for the whole kernel.  Each lane loads one
-//    contiguous d_h/4 slice of its row; the same k-slot mapping is used for q,
-//    so the contraction is unchanged.
+//    q^T held in registers for the whole kernel as a bf16 hi + lo pair (two
+//    products; the cache rows are bf16 already, so the scores carry
+//    fp32-level accuracy: a bf16 query alone costs ~2^-9 of each score, which
+//    sharp heads at long context turn into output errors near 5e-3).  Each
+//    lane loads one contiguous d_h/4 slice of its row; the same k-slot mapping
+//    is used for q, so the contraction is unchanged.
 //  * the head factor: every lane's 4 output rows of a tile are R whole tokens'
 //    ranks (R in {1,2,4}), so s_t = sum_r A_K[t,head,r] P[(t,r),head] is
 //    lane-local; the block maximum per head crosses the four lane groups with
@@ -97,9 +100,14 @@ struct DecodeMfmaCfg {
   // a second block in flight (its registers spill beyond these sizes)
   static constexpr bool kPrefetch = DH == 64 && (R == 1 ? HT == 1 : HT <= 2);
   static constexpr size_t kLoopBytes = 4 * 32 * LROW * sizeof(bf16_t);
+  // the query's lo half in LDS instead of registers (lane-major, 16 bytes a
+  // lane per (head tile, k-step)) where the registers would spill
+  static constexpr bool kQloLds = (DH == 64 && HT == 4) || (DH == 128 && R == 1 && HT == 2);
+  static constexpr size_t kQloBytes = kQloLds ? (size_t)4 * HT * KS * 64 * 16 : 0;   // four waves
   static constexpr size_t kMergeBytes = (8 * HP + 2 * HP * OST) * sizeof(float);
-  static constexpr size_t kLds = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
-  static_assert(kLds <= 65536, "LDS per workgroup");
+  static constexpr size_t kLds =
+      kLoopBytes + kQloBytes > kMergeBytes ? kLoopBytes + kQloBytes : kMergeBytes;
+  static_assert(kLds <= 160 * 1024, "LDS per workgroup (gfx950: 160 KB)");
 };
 
 // LDS the host checks before choosing this kernel: staged query factors (bytes).
@@ -170,6 +178,8 @@ __device__ __forceinline__ void load_block(BlockRegs<DH, R, HT>& g, const ChunkB
 template <int DH, int R, int HT>
 __device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf16_t* lbv, int tb, int last,
                                               int lane, const bf16x8_t (&qop)[HT][DecodeMfmaCfg<DH, R, HT>::KS],
+                                              const bf16x8_t (&qlo)[HT][DecodeMfmaCfg<DH, R, HT>::KS],
+                                              const bf16x8_t* qlo_lds,
                                               float (&m_run)[HT], float (&l_run)[HT],
                                               f32x4_t (&oacc)[HT][DecodeMfmaCfg<DH, R, HT>::DT]) {
   using C = DecodeMfmaCfg<DH, R, HT>;
@@ -192,10 +202,20 @@ __device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf1
   for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      f32x4_t accv = {0.f, 0.f, 0.f, 0.f};
+      // hi and lo products in two independent chains summed at the end (one
+      // chain from three head tiles on, where the second would spill)
+      constexpr bool kTwoChains = HT <= 2;
+      f32x4_t acch = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) accv = mfma_bf16(as_bf16x8(g.bk[st][ks]), qop[ht][ks], accv);
-      sacc[st][ht] = accv;
+      for (int ks = 0; ks < KS; ++ks) {
+        acch = mfma_bf16(as_bf16x8(g.bk[st][ks]), qop[ht][ks], acch);
+        f32x4_t& al = kTwoChains ? accl : acch;
+        if constexpr (DecodeMfmaCfg<DH, R, HT>::kQloLds)
+          al = mfma_bf16(as_bf16x8(g.bk[st][ks]), qlo_lds[(ht * KS + ks) * 64 + lane], al);
+        else
+          al = mfma_bf16(as_bf16x8(g.bk[st][ks]), qlo[ht][ks], al);
+      }
+      sacc[st][ht] = kTwoChains ? acch + accl : acch;
     }
 
   // online softmax per head, and the value-product operand C
@@ -312,7 +332,9 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
 
   // ---- query operand, via the query factors staged in LDS (one round trip).
   //      Lane (head = 16*ht + li, slice lg) holds q[head][lg*DH/4 + 8*ks + j].
-  bf16x8_t qop[HT][KS];
+  bf16x8_t qop[HT][KS], qlo[HT][KS];   // q = hi + lo
+  // the wave's lo halves in LDS, past the loop's B_V tiles (not the staged factors)
+  bf16x8_t* qlo_lds = reinterpret_cast<bf16x8_t*>(smem + C::kLoopBytes) + wave * HT * KS * 64;
   {
     const bf16_t* AQ = reinterpret_cast<const bf16_t*>(a.a_q);
     const bf16_t* BQ = reinterpret_cast<const bf16_t*>(a.b_q);
@@ -350,7 +372,16 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] *= a.q_scale;
         }
-        qop[ht][ks] = pack8_int(v);
+        // q = hi + lo with the hardware conversion (the prologue has registers
+        // to spare, and it sits on every workgroup's latency path)
+        float vl[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vl[j] = v[j] - bf16_to_f32(f32_to_bf16(v[j]));
+        qop[ht][ks] = pack8(v);
+        if constexpr (C::kQloLds)
+          qlo_lds[(ht * KS + ks) * 64 + lane] = pack8(vl);
+        else
+          qlo[ht][ks] = pack8(vl);
       }
     }
     __syncthreads();
@@ -370,17 +401,17 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
   if constexpr (C::kPrefetch) {
     // two register sets in flight: blocks vb and vb+4 of this wave
     for (int vb = wave; vb < nvb; vb += 8) {
-      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, lane, qop, m_run, l_run, oacc);
+      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
       if (vb + 8 < nvb) load(r0, vb + 8);
       if (vb + 4 < nvb) {
-        compute_block<DH, R, HT>(r1, lbv, (vb + 4) * VBT, last, lane, qop, m_run, l_run, oacc);
+        compute_block<DH, R, HT>(r1, lbv, (vb + 4) * VBT, last, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
         if (vb + 12 < nvb) load(r1, vb + 12);
       }
     }
   } else {
     for (int vb = wave; vb < nvb; vb += 4) {
       if (vb != wave) load(r0, vb);
-      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, lane, qop, m_run, l_run, oacc);
+      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
     }
   }
 

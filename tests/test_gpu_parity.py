@@ -330,6 +330,43 @@ def test_prefill_full_size_sampled_rows(wl_name, B, S, n_rows):
     assert_close(out[:, rows], ref[:, rows], "bf16", f"prefill {wl_name} sampled rows")
 
 
+def test_prefill_kvonly_full_size_sampled_rows():
+    """The KV-only prefill at its full size (32 sequences of 16,384 tokens, 24
+    heads of 64, plain Q, R 4) in one call; the oracle checks 256 sampled query
+    rows (16 per sequence, 16 sequences, every head), rebuilding each sampled
+    sequence's K and V in fp64 once and attending those rows alone."""
+    require_gpu()
+    wl = I.WORKLOADS["kvonly_b32_ctx16k"]
+    sh = wl.shape
+    dims = D(sh.d_model, sh.n_heads, sh.head_dim, sh.rank_q, sh.rank_k, sh.rank_v, "bf16")
+    B, S = wl.batch, wl.seq
+    announce(f"prefill full size kvonly_b32_ctx16k B={B} S={S}")
+    kv = I.factors(sh, B, S, seed=141, dtype="bf16", with_query=False)
+    fq = I.factors(sh, B, S, seed=142, dtype="bf16")
+    cache = T.new_cache(dims, B, S)
+    fill_cache(cache, kv)
+    out = T.tpa_prefill_attn(dims, query_factors_gpu(T, dims, fq), cache, 0, True)
+    torch.cuda.synchronize()
+    del cache
+    rng = np.random.default_rng(143)
+    seqs = np.sort(rng.choice(B, 16, replace=False))
+    dh, h = sh.head_dim, sh.n_heads
+    got, want = [], []
+    for b in seqs:
+        rows = np.unique(np.concatenate([[0, S - 1], rng.integers(0, S, 14)])) if b == seqs[0] else \
+            np.unique(rng.integers(0, S, 16))
+        T_b = int(rows.max()) + 1
+        k = O.reconstruct(I.to_f64(kv["a_k"][b, :T_b]), I.to_f64(kv["b_k"][b, :T_b]))   # [T_b, h, d_h]
+        v = O.reconstruct(I.to_f64(kv["a_v"][b, :T_b]), I.to_f64(kv["b_v"][b, :T_b]))
+        q = I.to_f64(fq["q"][b, rows])                                                 # [rows, h, d_h]
+        ref = np.empty((len(rows), h * dh))
+        for hh in range(h):
+            ref[:, hh * dh:(hh + 1) * dh] = O.attend_head(q[:, hh], k[:, hh], v[:, hh], rows, True)
+        got.append(out[b, torch.as_tensor(rows, device=out.device)])
+        want.append(ref)
+    assert_close(torch.cat(got), np.concatenate(want), "bf16", "prefill kvonly_b32_ctx16k sampled rows")
+
+
 def test_decode_step_graph_replay_matches_eager():
     """The decode step (projection into the cache slot, decode attention) captured
     as a HIP graph and replayed several times, with eager work and synchronisation
@@ -377,26 +414,37 @@ def test_decode_step_graph_replay_matches_eager():
 
 def _oracle_decode_heads(fq: dict, kv: dict, dims, pairs, ctx):
     """fp64 oracle decode output of the sampled (sequence, head) pairs only: each
-    pair is reconstructed and attended on its own (its own definition)."""
+    sequence's sampled heads are reconstructed together and attended one by one
+    (each output is its own definition)."""
     od = oracle_dims(dims)
     Q = O.queries(oracle_query(fq, dims), od)                   # [B, 1, h, d_h]
     out = {}
-    for b, hh in pairs:
-        ak = I.to_f64(kv["a_k"][b, :ctx, hh:hh + 1])
-        bk = I.to_f64(kv["b_k"][b, :ctx])
-        av = I.to_f64(kv["a_v"][b, :ctx, hh:hh + 1])
-        bv = I.to_f64(kv["b_v"][b, :ctx])
-        k = O.reconstruct(ak, bk)[:, 0, :]
-        v = O.reconstruct(av, bv)[:, 0, :]
-        out[(b, hh)] = O.attend_head(Q[b, :, hh], k, v, np.array([ctx - 1]), True)[0]
+    for b in sorted({p[0] for p in pairs}):
+        heads = sorted({hh for bb, hh in pairs if bb == b})
+        k = O.reconstruct(I.to_f64(kv["a_k"][b, :ctx, heads]), I.to_f64(kv["b_k"][b, :ctx]))   # [ctx, n, d_h]
+        v = O.reconstruct(I.to_f64(kv["a_v"][b, :ctx, heads]), I.to_f64(kv["b_v"][b, :ctx]))
+        for j, hh in enumerate(heads):
+            out[(b, hh)] = O.attend_head(Q[b, :, hh], k[:, j], v[:, j], np.array([ctx - 1]), True)[0]
     return out
 
 
-@pytest.mark.parametrize("wl_name,pairs", [
-    ("decode_b8_ctx128k", [(0, 0), (3, 17), (7, 31)]),
-    ("kvonly_b32_ctx16k", [(0, 0), (13, 5), (31, 23)]),
-])
-def test_decode_full_size_sampled(wl_name, pairs):
+def _decode_pairs(wl_name):
+    """The sampled (sequence, head) pairs: every pair of the KV-only workload; two
+    seeded heads per sequence (incl. the first and last) of the long-context one,
+    whose per-sequence fp64 rebuild of every head would take 4.3 GB."""
+    wl = I.WORKLOADS[wl_name]
+    B, h = wl.batch, wl.shape.n_heads
+    if wl_name == "kvonly_b32_ctx16k":
+        return [(b, hh) for b in range(B) for hh in range(h)]
+    rng = np.random.default_rng(144)
+    pairs = [(0, 0), (B - 1, h - 1)]
+    for b in range(B):
+        pairs += [(b, int(x)) for x in rng.choice(h, 2, replace=False)]
+    return sorted(set(pairs))
+
+
+@pytest.mark.parametrize("wl_name", ["decode_b8_ctx128k", "kvonly_b32_ctx16k"])
+def test_decode_full_size_sampled(wl_name):
     """Decode at the workload's full size, in the launch configuration of a real
     call; the oracle computes sampled (sequence, head) outputs one by one."""
     require_gpu()
@@ -404,7 +452,8 @@ def test_decode_full_size_sampled(wl_name, pairs):
     sh = wl.shape
     dims = D(sh.d_model, sh.n_heads, sh.head_dim, sh.rank_q, sh.rank_k, sh.rank_v, "bf16")
     B, ctx = wl.batch, wl.seq + 1
-    announce(f"decode full size {wl_name} B={B} ctx={ctx}")
+    pairs = _decode_pairs(wl_name)
+    announce(f"decode full size {wl_name} B={B} ctx={ctx}, {len(pairs)} (sequence, head) pairs")
     kv = I.factors(sh, B, ctx, seed=121, dtype="bf16", with_query=False)
     fq = I.factors(sh, B, 1, seed=122, dtype="bf16")
     cache = T.new_cache(dims, B, ctx)
