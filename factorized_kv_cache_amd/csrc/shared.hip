@@ -30,9 +30,10 @@
 // past R_K are zero), so the lane holds whole heads (HPL = 4 / RKP per tile):
 // the rank sum of a score stays in the lane, and the head factors it needs are
 // contiguous in its key's cache row, loaded straight into registers ahead of
-// the products.  Each lane keeps an online softmax per head over its own keys; the 16
-// keys of a wave merge through DPP, the four waves of a tile group through LDS,
-// and a second pass merges the chunks over a fixed tree.
+// the products.  Each lane keeps an online softmax per head over its own keys;
+// the 16 keys of a wave merge through DPP, the four waves of a tile group
+// through LDS, and a second pass merges the chunks in a fixed order (one wave
+// per sequence and head).
 #include "kernels.h"
 #include "mfma.h"
 
