@@ -167,8 +167,11 @@ __device__ __forceinline__ void split_pair8(const float (&x)[8], bf16x8_t& hi, b
 
 // NT tiles per wave at most, HPL heads per lane per tile (RKP = 4 / HPL
 // columns each), MRV >= R_V value ranks.  blockDim = 256 x tile groups.
-template <typename T, int NT, int HPL, int MRV>
-__global__ void __launch_bounds__(64 * 4 * kShMaxG) shared_decode_kernel(AttnArgs a, RopeTable tab,
+// WIDE: four tiles of two heads per lane in one tile group (256 threads), which
+// needs up to 168 registers: three resident waves per SIMD instead of four,
+// but each key's features are formed once instead of once per tile group.
+template <typename T, int NT, int HPL, int MRV, bool WIDE>
+__global__ void __launch_bounds__(WIDE ? 256 : 64 * 4 * kShMaxG, WIDE ? 3 : 1) shared_decode_kernel(AttnArgs a, RopeTable tab,
                                                                         int64_t ctx_len, int64_t chunk,
                                                                         int n_chunks, float* part) {
   constexpr int RKP = 4 / HPL;
@@ -432,7 +435,10 @@ static size_t shared_device_lds() {
 // registers of alpha/beta operands in flight.  The tile groups grow until the
 // instance's tiles (a power of two) cost at most 76 such registers, or 88 for
 // four tiles of one head per lane: the bounds under which every instance fits
-// the 128 registers of four resident waves per SIMD without spills.
+// the 128 registers of four resident waves per SIMD without spills.  Four
+// tiles of two heads per lane in bf16 (up to two value ranks) fit 168
+// registers as one 256-thread tile group (three waves per SIMD); that form is
+// taken when one group covers the layer, so each feature is formed once.
 struct SharedShape {
   int hpl, mrv, groups, ntw, nt_max;
 };
@@ -441,6 +447,10 @@ __host__ __device__ constexpr bool shared_fits(int es, int nt_max, int hpl, int 
   const int per_tile = hpl * (2 + mrv) + (4 * es + 3) / 4 + (hpl * mrv * es + 3) / 4 + 12;
   return (nt_max >= 1 && nt_max <= 2 && nt_max * per_tile <= 76) ||
          (nt_max == 4 && hpl == 1 && nt_max * per_tile <= 88);
+}
+
+__host__ __device__ constexpr bool shared_wide(int es, int nt_max, int hpl, int mrv) {
+  return nt_max == 4 && hpl == 2 && es == 2 && mrv <= 2;
 }
 
 static SharedShape shared_shape(int dtype, const AttnArgs& a) {
@@ -456,7 +466,7 @@ static SharedShape shared_shape(int dtype, const AttnArgs& a) {
   for (int g = 1; g <= kShMaxG; g *= 2) {
     const int ntw = (nt + g - 1) / g;
     const int ntm = ntw <= 1 ? 1 : (ntw <= 2 ? 2 : (ntw <= 4 ? 4 : 0));
-    if (shared_fits(es, ntm, s.hpl, s.mrv)) {
+    if (shared_fits(es, ntm, s.hpl, s.mrv) || (g == 1 && shared_wide(es, ntm, s.hpl, s.mrv))) {
       s.groups = g;
       s.ntw = ntw;
       s.nt_max = ntm;
@@ -496,10 +506,13 @@ size_t shared_decode_workspace_bytes(const SharedPlan& p, const AttnArgs& a) {
 template <typename T, int NT, int HPL, int MRV>
 static void launch_shared_t(const AttnArgs& a, const RopeTable& tab, int64_t ctx_len, const SharedPlan& p,
                             int groups, float* ws, hipStream_t st) {
-  // only the instances the shape rule can pick are built
-  if constexpr (shared_fits((int)sizeof(T), NT, HPL, MRV)) {
+  // only the instances the shape rule can pick are built; the wide form runs
+  // as a single tile group
+  constexpr bool WIDE = shared_wide((int)sizeof(T), NT, HPL, MRV);
+  if constexpr (shared_fits((int)sizeof(T), NT, HPL, MRV) || WIDE) {
+    if (WIDE && groups != 1) return;
     const dim3 grid((unsigned)p.n_chunks, (unsigned)a.n_batch);
-    hipLaunchKernelGGL((shared_decode_kernel<T, NT, HPL, MRV>), grid, dim3(256 * groups),
+    hipLaunchKernelGGL((shared_decode_kernel<T, NT, HPL, MRV, WIDE>), grid, dim3(256 * groups),
                        shared_carve(a.h, a.d_h, a.rq, a.rk).end, st, a, tab, ctx_len, p.chunk_tokens,
                        (int)p.n_chunks, ws);
     hipLaunchKernelGGL((shared_combine_kernel<T, MRV>),
@@ -529,7 +542,7 @@ static void launch_shared_dt(const AttnArgs& a, const RopeTable& tab, int64_t ct
                              const SharedShape& s, float* ws, hipStream_t st) {
   if (s.nt_max == 1) launch_shared_h<T, 1>(a, tab, ctx_len, p, s, ws, st);
   else if (s.nt_max == 2) launch_shared_h<T, 2>(a, tab, ctx_len, p, s, ws, st);
-  else launch_shared_v<T, 4, 1>(a, tab, ctx_len, p, s, ws, st);   // four tiles only at one head per lane
+  else launch_shared_h<T, 4>(a, tab, ctx_len, p, s, ws, st);
 }
 
 hipError_t launch_shared_decode(int dtype, const AttnArgs& a, const RopeTable& tab, int64_t ctx_len,
