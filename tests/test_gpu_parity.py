@@ -468,20 +468,28 @@ def test_decode_full_size_sampled(wl_name):
     del cache, kv
 
 
-def test_mqa_equivalence_kvonly_shape():
-    """R_K = R_V = 1 with the head factors constant 1 is multi-query attention
-    (one K/V head shared by all query heads).  Decode and prefill at the KV-only
-    shape (24 heads of 64, plain Q) against textbook MQA through torch's scaled
-    dot-product attention in fp64, written without the factor machinery."""
+@pytest.mark.parametrize("name,rank,n_kv", [("MQA", 1, 1), ("GQA", 4, 4), ("MHA", 24, 24)])
+def test_textbook_equivalence_kvonly_shape(name, rank, n_kv):
+    """Non-contextual head factors reduce TPA to the textbook forms: R = 1 with
+    a = 1 is multi-query attention; R = g groups with a_r[h] = g for h in group r
+    (0 otherwise) is grouped-query attention with g K/V heads; R = h with
+    a_r[h] = h for r = h is multi-head attention (the factor cancels the 1/R).
+    Decode and prefill at the KV-only shape (24 heads of 64, plain Q) against
+    the textbook forms through torch's scaled dot-product attention in fp64,
+    written without the factor machinery.  R = 4 runs the matrix-core kernels,
+    R = 24 the general ones."""
     require_gpu()
     import textbook
-    B, S, ctx = 4, 257, 2048
-    dims = D(1536, 24, 64, 0, 1, 1, "bf16")
-    announce("MQA equivalence at the KV-only shape")
+    B, S, ctx, h = 4, 257, 2048, 24
+    dims = D(1536, h, 64, 0, rank, rank, "bf16")
+    announce(f"{name} equivalence at the KV-only shape (R = {rank})")
     sh = shape_of(dims)
     kv = I.factors(sh, B, ctx, seed=131, dtype="bf16", std=1.0, with_query=False)
+    group = torch.arange(h) // (h // n_kv)                              # K/V head of each query head
+    a = torch.zeros(h, rank, dtype=torch.bfloat16)
+    a[torch.arange(h), group] = float(rank)
     for k in ("a_k", "a_v"):
-        kv[k] = torch.ones_like(kv[k])
+        kv[k] = a.expand(B, ctx, h, rank).contiguous()
     fq = I.factors(sh, B, S, seed=132, dtype="bf16", std=1.0)
     cache = T.new_cache(dims, B, ctx)
     fill_cache(cache, kv)
@@ -492,8 +500,8 @@ def test_mqa_equivalence_kvonly_shape():
                             T.new_workspace(dims, B, ctx))
     torch.cuda.synchronize()
     q = I.to_f64(fq["q"])                                     # [B, S, 24, 64]
-    k = I.to_f64(kv["b_k"])                                   # [B, ctx, 1, 64]: the shared head
+    k = I.to_f64(kv["b_k"])                                   # [B, ctx, n_kv, 64]: the K/V heads
     v = I.to_f64(kv["b_v"])
     ref = textbook.attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), ctx - S, True).numpy()
-    assert_close(pre, ref, "bf16", "prefill vs textbook MQA")
-    assert_close(dec, ref[:, -1], "bf16", "decode vs textbook MQA")
+    assert_close(pre, ref, "bf16", f"prefill vs textbook {name}")
+    assert_close(dec, ref[:, -1], "bf16", f"decode vs textbook {name}")
