@@ -155,7 +155,7 @@ struct SharedPlan {
   int64_t n_chunks;
 };
 bool shared_decode_supported(int dtype, const AttnArgs& a);
-SharedPlan plan_shared_decode(const AttnArgs& a, int64_t ctx_len);
+SharedPlan plan_shared_decode(int dtype, const AttnArgs& a, int64_t ctx_len);
 size_t shared_decode_workspace_bytes(const SharedPlan& p, const AttnArgs& a);
 hipError_t launch_shared_decode(int dtype, const AttnArgs& a, const RopeTable& tab, int64_t ctx_len,
                                 const SharedPlan& p, void* ws, hipStream_t st);

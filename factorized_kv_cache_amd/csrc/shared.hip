@@ -476,17 +476,28 @@ static SharedShape shared_shape(int dtype, const AttnArgs& a) {
   return s;
 }
 
-#ifndef TPA_SHARED_WGS
-#define TPA_SHARED_WGS 1024
-#endif
-
-// Chunks of whole 64-key blocks, about TPA_SHARED_WGS workgroups in all.
-SharedPlan plan_shared_decode(const AttnArgs& a, int64_t ctx_len) {
+// Chunks of whole 64-key blocks.  The grid is sized to one round of resident
+// workgroups: 256 CUs times the workgroups a CU holds (three for the wide
+// form, else four waves per SIMD over the tile groups; fewer if LDS runs
+// out).  Each sequence gets floor(slots / B) chunks and its blocks are spread
+// evenly over them, so no partial second round trails the first (at
+// 8 x 131,073 keys, h 32: 968 workgroups over 768 slots took 131 us, 752 in
+// one round 112 us).
+SharedPlan plan_shared_decode(int dtype, const AttnArgs& a, int64_t ctx_len) {
   SharedPlan p;
-  int64_t n = (TPA_SHARED_WGS + a.n_batch - 1) / a.n_batch;
-  const int64_t max_n = (ctx_len + kShB - 1) / kShB;
-  n = n < 1 ? 1 : (n > max_n ? max_n : n);
-  p.chunk_tokens = ((ctx_len + n - 1) / n + kShB - 1) / kShB * kShB;
+  const SharedShape s = shared_shape(dtype, a);
+  const bool wide = s.groups == 1 && shared_wide(dtype == kF32 ? 4 : 2, s.nt_max, s.hpl, s.mrv);
+  const int groups = s.groups > 0 ? s.groups : 1;
+  int64_t per_cu = wide ? 3 : 4 / groups;
+  const size_t lds = shared_carve(a.h, a.d_h, a.rq, a.rk).end;
+  const size_t cu_lds = shared_device_lds();
+  if (lds > 0 && cu_lds > 0 && (int64_t)(cu_lds / lds) < per_cu) per_cu = (int64_t)(cu_lds / lds);
+  if (per_cu < 1) per_cu = 1;
+  int64_t per_seq = 256 * per_cu / a.n_batch;
+  if (per_seq < 1) per_seq = 1;
+  const int64_t blocks = (ctx_len + kShB - 1) / kShB;
+  const int64_t per_chunk = (blocks + per_seq - 1) / per_seq;
+  p.chunk_tokens = per_chunk * kShB;
   p.n_chunks = (ctx_len + p.chunk_tokens - 1) / p.chunk_tokens;
   return p;
 }

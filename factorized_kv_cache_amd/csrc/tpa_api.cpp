@@ -561,7 +561,7 @@ size_t tpa_shared_decode_workspace_bytes(const tpa_dims* d, int64_t n_batch, int
   memset(&c, 0, sizeof(c));
   c.max_seq = ctx_len;
   const tpa::AttnArgs a = attn_args(d, &q, 1, &c, n_batch, 1, ctx_len - 1, 1, nullptr);
-  return tpa::shared_decode_workspace_bytes(tpa::plan_shared_decode(a, ctx_len), a);
+  return tpa::shared_decode_workspace_bytes(tpa::plan_shared_decode(d->dtype, a, ctx_len), a);
 }
 
 tpa_status tpa_shared_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_shared_cache* c,
@@ -587,7 +587,7 @@ tpa_status tpa_shared_decode_attn(const tpa_dims* d, const tpa_factors* q, const
     return fail(TPA_ERR_UNSUPPORTED, "shared-basis decode takes d_h a multiple of 32 up to 128, R_K and R_V "
                                      "up to 4, per-query tables that fit the device's LDS and per-lane state "
                                      "that fits the registers");
-  const tpa::SharedPlan p = tpa::plan_shared_decode(a, ctx_len);
+  const tpa::SharedPlan p = tpa::plan_shared_decode(d->dtype, a, ctx_len);
   const size_t need = tpa::shared_decode_workspace_bytes(p, a);
   if (!workspace || ws_bytes < need)
     return fail(TPA_ERR_WORKSPACE, "shared decode workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
