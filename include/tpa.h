@@ -22,8 +22,14 @@
  *   kernels, anything else runs a general kernel with the same results
  *   up to rounding order.
  * - Element type: dims->dtype is TPA_F32 (float) or TPA_BF16 (bfloat16, stored
- *   as 16-bit words).  All tensors of a call use it.  Arithmetic is float32;
- *   bf16 results are rounded to nearest even.
+ *   as 16-bit words).  All tensors of a call use it.  Arithmetic is float32
+ *   with float32 accumulation; bf16 results are rounded to nearest even.  In
+ *   bf16 the matrix-core kernels take bf16 operands: the prefill's query,
+ *   rebuilt keys and values and probabilities are rounded to bf16; the
+ *   decode's query enters as a bf16 hi + lo pair (fp32-level scores) and its
+ *   probability-weighted value factors are rounded to bf16; the backward and
+ *   the shared-basis decode split their sensitive operands into hi + lo pairs
+ *   as documented with each call.
  * - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  *   stream).  Every call only enqueues work and returns; ordering between
  *   calls is the caller's, through the stream.
