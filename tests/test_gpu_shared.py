@@ -103,6 +103,39 @@ def test_shared_decode_full_size():
     assert_close(out, oracle_shared(fq, f, basis, dims, B, ctx), "bf16", "shared decode full size")
 
 
+def test_shared_decode_long_context_sampled_heads():
+    """The long-context decode shape the benchmark times (8 sequences of
+    131,072 cached keys + the new one, d_model 4096, h 32, d_h 128, R_Q 6, R 2)
+    with a shared basis, in one call; the oracle checks two seeded heads per
+    sequence (and the first and last), rebuilding each sampled head's keys and
+    values in fp64 on its own."""
+    require_gpu()
+    wl = I.WORKLOADS["decode_b8_ctx128k"]
+    s = wl.shape
+    dims = D(s.d_model, s.n_heads, s.head_dim, s.rank_q, s.rank_k, s.rank_v, "bf16", s.rope_base)
+    B, ctx = wl.batch, wl.seq + 1
+    announce(f"shared decode long context B={B} ctx={ctx}")
+    f, basis, fq, cache = shared_setup(dims, B, ctx, seed=91, extra=0)
+    q = query_factors_gpu(T, dims, fq, squeeze=True)
+    ws = torch.empty(T.tpa_shared_decode_workspace_bytes(dims, B, ctx), dtype=torch.uint8, device="cuda")
+    out = T.tpa_shared_decode_attn(dims, q, cache, ctx, ws)
+    torch.cuda.synchronize()
+    del cache
+    rng = np.random.default_rng(92)
+    h, dh = s.n_heads, s.head_dim
+    pairs = sorted({(0, 0), (B - 1, h - 1)} | {(b, int(x)) for b in range(B) for x in rng.choice(h, 2, replace=False)})
+    od = oracle_dims(dims)
+    Q = O.queries(oracle_query(fq, dims), od)                               # [B, 1, h, d_h]
+    bk, bv = I.to_f64(basis["b_k"]), I.to_f64(basis["b_v"])
+    got, want = [], []
+    for b, hh in pairs:
+        k, v = O.shared_keys_values(I.to_f64(f["a_k"][b, :, hh:hh + 1]), I.to_f64(f["a_v"][b, :, hh:hh + 1]),
+                                    bk, bv, od.rope_base, ctx)              # [ctx, 1, d_h]
+        want.append(O.attend_head(Q[b, :, hh], k[:, 0], v[:, 0], np.array([ctx - 1]), True)[0])
+        got.append(out[b, hh * dh:(hh + 1) * dh])
+    assert_close(torch.stack(got), np.stack(want), "bf16", f"shared decode long context, {len(pairs)} heads")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_shared_equals_standard_decode(dtype):
     """A standard cache holding, for every token t, RoPE_t(B_K) (rotated by the
