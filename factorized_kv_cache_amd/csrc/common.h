@@ -44,12 +44,24 @@ struct RopeTable {
   double rev[kMaxRopePairs];
 };
 
-__device__ __forceinline__ void rope_cos_sin(const RopeTable& tab, int64_t pos, int pair, float& c, float& s) {
-  double turns = (double)pos * tab.rev[pair];
+// rev points at the table's frequencies; kernels whose lanes index it with
+// differing pairs keep a copy in LDS and pass that.
+__device__ __forceinline__ void rope_cos_sin(const double* rev, int64_t pos, int pair, float& c, float& s) {
+  double turns = (double)pos * rev[pair];
   turns -= rint(turns);
   const float t = (float)turns;
   s = __builtin_amdgcn_sinf(t);
   c = __builtin_amdgcn_cosf(t);
+}
+
+__device__ __forceinline__ void rope_cos_sin(const RopeTable& tab, int64_t pos, int pair, float& c, float& s) {
+  rope_cos_sin(tab.rev, pos, pair, c, s);
+}
+
+// Copies the first n_pairs frequencies into LDS; the caller's next barrier
+// makes them visible to the workgroup.
+__device__ __forceinline__ void rope_stage(const RopeTable& tab, int n_pairs, double* s_rev) {
+  for (int i = threadIdx.x; i < n_pairs && i < kMaxRopePairs; i += blockDim.x) s_rev[i] = tab.rev[i];
 }
 
 // Softmax runs in base 2: scores are pre-multiplied by log2(e).

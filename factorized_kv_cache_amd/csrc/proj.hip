@@ -16,12 +16,13 @@ namespace tpa {
 
 // Writes the pair of columns (n, n+1) of row m (n even); n+1 may be past N.
 template <typename T>
-__device__ __forceinline__ void proj_store_pair(const ProjArgs& a, int64_t m, int n, float v0, float v1) {
+__device__ __forceinline__ void proj_store_pair(const ProjArgs& a, const double* rev, int64_t m, int n, float v0,
+                                                float v1) {
   const int64_t s = m % a.S;
   const int64_t b = m / a.S;
   if (n < a.rot_cols) {
     float c, sn;
-    rope_cos_sin(a.rope, a.start_pos + s, (n % a.head_dim) >> 1, c, sn);
+    rope_cos_sin(rev, a.start_pos + s, (n % a.head_dim) >> 1, c, sn);
     const float r0 = v0 * c - v1 * sn;
     const float r1 = v0 * sn + v1 * c;
     v0 = r0;
@@ -39,10 +40,11 @@ __device__ __forceinline__ void proj_store_pair(const ProjArgs& a, int64_t m, in
 }
 
 // Writes columns n .. n+7 of row m = b*S + s (n a multiple of 8) from float32
-// values v, rotating the pairs below rot_cols.  With vec8 the piece lies in one
+// values v, rotating the pairs below rot_cols (frequencies from rev, in LDS).  With vec8 the piece lies in one
 // segment and one head and goes out as a single 16-byte store; otherwise each
 // column is placed on its own (columns past N are dropped).
-__device__ __forceinline__ void proj_store_piece8(const ProjArgs& a, uint32_t b, uint32_t s, int n, float* v) {
+__device__ __forceinline__ void proj_store_piece8(const ProjArgs& a, const double* rev, uint32_t b, uint32_t s, int n,
+                                                  float* v) {
   const int64_t pos = a.start_pos + s;
   if (a.vec8) {
     if (n < a.rot_cols) {
@@ -50,7 +52,7 @@ __device__ __forceinline__ void proj_store_piece8(const ProjArgs& a, uint32_t b,
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float c, sn;
-        rope_cos_sin(a.rope, pos, p0 + j, c, sn);
+        rope_cos_sin(rev, pos, p0 + j, c, sn);
         const float r0 = v[2 * j] * c - v[2 * j + 1] * sn;
         const float r1 = v[2 * j] * sn + v[2 * j + 1] * c;
         v[2 * j] = r0;
@@ -70,7 +72,7 @@ __device__ __forceinline__ void proj_store_piece8(const ProjArgs& a, uint32_t b,
     const int c0 = n + 2 * j;
     if (c0 < a.rot_cols) {
       float c, sn;
-      rope_cos_sin(a.rope, pos, (c0 % a.head_dim) >> 1, c, sn);
+      rope_cos_sin(rev, pos, (c0 % a.head_dim) >> 1, c, sn);
       const float r0 = v[2 * j] * c - v[2 * j + 1] * sn;
       const float r1 = v[2 * j] * sn + v[2 * j + 1] * c;
       v[2 * j] = r0;
@@ -94,6 +96,9 @@ __global__ void __launch_bounds__(256) proj_generic_kernel(ProjArgs a) {
   constexpr int BM = 64, BN = 64, BK = 16;
   __shared__ float xs[BK][BM + 4];
   __shared__ float ws[BK][BN + 4];
+  __shared__ double s_rev[kMaxRopePairs];
+  rope_stage(a.rope, a.head_dim >> 1, s_rev);
+  __syncthreads();
   const T* X = reinterpret_cast<const T*>(a.x);
   const T* W = reinterpret_cast<const T*>(a.w);
   const int tid = threadIdx.x;
@@ -134,7 +139,7 @@ __global__ void __launch_bounds__(256) proj_generic_kernel(ProjArgs a) {
 #pragma unroll
     for (int jp = 0; jp < 2; ++jp) {
       const int n = n0 + tx * 4 + 2 * jp;
-      if (n < a.N) proj_store_pair<T>(a, m, n, acc[i][2 * jp], acc[i][2 * jp + 1]);
+      if (n < a.N) proj_store_pair<T>(a, s_rev, m, n, acc[i][2 * jp], acc[i][2 * jp + 1]);
     }
   }
 }
@@ -153,6 +158,8 @@ constexpr int kSkinnyWaves = 8;
 template <int MT, int U>
 __global__ void __launch_bounds__(64 * kSkinnyWaves) proj_skinny_kernel(ProjArgs a) {
   __shared__ float red[kSkinnyWaves][16][16 * MT + 1];
+  __shared__ double s_rev[kMaxRopePairs];
+  rope_stage(a.rope, a.head_dim >> 1, s_rev);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int n0 = blockIdx.x * 16;
@@ -202,25 +209,28 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) proj_skinny_kernel(ProjArgs
     for (int q = 0; q < 8; ++q) v[q] += red[w][8 * (item & 1) + q][m];
   const uint32_t S = (uint32_t)a.S;
   const uint32_t b = (uint32_t)m / S;
-  proj_store_piece8(a, b, (uint32_t)m - b * S, n, v);
+  proj_store_piece8(a, s_rev, b, (uint32_t)m - b * S, n, v);
 }
 
 // ---------------------------------------------------------------------------
 // Many tokens (prefill): 128 x 128 output tile per workgroup, four waves of
-// 64 x 64, K staged through LDS 64 at a time with the next slab held in
-// registers while the current one is multiplied.
+// 64 x 64, K staged through two LDS slab buffers 64 at a time.  After a slab's
+// products each thread stores the next slab (held in registers) into the other
+// buffer and issues the loads of the one after, so one barrier per slab
+// separates the buffers' writers from their readers and the loads have a whole
+// slab of products to arrive.
 // ---------------------------------------------------------------------------
 constexpr int kPBM = 128, kPBN = 128, kPBK = 64, kPLDK = kPBK + 8;
+constexpr int kPSlab = (kPBM + kPBN) * kPLDK;   // bf16 elements of one slab buffer
 
 // The epilogue stages half of the fp32 tile (64 rows) at a time in the same
 // LDS, then each thread rotates and stores 8-column pieces.
 constexpr int kPLDT = kPBN + 4;
-static_assert(64 * kPLDT * 4 <= (kPBM + kPBN) * kPLDK * 2, "epilogue tile must fit the slab buffers");
+static_assert(64 * kPLDT * 4 <= 2 * kPSlab * 2, "epilogue tile must fit the slab buffers");
 
 __global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
-  __shared__ __align__(16) bf16_t lds[(kPBM + kPBN) * kPLDK];
-  bf16_t* xs = lds;
-  bf16_t* ws = lds + kPBM * kPLDK;
+  __shared__ __align__(16) bf16_t lds[2 * kPSlab];
+  __shared__ double s_rev[kMaxRopePairs];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
@@ -233,6 +243,7 @@ __global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
   const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
   const int mtile = (q / n_ntiles) * 8 + xcd, ntile = q % n_ntiles;
   if (mtile >= n_mtiles) return;
+  rope_stage(a.rope, a.head_dim >> 1, s_rev);   // visible after the first barrier
   const int64_t m0 = (int64_t)mtile * kPBM;
   const int n0 = ntile * kPBN;
   const int64_t M = a.M, K = a.K;
@@ -264,7 +275,7 @@ __global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int srow = tid >> 3, spc = tid & 7;   // row of piece q is srow + 32 q
-  for (int64_t k0 = 0; k0 < K; k0 += kPBK) {
+  auto store_slab = [&](bf16_t* xs, bf16_t* ws) __attribute__((always_inline)) {
     *reinterpret_cast<uint4*>(xs + (srow + 0) * kPLDK + spc * 8) = xr0;
     *reinterpret_cast<uint4*>(xs + (srow + 32) * kPLDK + spc * 8) = xr1;
     *reinterpret_cast<uint4*>(xs + (srow + 64) * kPLDK + spc * 8) = xr2;
@@ -273,9 +284,8 @@ __global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
     *reinterpret_cast<uint4*>(ws + (srow + 32) * kPLDK + spc * 8) = wr1;
     *reinterpret_cast<uint4*>(ws + (srow + 64) * kPLDK + spc * 8) = wr2;
     *reinterpret_cast<uint4*>(ws + (srow + 96) * kPLDK + spc * 8) = wr3;
-    __syncthreads();
-    // next slab (the last iteration reloads the final slab; it is never used)
-    const int64_t kn = k0 + kPBK < K ? k0 + kPBK : k0;
+  };
+  auto load_slab = [&](int64_t kn) __attribute__((always_inline)) {
     xr0 = *reinterpret_cast<const uint4*>(xsrc[0] + kn);
     xr1 = *reinterpret_cast<const uint4*>(xsrc[1] + kn);
     xr2 = *reinterpret_cast<const uint4*>(xsrc[2] + kn);
@@ -284,6 +294,15 @@ __global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
     wr1 = *reinterpret_cast<const uint4*>(wsrc[1] + kn);
     wr2 = *reinterpret_cast<const uint4*>(wsrc[2] + kn);
     wr3 = *reinterpret_cast<const uint4*>(wsrc[3] + kn);
+  };
+  // slab 0 into buffer 0; slab 1's loads go out
+  store_slab(lds, lds + kPBM * kPLDK);
+  load_slab(kPBK < K ? kPBK : 0);
+  __syncthreads();
+  int cur = 0;
+  for (int64_t k0 = 0; k0 < K; k0 += kPBK) {
+    const bf16_t* xs = lds + cur * kPSlab;
+    const bf16_t* ws = xs + kPBM * kPLDK;
 #pragma unroll
     for (int ks = 0; ks < kPBK / 32; ++ks) {
       bf16x8_t af[4], bfr[4];
@@ -297,7 +316,15 @@ __global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma_bf16(af[tm], bfr[tn], acc[tm][tn]);
     }
+    if (k0 + kPBK < K) {
+      // the other buffer was last read before the previous barrier
+      bf16_t* nx = lds + (cur ^ 1) * kPSlab;
+      store_slab(nx, nx + kPBM * kPLDK);
+      const int64_t k2 = k0 + 2 * kPBK;
+      load_slab(k2 < K ? k2 : k0 + kPBK);   // past the end: reload the last slab, never stored
+    }
     __syncthreads();
+    cur ^= 1;
   }
   // Tile rows wm*64 + tm*16 + 4*lg + i, columns wn*64 + tn*16 + li.
   float* tile = reinterpret_cast<float*>(lds);
@@ -326,7 +353,7 @@ __global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
         v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
         v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
         const uint32_t b = (uint32_t)m / S;
-        proj_store_piece8(a, b, (uint32_t)m - b * S, n, v);
+        proj_store_piece8(a, s_rev, b, (uint32_t)m - b * S, n, v);
       }
     }
     if (half == 0) __syncthreads();
