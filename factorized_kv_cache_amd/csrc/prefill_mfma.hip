@@ -62,6 +62,18 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 #define TPA_PF_LAZY 1
 #endif
 
+// max(a, b) for scores (finite or -inf): IEEE maximum, which propagates NaN
+// instead of quieting its operands, so the swapped-in value needs no extra
+// instruction.
+__device__ __forceinline__ float max_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+__device__ __forceinline__ float lane_group_max_nn(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = max_nn(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return max_nn(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int R>
 __device__ __forceinline__ void factor_combine(typename RankWordP<R>::type a, const uint4 (&b)[R], float (&out)[8]) {
   if constexpr (R == 1 || !TPA_PF_DOT2) {
@@ -225,8 +237,10 @@ __device__ __forceinline__ void store_rebuild(const RebuildRegs<DH, R>& g, bf16_
 }
 
 // One key block of the online-softmax attention for this wave's QT x 16 queries
-// (positions wpos0 ..), reading K and V^T of the block from LDS.
-template <int DH>
+// (positions wpos0 ..), reading K and V^T of the block from LDS.  EARLY_V:
+// read all of the block's V^T operands right after the score products, so the
+// softmax hides their latency (where the registers allow it).
+template <int DH, bool EARLY_V>
 __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t* vt_lds, int64_t k0, int64_t kend,
                                              int64_t wpos0, bool causal, int li, int lg,
                                              const bf16x8_t (&qop)[PrefillMfmaCfg<DH>::QT][PrefillMfmaCfg<DH>::KS],
@@ -250,6 +264,21 @@ __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t*
         for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16(kf[ks], qop[qt][ks], acc);
         sacc[kt][qt] = acc;
       }
+    }
+
+    // ---- V^T operands of the block
+    auto read_vt = [&](int dt, int kb) __attribute__((always_inline)) {
+      const bf16_t* vrow = vt_lds + (dt * 16 + li) * LDV + kb * 32 + 4 * lg;
+      const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+      return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
+    bf16x8_t vfe[EARLY_V ? DT + 1 : 1][KB];
+    if constexpr (EARLY_V) {
+#pragma unroll
+      for (int dt = 0; dt <= DT; ++dt)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) vfe[dt][kb] = read_vt(dt, kb);
     }
 
     // ---- mask (only where the block reaches past a query of this wave)
@@ -276,8 +305,8 @@ __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t*
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, sacc[kt][qt][i]);
-      bmax = lane_group_max(bmax);
+        for (int i = 0; i < 4; ++i) bmax = max_nn(bmax, sacc[kt][qt][i]);
+      bmax = lane_group_max_nn(bmax);
       const bool grow = bmax > m_run[qt] + (TPA_PF_LAZY ? C::kRescaleSlack : 0.f);
       if (__any(grow)) {
         const float m_new = grow ? bmax : m_run[qt];
@@ -302,10 +331,9 @@ __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t*
     for (int dt = 0; dt <= DT; ++dt) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const bf16_t* vrow = vt_lds + (dt * 16 + li) * LDV + kb * 32 + 4 * lg;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        const bf16x8_t vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        bf16x8_t vf;
+        if constexpr (EARLY_V) vf = vfe[dt][kb];
+        else vf = read_vt(dt, kb);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) oacc[qt][dt] = mfma_bf16(vf, pop[qt][kb], oacc[qt][dt]);
       }
@@ -411,7 +439,8 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
     const int64_t k0 = (int64_t)blk * BN;
-    attend_block<DH>(KS_BUF(blk & 1), VT_BUF(blk & 1), k0, kend, wpos0, causal, li, lg, qop, m_run, oacc);
+    attend_block<DH, DH == 64 && R <= 2>(KS_BUF(blk & 1), VT_BUF(blk & 1), k0, kend, wpos0, causal, li, lg, qop,
+                                          m_run, oacc);
     // rebuild the next block into the other buffer; with depth 1 its factors
     // were loaded a block ago and the block after it starts loading now
     if (blk + 1 < nblk) {
