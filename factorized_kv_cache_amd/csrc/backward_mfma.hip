@@ -154,6 +154,14 @@ __device__ __forceinline__ bf16x8_t tr_operand(const bf16_t* tr_row, int c0, int
 
 __device__ __forceinline__ bf16x8_t ld8(const bf16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
+// Makes the wave wait here for the loads of a value the tile loop reads.  The
+// memory counter is in order, so a wait for such a value inside the loop would
+// also hold every iteration until the next tile's staged loads had arrived.
+template <typename T>
+__device__ __forceinline__ void settle(const T& v) {
+  asm volatile("" ::"v"(v));
+}
+
 // v where ok, else zeros.
 __device__ __forceinline__ u32x4_t keep_if(bool ok, u32x4_t v) {
   const u32x4_t z = {0u, 0u, 0u, 0u};
@@ -213,9 +221,13 @@ struct BwdKvCfg {
   static_assert(ITEMS % 64 == 0 && ITEMS <= 256, "staging by whole waves");
 };
 
+// Rows past the last query are loaded clamped and zeroed only when stored, so
+// that nothing consumes the loads before the next tile's store: their latency
+// then overlaps a whole tile of products.
 struct KvStage {
   u32x4_t qh0, qh1, ql0, ql1, o0, o1;
   float lse, dv;
+  bool ok0, ok1, ok;
 };
 
 template <int DH>
@@ -229,20 +241,22 @@ __device__ __forceinline__ void kv_stage_load(KvStage& r, const AttnArgs& a, con
     const bool ok0 = s < a.S, ok1 = s + 1 < a.S;
     const int64_t off0 = ((b * a.S + (ok0 ? s : a.S - 1)) * a.h + hh) * (int64_t)DH + 8 * c;
     const int64_t off1 = ((b * a.S + (ok1 ? s + 1 : a.S - 1)) * a.h + hh) * (int64_t)DH + 8 * c;
-    r.qh0 = keep_if(ok0, ld16(g.q_hi + off0));
-    r.qh1 = keep_if(ok1, ld16(g.q_hi + off1));
-    r.ql0 = keep_if(ok0, ld16(g.q_lo + off0));
-    r.ql1 = keep_if(ok1, ld16(g.q_lo + off1));
-    r.o0 = keep_if(ok0, ld16(dO + off0));
-    r.o1 = keep_if(ok1, ld16(dO + off1));
+    r.qh0 = ld16(g.q_hi + off0);
+    r.qh1 = ld16(g.q_hi + off1);
+    r.ql0 = ld16(g.q_lo + off0);
+    r.ql1 = ld16(g.q_lo + off1);
+    r.o0 = ld16(dO + off0);
+    r.o1 = ld16(dO + off1);
+    r.ok0 = ok0;
+    r.ok1 = ok1;
   }
   if (threadIdx.x < C::BQ) {
     const int64_t s = s0 + threadIdx.x;
     const bool ok = s < a.S;
     const int64_t i = (b * a.S + (ok ? s : a.S - 1)) * a.h + hh;
-    const float l = g.lse[i], d = g.dvec[i];
-    r.lse = ok ? l : 0.f;
-    r.dv = ok ? d : 0.f;
+    r.lse = g.lse[i];
+    r.dv = g.dvec[i];
+    r.ok = ok;
   }
 }
 
@@ -251,18 +265,21 @@ __device__ __forceinline__ void kv_stage_store(const KvStage& r, bf16_t* buf) {
   using C = BwdKvCfg<DH>;
   if (threadIdx.x < C::ITEMS) {
     const int c = threadIdx.x % C::NP, p = threadIdx.x / C::NP;
-    put_rows(r.qh0, r.qh1, buf, C::LDR, 2 * p, 8 * c);
-    put_rows(r.ql0, r.ql1, buf + C::ROWT, C::LDR, 2 * p, 8 * c);
-    put_rows(r.o0, r.o1, buf + 2 * C::ROWT, C::LDR, 2 * p, 8 * c);
+    const u32x4_t qh0 = keep_if(r.ok0, r.qh0), qh1 = keep_if(r.ok1, r.qh1);
+    const u32x4_t ql0 = keep_if(r.ok0, r.ql0), ql1 = keep_if(r.ok1, r.ql1);
+    const u32x4_t o0 = keep_if(r.ok0, r.o0), o1 = keep_if(r.ok1, r.o1);
+    put_rows(qh0, qh1, buf, C::LDR, 2 * p, 8 * c);
+    put_rows(ql0, ql1, buf + C::ROWT, C::LDR, 2 * p, 8 * c);
+    put_rows(o0, o1, buf + 2 * C::ROWT, C::LDR, 2 * p, 8 * c);
     bf16_t* tr = buf + 3 * C::ROWT;
-    put_tr(r.qh0, r.qh1, tr, C::LDT, 2 * p, 8 * c);
-    put_tr(r.ql0, r.ql1, tr + C::TRT, C::LDT, 2 * p, 8 * c);
-    put_tr(r.o0, r.o1, tr + 2 * C::TRT, C::LDT, 2 * p, 8 * c);
+    put_tr(qh0, qh1, tr, C::LDT, 2 * p, 8 * c);
+    put_tr(ql0, ql1, tr + C::TRT, C::LDT, 2 * p, 8 * c);
+    put_tr(o0, o1, tr + 2 * C::TRT, C::LDT, 2 * p, 8 * c);
   }
   if (threadIdx.x < C::BQ) {
     float* st = reinterpret_cast<float*>(buf + 3 * C::ROWT + 3 * C::TRT);
-    st[threadIdx.x] = r.lse;
-    st[C::BQ + threadIdx.x] = r.dv;
+    st[threadIdx.x] = r.ok ? r.lse : 0.f;
+    st[C::BQ + threadIdx.x] = r.ok ? r.dv : 0.f;
   }
 }
 
@@ -315,6 +332,14 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_mfma_kernel(AttnArgs a, BwdAr
   const float inv_rv = 1.f / (float)a.rv;
 
   kv_stage_store<DH>(sr, lds);
+#pragma unroll
+  for (int kt = 0; kt < KW; ++kt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      settle(kh[kt][ks]);
+      settle(kl[kt][ks]);
+      settle(vo[kt][ks]);
+    }
   if (ntiles > 1) kv_stage_load<DH>(sr, a, g, b, hh, s_lo + BQ);
   __syncthreads();
   for (int tile = 0; tile < ntiles; ++tile) {
@@ -493,6 +518,10 @@ __global__ void __launch_bounds__(256, 2) bwd_query_mfma_kernel(AttnArgs a, BwdA
   using C = BwdQCfg<DH, STATS>;
   constexpr int QT = C::QT, BM = C::BM, BN = C::BN, KT = C::KT, KS = C::KS, DT = C::DT;
   constexpr int LDR = C::LDR, LDT = C::LDT;
+  // dQ at d_h = 64 reads its k^T operands ahead of the dS step (221 registers);
+  // in the statistics pass the extra registers would cost the third wave per
+  // SIMD, which is worth more there than the early reads
+  constexpr bool kEarlyT = DH == 64 && !STATS;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16_t* const lds = reinterpret_cast<bf16_t*>(smem);
   const int lane = threadIdx.x & 63;
@@ -558,6 +587,19 @@ __global__ void __launch_bounds__(256, 2) bwd_query_mfma_kernel(AttnArgs a, BwdA
   const int64_t wpos0 = a.start_pos + sw0;   // first position of this wave's queries
 
   q_stage_store<DH, STATS>(sr, lds);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      settle(qh[qt][ks]);
+      settle(ql[qt][ks]);
+      if constexpr (!STATS) settle(dop[qt][ks]);
+    }
+    if constexpr (!STATS) {
+      settle(lse[qt]);
+      settle(dd[qt]);
+    }
+  }
   if (nblk > 1) q_stage_load<DH, STATS>(sr, g, b, hh, h, n_keys, BN);
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
@@ -591,6 +633,19 @@ __global__ void __launch_bounds__(256, 2) bwd_query_mfma_kernel(AttnArgs a, BwdA
           pacc[kt][qt] = p;
         }
       }
+      // the transposed operands of the second product (statistics: v^T with its
+      // ones row; dQ: k^T hi, lo), read now so the elementwise step hides their
+      // latency
+      constexpr int NE = !kEarlyT ? 1 : STATS ? DT + 1 : 2 * DT;
+      bf16x8_t tre[NE];
+      if constexpr (kEarlyT) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          const int dt = STATS ? e : e >> 1;
+          const bf16_t* base = STATS ? buf + 2 * C::ROWT : buf + 3 * C::ROWT + ((e & 1) ? C::TRT : 0);
+          tre[e] = tr_operand(base + (16 * dt + li) * LDT, 0, lg);
+        }
+      }
       const bool need_mask = (causal && k0 + BN - 1 > wpos0) || (k0 + BN > kend);
       if (need_mask) {
 #pragma unroll
@@ -613,8 +668,8 @@ __global__ void __launch_bounds__(256, 2) bwd_query_mfma_kernel(AttnArgs a, BwdA
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, sacc[kt][qt][i]);
-          bmax = lane_group_max(bmax);
+            for (int i = 0; i < 4; ++i) bmax = max_nn(bmax, sacc[kt][qt][i]);
+          bmax = lane_group_max_nn(bmax);
           const bool grow = bmax > m_run[qt] + C::kRescaleSlack;
           if (__any(grow)) {
             const float m_new = grow ? bmax : m_run[qt];
@@ -635,7 +690,8 @@ __global__ void __launch_bounds__(256, 2) bwd_query_mfma_kernel(AttnArgs a, BwdA
           const bf16_t* vt = buf + 2 * C::ROWT;
 #pragma unroll
           for (int dt = 0; dt <= DT; ++dt)
-            acc[qt][dt] = mfma_bf16(tr_operand(vt + (16 * dt + li) * LDT, 0, lg), pop, acc[qt][dt]);
+            acc[qt][dt] = mfma_bf16(kEarlyT ? tre[kEarlyT ? dt : 0] : tr_operand(vt + (16 * dt + li) * LDT, 0, lg),
+                                    pop, acc[qt][dt]);
         }
       } else {
         // dS^T = P^T (dP^T - D) as hi + lo; dQ^T += k^T dS^T (k^ as hi + lo)
@@ -654,8 +710,9 @@ __global__ void __launch_bounds__(256, 2) bwd_query_mfma_kernel(AttnArgs a, BwdA
         const bf16_t* kt_hi = buf + 3 * C::ROWT;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const bf16x8_t ka = tr_operand(kt_hi + (16 * dt + li) * LDT, 0, lg);
-          const bf16x8_t kb = tr_operand(kt_hi + C::TRT + (16 * dt + li) * LDT, 0, lg);
+          const bf16x8_t ka = kEarlyT ? tre[kEarlyT ? 2 * dt : 0] : tr_operand(kt_hi + (16 * dt + li) * LDT, 0, lg);
+          const bf16x8_t kb =
+              kEarlyT ? tre[kEarlyT ? 2 * dt + 1 : 0] : tr_operand(kt_hi + C::TRT + (16 * dt + li) * LDT, 0, lg);
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt) {
             acc[qt][dt] = mfma_bf16(ka, dsh[qt], acc[qt][dt]);

@@ -42,6 +42,18 @@ __device__ __forceinline__ float lane_group_max(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// max(a, b) for scores (finite or -inf): IEEE maximum, which propagates NaN
+// instead of quieting its operands, so a swapped-in value needs no extra
+// instruction.
+__device__ __forceinline__ float max_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+__device__ __forceinline__ float lane_group_max_nn(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = max_nn(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return max_nn(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float lane_group_sum(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);

@@ -62,18 +62,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 #define TPA_PF_LAZY 1
 #endif
 
-// max(a, b) for scores (finite or -inf): IEEE maximum, which propagates NaN
-// instead of quieting its operands, so the swapped-in value needs no extra
-// instruction.
-__device__ __forceinline__ float max_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-
-__device__ __forceinline__ float lane_group_max_nn(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = max_nn(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return max_nn(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 template <int R>
 __device__ __forceinline__ void factor_combine(typename RankWordP<R>::type a, const uint4 (&b)[R], float (&out)[8]) {
   if constexpr (R == 1 || !TPA_PF_DOT2) {
