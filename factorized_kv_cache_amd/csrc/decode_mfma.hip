@@ -40,9 +40,11 @@
 namespace tpa {
 
 // Narrowing to bf16 (round to nearest, ties to even, NaNs kept quiet) with
-// integer operations.  This kernel is bound by HBM, not by its VALU; with the
-// packed hardware conversion the compiler schedules the d_h = 128 value loop
-// past the two-waves-per-SIMD register budget (spills), with this form it fits.
+// integer operations, for the d_h = 128 value operand: with the packed
+// hardware conversion the compiler schedules that value loop past the
+// two-waves-per-SIMD register budget (spills), with this form it fits.  At
+// d_h = 64 the hardware conversion fits and is cheaper (two values per
+// instruction, no per-value branch).
 __device__ __forceinline__ uint16_t bf16_rne_int(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
@@ -237,10 +239,10 @@ __device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf1
         for (int rr = 0; rr < R; ++rr) v = fmaf(ak[rr], sacc[st][ht][k * R + rr], v);
         const bool valid = tb + (st * 16 + lg * 4) / R + k <= last;
         s[st][k] = valid ? v : -INFINITY;
-        bmax = fmaxf(bmax, s[st][k]);
+        bmax = max_nn(bmax, s[st][k]);
       }
-    bmax = lane_group_max(bmax);
-    const float m_new = fmaxf(m_run[ht], bmax);
+    bmax = lane_group_max_nn(bmax);
+    const float m_new = max_nn(m_run[ht], bmax);
     const float alpha = fast_exp2(m_run[ht] - m_new);
     m_run[ht] = m_new;
     float psum = 0.f;
@@ -255,7 +257,8 @@ __device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf1
         for (int rr = 0; rr < R; ++rr) cv[st * 4 + k * R + rr] = p * av[st][k * R + rr];
       }
     l_run[ht] = l_run[ht] * alpha + psum;
-    cop[ht] = pack8_int(cv);
+    if constexpr (DH == 64) cop[ht] = pack8(cv);
+    else cop[ht] = pack8_int(cv);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[ht][dt] *= alpha;
   }
