@@ -212,6 +212,7 @@ __global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(AttnArg
   }
 }
 
+bool decode_mfma_shape_ok(int dtype, const AttnArgs& a);
 bool decode_mfma_supported(int dtype, const AttnArgs& a);
 int64_t decode_mfma_wave_tokens(const AttnArgs& a);
 hipError_t launch_decode_mfma(const AttnArgs& a, int64_t ctx_len, int64_t chunk, int64_t n_chunks, float* ws,
@@ -261,13 +262,13 @@ static size_t partial_bytes(const DecodePlan& p, const AttnArgs& a) {
   return (size_t)a.n_batch * (size_t)p.n_chunks * (size_t)a.h * (size_t)(a.d_h + 2) * sizeof(float);
 }
 
-// Workspace: partials for either plan, so the size does not depend on pointer
-// alignment.
-size_t decode_workspace_bytes(const DecodePlan& p, const AttnArgs& a) {
-  (void)p;
+// Workspace: partials for either plan the shape allows, so the size does not
+// depend on pointer alignment.  (The matrix-core plan exists only for the
+// shapes that kernel takes: its block of tokens per wave is 4 * (32 / R_K).)
+size_t decode_workspace_bytes(int dtype, const AttnArgs& a) {
   const int64_t ctx_len = a.start_pos + 1;
   const size_t n = partial_bytes(plan_generic(ctx_len), a);
-  const size_t m = partial_bytes(plan_mfma(a, ctx_len), a);
+  const size_t m = decode_mfma_shape_ok(dtype, a) ? partial_bytes(plan_mfma(a, ctx_len), a) : 0;
   return n > m ? n : m;
 }
 

@@ -481,7 +481,9 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
 
 }
 
-bool decode_mfma_supported(int dtype, const AttnArgs& a) {
+// The shape conditions of the matrix-core decode: everything but the operand
+// alignment, which depends on the caller's pointers.
+bool decode_mfma_shape_ok(int dtype, const AttnArgs& a) {
   if (dtype != kBF16) return false;
   if (a.rk != a.rv || !(a.rk == 1 || a.rk == 2 || a.rk == 4)) return false;
   if (!(a.d_h == 64 || a.d_h == 128)) return false;
@@ -491,6 +493,11 @@ bool decode_mfma_supported(int dtype, const AttnArgs& a) {
   const size_t qbytes = (a.rq ? (size_t)a.rq * (a.h + a.d_h) : (size_t)a.h * a.d_h) * sizeof(bf16_t);
   if (qbytes > kDecodeMfmaQueryLds) return false;
   if (a.pm.block_table && a.pm.page_tokens % 32) return false;   // pages of whole value blocks
+  return true;
+}
+
+bool decode_mfma_supported(int dtype, const AttnArgs& a) {
+  if (!decode_mfma_shape_ok(dtype, a)) return false;
   const void* ptrs[5] = {a.b_q, a.c_ak, a.c_bk, a.c_av, a.c_bv};
   for (int i = 0; i < 5; ++i)
     if (((uintptr_t)ptrs[i]) % 16) return false;

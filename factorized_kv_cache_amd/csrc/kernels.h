@@ -140,7 +140,7 @@ struct DecodePlan {
   int kernel;            // 0 = general VALU kernel, 1 = MFMA kernel
 };
 DecodePlan plan_decode(int dtype, const AttnArgs& a, int64_t ctx_len);
-size_t decode_workspace_bytes(const DecodePlan& p, const AttnArgs& a);
+size_t decode_workspace_bytes(int dtype, const AttnArgs& a);
 hipError_t launch_decode(int dtype, const AttnArgs& a, int64_t ctx_len, const DecodePlan& p, void* ws,
                          hipStream_t st);
 

@@ -339,7 +339,7 @@ size_t tpa_decode_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t ct
   memset(&c, 0, sizeof(c));
   c.max_seq = ctx_len;
   tpa::AttnArgs a = attn_args(d, &q, 1, &c, n_batch, 1, ctx_len - 1, 1, nullptr);
-  return tpa::decode_workspace_bytes(tpa::plan_decode(d->dtype, a, ctx_len), a);
+  return tpa::decode_workspace_bytes(d->dtype, a);
 }
 
 tpa_status tpa_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
@@ -360,7 +360,7 @@ tpa_status tpa_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_ca
   if ((st = resolve_stride(q->q_batch_stride, 1, "q_batch_stride", &qs)) != TPA_OK) return st;
   tpa::AttnArgs a = attn_args(d, q, qs, c, n_batch, 1, ctx_len - 1, 1, out);
   const tpa::DecodePlan p = tpa::plan_decode(d->dtype, a, ctx_len);
-  const size_t need = tpa::decode_workspace_bytes(p, a);
+  const size_t need = tpa::decode_workspace_bytes(d->dtype, a);
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(TPA_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
                 workspace ? "" : ", NULL");
@@ -510,7 +510,7 @@ tpa_status tpa_paged_decode_attn(const tpa_dims* d, const tpa_factors* q, const 
   a.pm = page_map(c);
   a.ctx_lens = ctx_lens;
   const tpa::DecodePlan p = tpa::plan_decode(d->dtype, a, max_ctx_len);
-  const size_t need = tpa::decode_workspace_bytes(p, a);
+  const size_t need = tpa::decode_workspace_bytes(d->dtype, a);
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(TPA_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
                 workspace ? "" : ", NULL");

@@ -82,7 +82,9 @@ typedef enum { TPA_F32 = 0, TPA_BF16 = 1 } tpa_dtype;
  * rank; key and value ranks are separate, as in its K_t and V_t equations).
  * Limits: d_model >= 1; 1 <= n_heads <= 256; head_dim even, 2..256;
  * rank_k, rank_v in 1..64; rank_q in 0..64, 0 selecting TPA-KVonly (Q is a
- * plain per-head projection, rotated like the key factors). */
+ * plain per-head projection, rotated like the key factors).  Dims outside
+ * these limits give TPA_ERR_INVALID; n_heads * head_dim above 8192 (one
+ * token's heads held by one workgroup) gives TPA_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t d_model;
   int32_t n_heads;   /* h */

@@ -214,3 +214,26 @@ def test_status_strings():
     for s in range(6):
         assert lib.tpa_status_string(s).decode() == T._STATUS[s]
     assert lib.tpa_status_string(99).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("kw", [
+    dict(n_heads=32, head_dim=256, rank_q=64, rank_k=64, rank_v=64),
+    dict(n_heads=256, head_dim=32),
+    dict(n_heads=1, head_dim=2, rank_q=1, rank_k=1, rank_v=1),
+    dict(rank_k=33, rank_v=5),
+])
+def test_workspace_sizes_at_the_limits(kw, dtype):
+    """Workspace sizing is host arithmetic only: at the dims limits every size
+    is positive and nothing faults (the matrix-core decode plan, whose block is
+    4 * (32 / R_K) tokens, exists only for the ranks that kernel takes).  Where
+    only the general decode applies, the size is its partials exactly: one
+    256-token chunk per sequence here, h * (d_h + 2) floats each."""
+    lib = T.library()
+    d = dims(dtype=dtype, **kw)
+    h, dh = d.n_heads, d.head_dim
+    for fn in ("tpa_decode_workspace_bytes", "tpa_paged_decode_workspace_bytes", "tpa_shared_decode_workspace_bytes"):
+        assert getattr(lib, fn)(ctypes.byref(d), 3, 21) > 0, fn
+    assert lib.tpa_prefill_backward_workspace_bytes(ctypes.byref(d), 2, 40, 5) > 0
+    if dtype == 0 or d.rank_k > 4:
+        assert lib.tpa_decode_workspace_bytes(ctypes.byref(d), 3, 21) == 3 * h * (dh + 2) * 4

@@ -83,6 +83,11 @@ PROJ_CASES = [
     (16, 1, 1024, 16, 64, 6, 2, 2, 4096),       # decode batch: few-token kernel
     (40, 1, 1536, 24, 64, 0, 4, 4, 16384),
     (3, 150, 1536, 24, 64, 0, 4, 4, 0),          # KV-only, many tokens
+    # the dims limits: every rank and head_dim at their maximum; the most heads
+    # (n_heads * head_dim = 8192); the smallest dims
+    (1, 5, 64, 32, 256, 64, 64, 64, 7),
+    (2, 9, 512, 256, 32, 2, 2, 2, 3),
+    (3, 4, 4, 1, 2, 1, 1, 1, 0),
 ]
 
 
@@ -155,6 +160,13 @@ DECODE_CASES = [
     ("h64_r4_bf16", "bf16", 2, 333, 1024, 64, 64, 2, 4, 4, 1.0),     # four head tiles
     ("h20_dh128_bf16", "bf16", 1, 999, 2560, 20, 128, 2, 2, 2, 1.0),
     ("h10_r2_bf16", "bf16", 2, 400, 640, 10, 64, 3, 2, 2, 1.0),
+    # the dims limits (see the projection cases); std chosen so the scores are O(1)
+    ("limit_dh256_r64_fp32", "f32", 1, 21, 128, 32, 256, 64, 64, 64, 3.0),
+    ("limit_dh256_r64_bf16", "bf16", 1, 21, 128, 32, 256, 64, 64, 64, 3.0),
+    ("limit_h256_fp32", "f32", 2, 37, 512, 256, 32, 2, 2, 2, 1.5),
+    ("limit_h256_bf16", "bf16", 2, 37, 512, 256, 32, 2, 2, 2, 1.5),
+    ("limit_min_dims_fp32", "f32", 3, 9, 4, 1, 2, 1, 1, 1, 1.5),
+    ("limit_min_dims_bf16", "bf16", 3, 9, 4, 1, 2, 1, 1, 1, 1.5),
 ]
 
 
@@ -195,6 +207,11 @@ PREFILL_CASES = [
     ("dh256_f32", "f32", 1, 40, 0, True, 64, 2, 256, 2, 2, 2, 0.5),
     ("odd_heads_r1_bf16", "bf16", 2, 200, 7, True, 320, 5, 64, 3, 1, 1, 1.0),
     ("odd_heads_dh128_bf16", "bf16", 1, 150, 0, True, 384, 3, 128, 2, 2, 2, 1.0),
+    # the dims limits
+    ("limit_dh256_r64_fp32", "f32", 1, 24, 3, True, 128, 32, 256, 64, 64, 64, 3.0),
+    ("limit_dh256_r64_bf16", "bf16", 1, 24, 3, True, 128, 32, 256, 64, 64, 64, 3.0),
+    ("limit_h256_bf16", "bf16", 1, 40, 5, True, 512, 256, 32, 2, 2, 2, 1.5),
+    ("limit_min_dims_fp32", "f32", 2, 17, 2, True, 4, 1, 2, 1, 1, 1, 1.5),
 ]
 
 
