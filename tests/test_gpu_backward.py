@@ -43,6 +43,11 @@ BACKWARD_CASES = [
     ("bf16_mfma_mqa_r1", "bf16", 2, 129, 0, True, 256, 8, 64, 2, 1, 1, 1.2),
     # a query block that ends exactly on a tile edge
     ("bf16_mfma_aligned", "bf16", 1, 256, 128, True, 128, 2, 64, 2, 2, 2, 1.0),
+    # the dims limits: d_h 256 with every rank at 64; 256 heads (n_heads * d_h
+    # = 8192); the smallest dims
+    ("limit_f32_dh256_r64", "f32", 1, 12, 3, True, 128, 32, 256, 64, 64, 64, 3.0),
+    ("limit_bf16_h256", "bf16", 1, 20, 2, True, 512, 256, 32, 2, 2, 2, 1.5),
+    ("limit_f32_min_dims", "f32", 2, 9, 1, True, 4, 1, 2, 1, 1, 1, 1.5),
 ]
 
 
