@@ -35,6 +35,18 @@ tpa_status hip_status(hipError_t e, const char* what) {
 
 constexpr int64_t kMaxTokens = (int64_t)1 << 31;
 
+// n_batch * seq_len < 2^31 for positive arguments, without overflowing int64
+// on the way (each factor is bounded first).
+static bool token_count_ok(int64_t n_batch, int64_t seq_len) {
+  return n_batch < kMaxTokens && seq_len < kMaxTokens && n_batch * seq_len < kMaxTokens;
+}
+
+// 0 <= start_pos and start_pos + seq_len < 2^31 for 0 < seq_len < 2^31,
+// without forming a sum that could overflow.
+static bool positions_ok(int64_t start_pos, int64_t seq_len) {
+  return start_pos >= 0 && start_pos < kMaxTokens - seq_len;
+}
+
 tpa_status check_dims(const tpa_dims* d) {
   if (!d) return fail(TPA_ERR_INVALID_ARGUMENT, "dims is NULL");
   if (d->d_model < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "d_model must be >= 1 (got %d)", d->d_model);
@@ -197,9 +209,8 @@ tpa_status tpa_factor_proj(const tpa_dims* d, const void* x, int64_t n_batch, in
   if (!out->a_k || !out->b_k || !out->a_v || !out->b_v)
     return fail(TPA_ERR_INVALID_ARGUMENT, "a key/value output tensor is NULL");
   if (n_batch < 1 || seq_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and seq_len must be >= 1");
-  if (n_batch >= kMaxTokens || seq_len >= kMaxTokens || n_batch * seq_len >= kMaxTokens)
-    return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
-  if (start_pos < 0 || start_pos + seq_len >= kMaxTokens)
+  if (!token_count_ok(n_batch, seq_len)) return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
+  if (!positions_ok(start_pos, seq_len))
     return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos must be in 0 .. 2^31 - seq_len");
   int64_t qs, kvs;
   if ((st = resolve_stride(out->q_batch_stride, seq_len, "q_batch_stride", &qs)) != TPA_OK) return st;
@@ -257,8 +268,8 @@ tpa_status tpa_rope_b(const tpa_dims* d, void* b, int64_t n_batch, int64_t seq_l
   if (!b) return fail(TPA_ERR_INVALID_ARGUMENT, "b is NULL");
   if (n_batch < 1 || seq_len < 1 || rows < 1)
     return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch, seq_len and rows must be >= 1");
-  if (n_batch * seq_len >= kMaxTokens) return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
-  if (start_pos < 0 || start_pos + seq_len >= kMaxTokens)
+  if (!token_count_ok(n_batch, seq_len)) return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
+  if (!positions_ok(start_pos, seq_len))
     return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos must be in 0 .. 2^31 - seq_len");
   tpa::RopeArgs a;
   memset(&a, 0, sizeof(a));
@@ -285,8 +296,8 @@ tpa_status tpa_cache_append(const tpa_dims* d, const tpa_cache* c, const tpa_fac
     return fail(TPA_ERR_CAPACITY, "n_batch %lld exceeds max_batch %lld", (long long)n_batch,
                 (long long)c->max_batch);
   if (seq_len > c->max_seq || start_pos > c->max_seq - seq_len)
-    return fail(TPA_ERR_CAPACITY, "start_pos + seq_len (%lld) exceeds max_seq %lld",
-                (long long)(start_pos + seq_len), (long long)c->max_seq);
+    return fail(TPA_ERR_CAPACITY, "start_pos %lld + seq_len %lld exceeds max_seq %lld", (long long)start_pos,
+                (long long)seq_len, (long long)c->max_seq);
   int64_t kvs;
   if ((st = resolve_stride(kv->kv_batch_stride, seq_len, "kv_batch_stride", &kvs)) != TPA_OK) return st;
   const int64_t es = (int64_t)elem_size(d);
@@ -323,8 +334,8 @@ tpa_status tpa_prefill_attn(const tpa_dims* d, const tpa_factors* q, const tpa_c
     return fail(TPA_ERR_CAPACITY, "n_batch %lld exceeds max_batch %lld", (long long)n_batch,
                 (long long)c->max_batch);
   if (seq_len > c->max_seq || start_pos > c->max_seq - seq_len)
-    return fail(TPA_ERR_CAPACITY, "start_pos + seq_len (%lld) exceeds max_seq %lld",
-                (long long)(start_pos + seq_len), (long long)c->max_seq);
+    return fail(TPA_ERR_CAPACITY, "start_pos %lld + seq_len %lld exceeds max_seq %lld", (long long)start_pos,
+                (long long)seq_len, (long long)c->max_seq);
   int64_t qs;
   if ((st = resolve_stride(q->q_batch_stride, seq_len, "q_batch_stride", &qs)) != TPA_OK) return st;
   tpa::AttnArgs a = attn_args(d, q, qs, c, n_batch, seq_len, start_pos, causal, out);
@@ -333,6 +344,7 @@ tpa_status tpa_prefill_attn(const tpa_dims* d, const tpa_factors* q, const tpa_c
 
 size_t tpa_decode_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t ctx_len) {
   if (check_dims(d) != TPA_OK || n_batch < 1 || ctx_len < 1) return 0;
+  if (n_batch > 65535 || ctx_len >= kMaxTokens) return 0;   // sizes the decode call rejects
   tpa_factors q;
   memset(&q, 0, sizeof(q));
   tpa_cache c;
@@ -371,6 +383,8 @@ tpa_status tpa_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_ca
 size_t tpa_prefill_backward_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t seq_len,
                                             int64_t start_pos) {
   if (check_dims(d) != TPA_OK || n_batch < 1 || seq_len < 1 || start_pos < 0) return 0;
+  // sizes the backward call rejects
+  if (n_batch > 65535 || !token_count_ok(n_batch, seq_len) || !positions_ok(start_pos, seq_len)) return 0;
   tpa_factors q;
   memset(&q, 0, sizeof(q));
   tpa_cache c;
@@ -398,7 +412,8 @@ tpa_status tpa_prefill_attn_backward(const tpa_dims* d, const tpa_factors* q, co
   if (n_batch > c->max_batch || n_batch > dkv->max_batch)
     return fail(TPA_ERR_CAPACITY, "n_batch %lld exceeds max_batch", (long long)n_batch);
   if (seq_len > c->max_seq || start_pos > c->max_seq - seq_len || start_pos + seq_len > dkv->max_seq)
-    return fail(TPA_ERR_CAPACITY, "start_pos + seq_len (%lld) exceeds max_seq", (long long)(start_pos + seq_len));
+    return fail(TPA_ERR_CAPACITY, "start_pos %lld + seq_len %lld exceeds max_seq", (long long)start_pos,
+                (long long)seq_len);
   if ((start_pos + seq_len) + seq_len >= kMaxTokens) return fail(TPA_ERR_UNSUPPORTED, "sequence too long");
   int64_t qs, dqs;
   if ((st = resolve_stride(q->q_batch_stride, seq_len, "q_batch_stride", &qs)) != TPA_OK) return st;
@@ -430,8 +445,8 @@ tpa_status tpa_rope_b_backward(const tpa_dims* d, float* g, int64_t n_batch, int
   if (!g) return fail(TPA_ERR_INVALID_ARGUMENT, "g is NULL");
   if (n_batch < 1 || seq_len < 1 || rows < 1)
     return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch, seq_len and rows must be >= 1");
-  if (n_batch * seq_len >= kMaxTokens) return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
-  if (start_pos < 0 || start_pos + seq_len >= kMaxTokens)
+  if (!token_count_ok(n_batch, seq_len)) return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
+  if (!positions_ok(start_pos, seq_len))
     return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos must be in 0 .. 2^31 - seq_len");
   tpa::RopeArgs a;
   memset(&a, 0, sizeof(a));
@@ -454,7 +469,7 @@ tpa_status tpa_paged_cache_append(const tpa_dims* d, const tpa_paged_cache* c, c
     return fail(TPA_ERR_INVALID_ARGUMENT, "a key/value factor tensor is NULL");
   if (!start_pos) return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos is NULL");
   if (n_batch < 1 || seq_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and seq_len must be >= 1");
-  if (n_batch * seq_len >= kMaxTokens) return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
+  if (!token_count_ok(n_batch, seq_len)) return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
   if ((st = check_paged(c, n_batch)) != TPA_OK) return st;
   int64_t kvs;
   if ((st = resolve_stride(kv->kv_batch_stride, seq_len, "kv_batch_stride", &kvs)) != TPA_OK) return st;
@@ -530,8 +545,8 @@ tpa_status tpa_shared_cache_append(const tpa_dims* d, const tpa_shared_cache* c,
     return fail(TPA_ERR_CAPACITY, "n_batch %lld exceeds max_batch %lld", (long long)n_batch,
                 (long long)c->max_batch);
   if (seq_len > c->max_seq || start_pos > c->max_seq - seq_len)
-    return fail(TPA_ERR_CAPACITY, "start_pos + seq_len (%lld) exceeds max_seq %lld",
-                (long long)(start_pos + seq_len), (long long)c->max_seq);
+    return fail(TPA_ERR_CAPACITY, "start_pos %lld + seq_len %lld exceeds max_seq %lld", (long long)start_pos,
+                (long long)seq_len, (long long)c->max_seq);
   int64_t kvs;
   if ((st = resolve_stride(kv->kv_batch_stride, seq_len, "kv_batch_stride", &kvs)) != TPA_OK) return st;
   const int64_t es = (int64_t)elem_size(d);
@@ -555,6 +570,7 @@ tpa_status tpa_shared_cache_append(const tpa_dims* d, const tpa_shared_cache* c,
 
 size_t tpa_shared_decode_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t ctx_len) {
   if (check_dims(d) != TPA_OK || n_batch < 1 || ctx_len < 1) return 0;
+  if (n_batch > 65535 || ctx_len >= kMaxTokens) return 0;   // sizes the decode call rejects
   tpa_factors q;
   memset(&q, 0, sizeof(q));
   tpa_cache c;
@@ -597,7 +613,9 @@ tpa_status tpa_shared_decode_attn(const tpa_dims* d, const tpa_factors* q, const
                     "tpa_shared_decode_attn");
 }
 
-const char* tpa_status_string(tpa_status s) {
+// Takes an int: a C caller may pass any int, and a value outside the enum's
+// range must not be loaded as a tpa_status in C++.
+const char* tpa_status_string(int s) {
   switch (s) {
     case TPA_OK: return "ok";
     case TPA_ERR_INVALID_ARGUMENT: return "invalid argument";

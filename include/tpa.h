@@ -180,7 +180,9 @@ tpa_status tpa_prefill_attn(const tpa_dims* dims, const tpa_factors* q, const tp
                             int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
                             void* stream);
 
-/* Bytes of device workspace tpa_decode_attn needs for this batch and context. */
+/* Bytes of device workspace tpa_decode_attn needs for this batch and context;
+ * 0 for dims or sizes that call rejects (n_batch outside 1..65535, ctx_len
+ * outside 1 .. 2^31 - 1). */
 size_t tpa_decode_workspace_bytes(const tpa_dims* dims, int64_t n_batch, int64_t ctx_len);
 
 /* Decode attention: one new query per sequence at position ctx_len - 1 over the
@@ -215,7 +217,9 @@ tpa_status tpa_decode_attn(const tpa_dims* dims, const tpa_factors* q, const tpa
  * and T = start_pos+S: float32 dQ, dK, dV (N*(S + 2T)*4), the bf16 operands of
  * the matrix-core kernels (N*(2S + 3T)*2) and two float32 statistics per
  * query and head (2*B*S*h*4).  The base address must be 16-byte aligned for
- * the matrix-core path (otherwise the general kernels run). */
+ * the matrix-core path (otherwise the general kernels run).  0 for dims or
+ * sizes the backward rejects (n_batch above 65535, B*S or start_pos + S of
+ * 2^31 or more). */
 size_t tpa_prefill_backward_workspace_bytes(const tpa_dims* dims, int64_t n_batch, int64_t seq_len,
                                             int64_t start_pos);
 
@@ -340,7 +344,8 @@ tpa_status tpa_shared_cache_append(const tpa_dims* dims, const tpa_shared_cache*
                                    int64_t n_batch, int64_t seq_len, int64_t start_pos, void* stream);
 
 /* Device workspace for tpa_shared_decode_attn: float32 partials
- * (max, sum, R_V weights) per sequence, key chunk and head. */
+ * (max, sum, R_V weights) per sequence, key chunk and head; 0 for dims or
+ * sizes as tpa_decode_workspace_bytes. */
 size_t tpa_shared_decode_workspace_bytes(const tpa_dims* dims, int64_t n_batch, int64_t ctx_len);
 
 /* Decode attention over a shared-basis cache: each sequence's new query
@@ -362,8 +367,9 @@ tpa_status tpa_shared_decode_attn(const tpa_dims* dims, const tpa_factors* q, co
                                   int64_t n_batch, int64_t ctx_len, void* out, void* workspace, size_t ws_bytes,
                                   void* stream);
 
-/* Static text for a status code. */
-const char* tpa_status_string(tpa_status status);
+/* Static text for a status code (a tpa_status value; any other int gives
+ * "unknown status"). */
+const char* tpa_status_string(int status);
 
 /* Description of the last error returned on the calling thread ("" if none). */
 const char* tpa_last_error(void);

@@ -237,3 +237,25 @@ def test_workspace_sizes_at_the_limits(kw, dtype):
     assert lib.tpa_prefill_backward_workspace_bytes(ctypes.byref(d), 2, 40, 5) > 0
     if dtype == 0 or d.rank_k > 4:
         assert lib.tpa_decode_workspace_bytes(ctypes.byref(d), 3, 21) == 3 * h * (dh + 2) * 4
+
+
+def test_sizes_far_past_the_limits():
+    """Workspace sizes for batches and lengths the calls reject are 0, and the
+    calls' own checks reject them without overflowing (the sizes are bounded
+    factor by factor before any product or sum is formed)."""
+    lib = T.library()
+    d = dims()
+    huge = [2**31, 2**40, 2**62, 2**63 - 1]
+    for fn in ("tpa_decode_workspace_bytes", "tpa_paged_decode_workspace_bytes", "tpa_shared_decode_workspace_bytes"):
+        assert getattr(lib, fn)(ctypes.byref(d), 65536, 10) == 0, fn
+        for v in huge:
+            assert getattr(lib, fn)(ctypes.byref(d), 1, v) == 0, fn
+            assert getattr(lib, fn)(ctypes.byref(d), v, v) == 0, fn
+    for v in huge:
+        assert lib.tpa_prefill_backward_workspace_bytes(ctypes.byref(d), v, v, 0) == 0
+        assert lib.tpa_prefill_backward_workspace_bytes(ctypes.byref(d), 1, 10, v) == 0
+    f = T.tpa_factors(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0)
+    for v in huge:
+        assert lib.tpa_factor_proj(ctypes.byref(d), FAKE, v, v, 0, FAKE, 1, ctypes.byref(f), None) == UNSUPPORTED
+        assert lib.tpa_factor_proj(ctypes.byref(d), FAKE, 1, 1, v, FAKE, 1, ctypes.byref(f), None) == INVALID
+        assert lib.tpa_rope_b(ctypes.byref(d), FAKE, v, v, 2, 0, None) == UNSUPPORTED
