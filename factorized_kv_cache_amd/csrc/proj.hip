@@ -214,11 +214,13 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) proj_skinny_kernel(ProjArgs
 
 // ---------------------------------------------------------------------------
 // Many tokens (prefill): 128 x 128 output tile per workgroup, four waves of
-// 64 x 64, K staged through two LDS slab buffers 64 at a time.  After a slab's
-// products each thread stores the next slab (held in registers) into the other
-// buffer and issues the loads of the one after, so one barrier per slab
-// separates the buffers' writers from their readers and the loads have a whole
-// slab of products to arrive.
+// 64 x 64, K staged through one LDS slab buffer 64 at a time.  The buffer is
+// single and nothing is prefetched into registers, so a workgroup needs 37 KB
+// of LDS and 128 registers: four workgroups share a CU and hide each other's
+// slab loads (the 896 tiles of a 16,384 x 800 projection then run in one
+// round).  Measured against two buffers with the next slab prefetched into
+// registers (two workgroups per CU): 61 against 68 us at 16,384 x 800 x 1024,
+// 1.25 against 1.37 ms at 131,072 x 2240 x 1536.
 // ---------------------------------------------------------------------------
 constexpr int kPBM = 128, kPBN = 128, kPBK = 64, kPLDK = kPBK + 8;
 constexpr int kPSlab = (kPBM + kPBN) * kPLDK;   // bf16 elements of one slab buffer
@@ -226,10 +228,10 @@ constexpr int kPSlab = (kPBM + kPBN) * kPLDK;   // bf16 elements of one slab buf
 // The epilogue stages half of the fp32 tile (64 rows) at a time in the same
 // LDS, then each thread rotates and stores 8-column pieces.
 constexpr int kPLDT = kPBN + 4;
-static_assert(64 * kPLDT * 4 <= 2 * kPSlab * 2, "epilogue tile must fit the slab buffers");
+static_assert(64 * kPLDT * 4 <= kPSlab * 2, "epilogue tile must fit the slab buffer");
 
-__global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
-  __shared__ __align__(16) bf16_t lds[2 * kPSlab];
+__global__ void __launch_bounds__(256, 4) proj_mfma_kernel(ProjArgs a) {
+  __shared__ __align__(16) bf16_t lds[kPSlab];
   __shared__ double s_rev[kMaxRopePairs];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -295,13 +297,10 @@ __global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
     wr2 = *reinterpret_cast<const uint4*>(wsrc[2] + kn);
     wr3 = *reinterpret_cast<const uint4*>(wsrc[3] + kn);
   };
-  // slab 0 into buffer 0; slab 1's loads go out
   store_slab(lds, lds + kPBM * kPLDK);
-  load_slab(kPBK < K ? kPBK : 0);
   __syncthreads();
-  int cur = 0;
   for (int64_t k0 = 0; k0 < K; k0 += kPBK) {
-    const bf16_t* xs = lds + cur * kPSlab;
+    const bf16_t* xs = lds;
     const bf16_t* ws = xs + kPBM * kPLDK;
 #pragma unroll
     for (int ks = 0; ks < kPBK / 32; ++ks) {
@@ -316,15 +315,12 @@ __global__ void __launch_bounds__(256, 2) proj_mfma_kernel(ProjArgs a) {
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma_bf16(af[tm], bfr[tn], acc[tm][tn]);
     }
+    __syncthreads();   // every wave has read the slab
     if (k0 + kPBK < K) {
-      // the other buffer was last read before the previous barrier
-      bf16_t* nx = lds + (cur ^ 1) * kPSlab;
-      store_slab(nx, nx + kPBM * kPLDK);
-      const int64_t k2 = k0 + 2 * kPBK;
-      load_slab(k2 < K ? k2 : k0 + kPBK);   // past the end: reload the last slab, never stored
+      load_slab(k0 + kPBK);
+      store_slab(lds, lds + kPBM * kPLDK);
+      __syncthreads();
     }
-    __syncthreads();
-    cur ^= 1;
   }
   // Tile rows wm*64 + tm*16 + 4*lg + i, columns wn*64 + tn*16 + li.
   float* tile = reinterpret_cast<float*>(lds);
