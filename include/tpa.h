@@ -92,7 +92,7 @@ typedef struct {
   int32_t rank_q;    /* R_Q, or 0 for TPA-KVonly */
   int32_t rank_k;    /* R_K */
   int32_t rank_v;    /* R_V */
-  double rope_base;  /* > 1, e.g. 10000 */
+  double rope_base;  /* finite and > 0, e.g. 10000 */
   int32_t dtype;     /* tpa_dtype */
 } tpa_dims;
 

@@ -441,15 +441,13 @@ def decode_shared(fq: Dict[str, np.ndarray], cache_a: Dict[str, np.ndarray], bas
 
 
 def layer_forward(x: np.ndarray, w: Dict[str, np.ndarray], dims: Dims, cache: Dict[str, np.ndarray],
-                  start_pos: int, causal: bool = True) -> np.ndarray:
+                  start_pos: int, causal: bool = True, rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """The whole TPA attention path for one block of tokens, without the output
-    projection: project, pre-rotate, append to the cache, attend over the cache."""
+    projection: project, pre-rotate, append to the cache, attend over the cache
+    ([coreui] "前向传播": the cache is written before it is read).  With `rows`
+    given, only those query rows are attended (the others stay NaN), as in
+    prefill."""
     B, S, _ = x.shape
     f = rotate_factors(project(x, w, dims), start_pos, dims)
     cache_append(cache, f, start_pos)
-    return prefill(f, cache, dims, B, S, start_pos, causal)
-
-
-def cache_elems_per_token(dims: Dims) -> int:
-    """Cached elements per token: h(R_K + R_V) + d_h(R_K + R_V)."""
-    return (dims.n_heads + dims.head_dim) * (dims.rank_k + dims.rank_v)
+    return prefill(f, cache, dims, B, S, start_pos, causal, rows=rows)

@@ -1,10 +1,17 @@
 """Helpers for the GPU parity tests: tolerances, comparisons, input plumbing.
 
 Tolerances: float32 mode max |err| <= 1e-4; bf16 mode max |err| <= 2e-2 and
-relative L2 error <= 5e-3, both against the fp64 oracle on the same inputs.
-The bf16 max-abs bound applies to outputs of magnitude up to 1 (every target
-workload's outputs are well below 1); above that it scales with max |ref|,
-because storing a result in bf16 alone moves it by up to 2^-8 of its magnitude.
+relative L2 error <= 5e-3, both against the fp64 oracle on the same inputs, as
+absolute bounds with no scaling.
+
+A bf16 output of magnitude m is stored with an error of up to half its unit in
+the last place: 2^-8 * 2^floor(log2 m), which is 7.8e-3 for m in [2, 4),
+1.6e-2 for m in [4, 8) and 3.1e-2 from 8 on, where the 2e-2 bound can no longer
+be met by any bf16 result.  assert_close refuses bf16 output cases whose
+reference reaches 8.  The attention cases keep their outputs below 4, so
+storage costs at most 7.8e-3 of the bound: the sharp cases keep their large
+query and key factors (sharp scores exercise the online softmax's rescaling)
+and draw the value factors at VALUE_STD_CAP at most.
 """
 import sys
 
@@ -18,6 +25,14 @@ import tpa_inputs as I
 F32_MAX_ABS = 1e-4
 BF16_MAX_ABS = 2e-2
 BF16_REL_L2 = 5e-3
+BF16_OUT_LIMIT = 8.0      # bf16 outputs below this: storage error <= 2^-6
+VALUE_STD_CAP = 0.8
+
+
+def value_std(std):
+    """Spread of the value factors for a case drawn with factor spread std (None:
+    the workload's own spread, whose outputs are small)."""
+    return None if std is None else min(std, VALUE_STD_CAP)
 
 
 def require_gpu():
@@ -45,13 +60,16 @@ def errors(got, ref):
 
 def assert_close(got, ref, dtype: str, what: str, max_abs=None, rel_l2=None):
     max_abs_err, rel = errors(got, ref)
-    print(f"  {what}: max_abs={max_abs_err:.3e} rel_l2={rel:.3e}", flush=True)
+    ref_max = float(np.max(np.abs(np.asarray(ref, dtype=np.float64)))) if np.size(ref) else 0.0
+    print(f"  {what}: max_abs={max_abs_err:.3e} rel_l2={rel:.3e} max|ref|={ref_max:.3g}", flush=True)
     if dtype == "f32":
         lim = F32_MAX_ABS if max_abs is None else max_abs
         assert max_abs_err <= lim, f"{what}: max abs err {max_abs_err:.3e} > {lim:.1e}"
     else:
-        scale = max(1.0, float(np.max(np.abs(np.asarray(ref, dtype=np.float64))))) if np.size(ref) else 1.0
-        lim_a = BF16_MAX_ABS * scale if max_abs is None else max_abs
+        if isinstance(got, torch.Tensor) and got.dtype == torch.bfloat16:
+            assert ref_max < BF16_OUT_LIMIT, (
+                f"{what}: outputs reach {ref_max:.3g}; bf16 storage alone could exceed the 2e-2 bound")
+        lim_a = BF16_MAX_ABS if max_abs is None else max_abs
         lim_r = BF16_REL_L2 if rel_l2 is None else rel_l2
         assert max_abs_err <= lim_a, f"{what}: max abs err {max_abs_err:.3e} > {lim_a:.1e}"
         assert rel <= lim_r, f"{what}: rel L2 err {rel:.3e} > {lim_r:.1e}"

@@ -1,7 +1,14 @@
 """GPU parity of the backward: gradients of the prefill attention with respect to
 the query factors and the cached key/value factors, and the gradient through
 the rotary embedding, against the fp64 oracle's written-out gradients (which
-are pinned to finite differences of the forward)."""
+are pinned to finite differences of the forward).
+
+Bounds.  fp32 mode: max |err| <= 1e-4 as for the forward.  bf16 mode: the
+gradients are float32 sums whose scale is set by the upstream gradient dO (they
+are linear in it) and grows with the number of keys and queries summed, so the
+bf16 bounds apply to them normalised by their largest magnitude:
+max |err| <= 2e-2 * max(1, max |ref|) and relative L2 <= 5e-3 (assert_grad).
+"""
 import numpy as np
 import pytest
 import torch
@@ -9,12 +16,19 @@ import torch
 import oracle.tpa_oracle as O
 import tpa_inputs as I
 from factorized_kv_cache_amd import tpa as T
-from gpu_util import (announce, assert_close, fill_cache, oracle_cache, oracle_dims, oracle_query,
+from gpu_util import (BF16_MAX_ABS, announce, assert_close, fill_cache, oracle_cache, oracle_dims, oracle_query,
                       query_factors_gpu, require_gpu, shape_of)
 
 pytestmark = pytest.mark.gpu
 
 KV = ("a_k", "b_k", "a_v", "b_v")
+
+
+def assert_grad(got, ref, dtype, what):
+    if dtype == "f32":
+        return assert_close(got, ref, dtype, what)
+    scale = max(1.0, float(np.max(np.abs(np.asarray(ref, dtype=np.float64))))) if np.size(ref) else 1.0
+    assert_close(got, ref, dtype, what, max_abs=BF16_MAX_ABS * scale)
 
 
 def D(d_model, h, dh, rq, rk, rv, dtype, base=10000.0):
@@ -87,12 +101,12 @@ def test_prefill_backward(case):
     dfq, ddkv = O.prefill_backward(oracle_query(fq, dims), oracle_cache(kv, od, B, n_keys), od, B, S, sp, causal,
                                    I.to_f64(dout))
     if dims.kv_only:
-        assert_close(dq.b_q, dfq["q"], dtype, f"{name} dQ")
+        assert_grad(dq.b_q, dfq["q"], dtype, f"{name} dQ")
     else:
-        assert_close(dq.a_q, dfq["a_q"], dtype, f"{name} dA_q")
-        assert_close(dq.b_q, dfq["b_q"], dtype, f"{name} dB_q")
+        assert_grad(dq.a_q, dfq["a_q"], dtype, f"{name} dA_q")
+        assert_grad(dq.b_q, dfq["b_q"], dtype, f"{name} dB_q")
     for k in KV:
-        assert_close(getattr(dkv, k)[:, :n_keys], ddkv[k], dtype, f"{name} d{k}")
+        assert_grad(getattr(dkv, k)[:, :n_keys], ddkv[k], dtype, f"{name} d{k}")
         assert torch.all(getattr(dkv, k)[:, n_keys:] == 0), f"{k}: positions past the keys were written"
 
 
@@ -134,9 +148,9 @@ def test_prefill_backward_full_size_sampled_heads():
     dfq, ddkv = O.prefill_backward(oracle_query(one(fq), dims), oracle_cache(one(kv), od, 1, S), od, 1, S, 0, True,
                                    I.to_f64(dout[:1]), heads=heads)
     for hh in heads:
-        assert_close(dq.a_q[0, :, hh], dfq["a_q"][0, :, hh], "bf16", f"full size dA_q head {hh}")
-        assert_close(dkv.a_k[0, :S, hh], ddkv["a_k"][0, :, hh], "bf16", f"full size dA_k head {hh}")
-        assert_close(dkv.a_v[0, :S, hh], ddkv["a_v"][0, :, hh], "bf16", f"full size dA_v head {hh}")
+        assert_grad(dq.a_q[0, :, hh], dfq["a_q"][0, :, hh], "bf16", f"full size dA_q head {hh}")
+        assert_grad(dkv.a_k[0, :S, hh], ddkv["a_k"][0, :, hh], "bf16", f"full size dA_k head {hh}")
+        assert_grad(dkv.a_v[0, :S, hh], ddkv["a_v"][0, :, hh], "bf16", f"full size dA_v head {hh}")
     fqc = {k: v.cuda() for k, v in fq.items()}
     kvc = {k: v.cuda() for k, v in kv.items()}
     for name, a, b, da, db in (("q", fqc["a_q"], fqc["b_q"], dq.a_q, dq.b_q),

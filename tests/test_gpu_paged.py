@@ -9,7 +9,8 @@ import torch
 import oracle.tpa_oracle as O
 import tpa_inputs as I
 from factorized_kv_cache_amd import tpa as T
-from gpu_util import announce, assert_close, oracle_dims, oracle_query, query_factors_gpu, require_gpu, shape_of
+from gpu_util import (announce, assert_close, oracle_dims, oracle_query, query_factors_gpu, require_gpu, shape_of,
+                      value_std)
 
 pytestmark = pytest.mark.gpu
 
@@ -106,7 +107,7 @@ def test_paged_decode(case):
     max_ctx = Tmax + extra
     announce(f"paged decode {name} lens={lens} page={page} max_ctx={max_ctx}")
     sh = shape_of(dims)
-    kv = I.factors(sh, B, Tmax, seed=81, dtype=dtype, std=std, with_query=False)
+    kv = I.factors(sh, B, Tmax, seed=81, dtype=dtype, std=std, with_query=False, v_std=value_std(std))
     fq = I.factors(sh, B, 1, seed=82, dtype=dtype, std=std)
     pps = (max_ctx + page - 1) // page
     n_pages = B * pps + 5

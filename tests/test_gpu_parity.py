@@ -9,7 +9,7 @@ import oracle.tpa_oracle as O
 import tpa_inputs as I
 from factorized_kv_cache_amd import tpa as T
 from gpu_util import (announce, assert_close, fill_cache, oracle_cache, oracle_dims, oracle_factors,
-                      oracle_query, query_factors_gpu, require_gpu, shape_of)
+                      oracle_query, query_factors_gpu, require_gpu, shape_of, value_std)
 
 pytestmark = pytest.mark.gpu
 
@@ -177,7 +177,7 @@ def test_decode(case):
     dims = D(dm, h, dh, rq, rk, rv, dtype)
     announce(f"decode {name} B={B} ctx={ctx}")
     sh = shape_of(dims)
-    kv = I.factors(sh, B, ctx, seed=61, dtype=dtype, std=std, with_query=False)
+    kv = I.factors(sh, B, ctx, seed=61, dtype=dtype, std=std, with_query=False, v_std=value_std(std))
     fq = I.factors(sh, B, 1, seed=62, dtype=dtype, std=std)
     cache = T.new_cache(dims, B, ctx + 3)
     fill_cache(cache, kv)
@@ -223,7 +223,7 @@ def test_prefill(case):
     announce(f"prefill {name} B={B} S={S} sp={sp} causal={causal}")
     sh = shape_of(dims)
     Tn = sp + S
-    kv = I.factors(sh, B, Tn, seed=71, dtype=dtype, std=std, with_query=False)
+    kv = I.factors(sh, B, Tn, seed=71, dtype=dtype, std=std, with_query=False, v_std=value_std(std))
     fq = I.factors(sh, B, S, seed=72, dtype=dtype, std=std)
     cache = T.new_cache(dims, B, Tn + 5)
     fill_cache(cache, kv)

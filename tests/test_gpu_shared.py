@@ -10,7 +10,8 @@ import torch
 import oracle.tpa_oracle as O
 import tpa_inputs as I
 from factorized_kv_cache_amd import tpa as T
-from gpu_util import announce, assert_close, oracle_dims, oracle_query, query_factors_gpu, require_gpu, shape_of
+from gpu_util import (announce, assert_close, oracle_dims, oracle_query, query_factors_gpu, require_gpu, shape_of,
+                      value_std)
 
 pytestmark = pytest.mark.gpu
 
@@ -21,8 +22,8 @@ def D(d_model, h, dh, rq, rk, rv, dtype, base=10000.0):
 
 def shared_setup(dims, B, ctx, seed, std=None, extra=3):
     sh = shape_of(dims)
-    f = I.factors(sh, B, ctx, seed=seed, dtype=dims.dtype, std=std, with_query=False)
-    basis = I.shared_basis(sh, seed=seed + 1, dtype=dims.dtype, std=std)
+    f = I.factors(sh, B, ctx, seed=seed, dtype=dims.dtype, std=std, with_query=False, v_std=value_std(std))
+    basis = I.shared_basis(sh, seed=seed + 1, dtype=dims.dtype, std=std, v_std=value_std(std))
     fq = I.factors(sh, B, 1, seed=seed + 2, dtype=dims.dtype, std=std)
     cache = T.new_shared_cache(dims, B, ctx + extra, basis["b_k"], basis["b_v"])
     cache.a_k[:, :ctx].copy_(f["a_k"].cuda())

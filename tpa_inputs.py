@@ -130,15 +130,19 @@ def factor_std(shape: Shape) -> float:
 
 
 def factors(shape: Shape, batch: int, seq: int, seed: int, dtype: str, std: Optional[float] = None,
-            salt: int = 0, with_query: bool = True) -> Dict[str, torch.Tensor]:
+            salt: int = 0, with_query: bool = True, v_std: Optional[float] = None) -> Dict[str, torch.Tensor]:
     """Directly drawn factor tensors, token-major, as a projection would lay them out.
 
     a_q [B,S,h,R_Q], b_q [B,S,R_Q,d_h] (KV-only: q [B,S,h,d_h]),
     a_k [B,S,h,R_K], b_k [B,S,R_K,d_h], a_v [B,S,h,R_V], b_v [B,S,R_V,d_h].
     The values are i.i.d. normal; "already rotated" is a statement about how they
     are used, and an i.i.d. isotropic draw has the same law before and after a rotation.
+    v_std, when given, is the spread of the value factors alone (a_v, b_v): the
+    query and key factors set how sharp the scores are, the value factors how
+    large the outputs are, and the two can be chosen apart.
     """
     s = factor_std(shape) if std is None else std
+    sv = s if v_std is None else v_std
     h, dh = shape.n_heads, shape.head_dim
     out = {}
     if with_query:
@@ -149,17 +153,20 @@ def factors(shape: Shape, batch: int, seq: int, seed: int, dtype: str, std: Opti
             out["b_q"] = normal((batch, seq, shape.rank_q, dh), s, seed, "f_b_q", dtype, salt)
     out["a_k"] = normal((batch, seq, h, shape.rank_k), s, seed, "f_a_k", dtype, salt)
     out["b_k"] = normal((batch, seq, shape.rank_k, dh), s, seed, "f_b_k", dtype, salt)
-    out["a_v"] = normal((batch, seq, h, shape.rank_v), s, seed, "f_a_v", dtype, salt)
-    out["b_v"] = normal((batch, seq, shape.rank_v, dh), s, seed, "f_b_v", dtype, salt)
+    out["a_v"] = normal((batch, seq, h, shape.rank_v), sv, seed, "f_a_v", dtype, salt)
+    out["b_v"] = normal((batch, seq, shape.rank_v, dh), sv, seed, "f_b_v", dtype, salt)
     return out
 
 
-def shared_basis(shape: Shape, seed: int, dtype: str, std: Optional[float] = None) -> Dict[str, torch.Tensor]:
+def shared_basis(shape: Shape, seed: int, dtype: str, std: Optional[float] = None,
+                 v_std: Optional[float] = None) -> Dict[str, torch.Tensor]:
     """Bases of the shared-basis variant, common to every token: b_k [R_K, d_h]
-    (unrotated) and b_v [R_V, d_h], i.i.d. normal with the factors' spread."""
+    (unrotated) and b_v [R_V, d_h], i.i.d. normal with the factors' spread
+    (v_std, when given, for b_v alone, as in factors)."""
     s = factor_std(shape) if std is None else std
+    sv = s if v_std is None else v_std
     return {"b_k": normal((shape.rank_k, shape.head_dim), s, seed, "basis_k", dtype),
-            "b_v": normal((shape.rank_v, shape.head_dim), s, seed, "basis_v", dtype)}
+            "b_v": normal((shape.rank_v, shape.head_dim), sv, seed, "basis_v", dtype)}
 
 
 def to_f64(t: torch.Tensor):
