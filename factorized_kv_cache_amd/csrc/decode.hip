@@ -15,6 +15,8 @@
 // sequence's keys write an empty partial (m = -inf, l = 0, acc = 0), which the
 // combine weighs by 0; with a paged cache every token's row goes through the
 // block table.
+#include <mutex>
+
 #include "kernels.h"
 
 namespace tpa {
@@ -262,6 +264,8 @@ static size_t partial_bytes(const DecodePlan& p, const AttnArgs& a) {
   return (size_t)a.n_batch * (size_t)p.n_chunks * (size_t)a.h * (size_t)(a.d_h + 2) * sizeof(float);
 }
 
+size_t decode_plan_bytes(const DecodePlan& p, const AttnArgs& a) { return partial_bytes(p, a); }
+
 // Workspace: partials for either plan the shape allows, so the size does not
 // depend on pointer alignment.  (The matrix-core plan exists only for the
 // shapes that kernel takes: its block of tokens per wave is 4 * (32 / R_K).)
@@ -270,6 +274,36 @@ size_t decode_workspace_bytes(int dtype, const AttnArgs& a) {
   const size_t n = partial_bytes(plan_generic(ctx_len), a);
   const size_t m = decode_mfma_shape_ok(dtype, a) ? partial_bytes(plan_mfma(a, ctx_len), a) : 0;
   return n > m ? n : m;
+}
+
+// Scratch of the allocation-free decode entry point: the chunk partials live in
+// this file-scope device array instead of a caller's workspace.  Every device
+// the library runs on holds its own copy until the process ends.  In host code
+// the name only identifies the symbol; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+void* g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(int dtype, const AttnArgs& a, int64_t ctx_len, const DecodePlan& p, void* ws,

@@ -141,8 +141,14 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(int dtype, const AttnArgs& a, int64_t ctx_len);
 size_t decode_workspace_bytes(int dtype, const AttnArgs& a);
+size_t decode_plan_bytes(const DecodePlan& p, const AttnArgs& a);   // partials of this plan
 hipError_t launch_decode(int dtype, const AttnArgs& a, int64_t ctx_len, const DecodePlan& p, void* ws,
                          hipStream_t st);
+
+// The allocation-free decode's scratch: a static device array of this size per
+// device; decode_scratch gives the current device's address (looked up once).
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch(void** ptr);
 
 hipError_t launch_prefill(int dtype, const AttnArgs& a, hipStream_t st);
 

@@ -354,8 +354,9 @@ size_t tpa_decode_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t ct
   return tpa::decode_workspace_bytes(d->dtype, a);
 }
 
-tpa_status tpa_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
-                           int64_t ctx_len, void* out, void* workspace, size_t ws_bytes, void* stream) {
+// Checks shared by the two dense decode entry points; fills the kernel arguments.
+static tpa_status decode_args(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
+                              int64_t ctx_len, void* out, tpa::AttnArgs* a) {
   tpa_status st = check_dims(d);
   if (st != TPA_OK) return st;
   if ((st = check_query(d, q)) != TPA_OK) return st;
@@ -370,7 +371,15 @@ tpa_status tpa_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_ca
     return fail(TPA_ERR_CAPACITY, "ctx_len %lld exceeds max_seq %lld", (long long)ctx_len, (long long)c->max_seq);
   int64_t qs;
   if ((st = resolve_stride(q->q_batch_stride, 1, "q_batch_stride", &qs)) != TPA_OK) return st;
-  tpa::AttnArgs a = attn_args(d, q, qs, c, n_batch, 1, ctx_len - 1, 1, out);
+  *a = attn_args(d, q, qs, c, n_batch, 1, ctx_len - 1, 1, out);
+  return TPA_OK;
+}
+
+tpa_status tpa_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
+                           int64_t ctx_len, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  tpa::AttnArgs a;
+  tpa_status st = decode_args(d, q, c, n_batch, ctx_len, out, &a);
+  if (st != TPA_OK) return st;
   const tpa::DecodePlan p = tpa::plan_decode(d->dtype, a, ctx_len);
   const size_t need = tpa::decode_workspace_bytes(d->dtype, a);
   if (need > 0 && (!workspace || ws_bytes < need))
@@ -378,6 +387,26 @@ tpa_status tpa_decode_attn(const tpa_dims* d, const tpa_factors* q, const tpa_ca
                 workspace ? "" : ", NULL");
   return hip_status(tpa::launch_decode(d->dtype, a, ctx_len, p, workspace, (hipStream_t)stream),
                     "tpa_decode_attn");
+}
+
+size_t tpa_decode_noalloc_max_bytes(void) { return tpa::kDecodeScratchBytes; }
+
+tpa_status tpa_decode_attn_noalloc(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
+                                   int64_t ctx_len, void* out, void* stream) {
+  tpa::AttnArgs a;
+  tpa_status st = decode_args(d, q, c, n_batch, ctx_len, out, &a);
+  if (st != TPA_OK) return st;
+  const tpa::DecodePlan p = tpa::plan_decode(d->dtype, a, ctx_len);
+  const size_t need = tpa::decode_plan_bytes(p, a);
+  if (need > tpa::kDecodeScratchBytes)
+    return fail(TPA_ERR_WORKSPACE,
+                "this decode needs %zu bytes of partials; the built-in scratch holds %zu (use tpa_decode_attn "
+                "with a workspace)", need, tpa::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = tpa::decode_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "tpa_decode_attn_noalloc (scratch address)");
+  return hip_status(tpa::launch_decode(d->dtype, a, ctx_len, p, scratch, (hipStream_t)stream),
+                    "tpa_decode_attn_noalloc");
 }
 
 size_t tpa_prefill_backward_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t seq_len,

@@ -72,6 +72,8 @@ def _load():
         "tpa_decode_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64]),
         "tpa_decode_attn": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_cache), i64, i64, vp, vp,
                                            ctypes.c_size_t, vp]),
+        "tpa_decode_noalloc_max_bytes": (ctypes.c_size_t, []),
+        "tpa_decode_attn_noalloc": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_cache), i64, i64, vp, vp]),
         "tpa_prefill_backward_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64, i64]),
         "tpa_prefill_attn_backward": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_cache), i64, i64, i64, i32,
                                                      vp, P(tpa_factors), P(tpa_cache), vp, ctypes.c_size_t, vp]),
@@ -99,6 +101,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("tpa_packed_weight_rows", "tpa_cache_elems_per_token", "tpa_factor_proj", "tpa_rope_b",
             "tpa_cache_append", "tpa_prefill_attn", "tpa_decode_workspace_bytes", "tpa_decode_attn",
+            "tpa_decode_noalloc_max_bytes", "tpa_decode_attn_noalloc",
             "tpa_prefill_backward_workspace_bytes", "tpa_prefill_attn_backward", "tpa_rope_b_backward",
             "tpa_paged_cache_append", "tpa_paged_decode_workspace_bytes", "tpa_paged_decode_attn",
             "tpa_shared_cache_append", "tpa_shared_decode_workspace_bytes", "tpa_shared_decode_attn",
@@ -364,6 +367,22 @@ def tpa_decode_attn(dims: Dims, q: Factors, cache: Cache, ctx_len: int, workspac
     _check(_lib.tpa_decode_attn(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B, ctx_len,
                                 _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream)))
+    return out
+
+
+def tpa_decode_noalloc_max_bytes() -> int:
+    return int(_lib.tpa_decode_noalloc_max_bytes())
+
+
+def tpa_decode_attn_noalloc(dims: Dims, q: Factors, cache: Cache, ctx_len: int, out: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """tpa_decode_attn with the chunk partials in the library's static device
+    scratch (no workspace argument).  Overlapping calls on one device race."""
+    B = q.b_q.shape[0]
+    if out is None:
+        out = torch.empty(B, dims.n_heads * dims.head_dim, dtype=dims.torch_dtype, device=q.b_q.device)
+    _check(_lib.tpa_decode_attn_noalloc(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B,
+                                        ctx_len, _ptr(out), _stream(stream)))
     return out
 
 

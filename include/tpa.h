@@ -205,6 +205,25 @@ tpa_status tpa_decode_attn(const tpa_dims* dims, const tpa_factors* q, const tpa
                            int64_t n_batch, int64_t ctx_len, void* out, void* workspace, size_t ws_bytes,
                            void* stream);
 
+/* Decode attention without a workspace argument, for callers that cannot
+ * allocate device memory at call time (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, checks,
+ * kernels, split and merge order as tpa_decode_attn, so the same bits; the
+ * chunk partials go to a static device array of tpa_decode_noalloc_max_bytes()
+ * bytes (16 MiB) that each device holds from the library's first use on it
+ * until the process ends.  The call allocates nothing.  Every call on one
+ * device shares that device's array and it keeps the last call's contents
+ * (nothing in it needs to start at zero): calls that may overlap on one
+ * device (several streams, several host threads) race and must be ordered
+ * by the caller.
+ * Errors: as tpa_decode_attn; TPA_ERR_WORKSPACE when the call's partials,
+ * n_batch * chunks * h * (d_h + 2) * 4 bytes for the plan it runs (about
+ * 8.5 MB for 8 sequences of 131073 keys at h 32, d_h 128), exceed the array;
+ * TPA_ERR_HIP if the array's device address cannot be taken. */
+size_t tpa_decode_noalloc_max_bytes(void);
+tpa_status tpa_decode_attn_noalloc(const tpa_dims* dims, const tpa_factors* q, const tpa_cache* cache,
+                                   int64_t n_batch, int64_t ctx_len, void* out, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Backward (training; the pages train TPA models, the arithmetic is the chain
  * rule through tpa_prefill_attn and tpa_rope_b).  Gradients are float32

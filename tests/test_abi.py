@@ -259,3 +259,19 @@ def test_sizes_far_past_the_limits():
         assert lib.tpa_factor_proj(ctypes.byref(d), FAKE, v, v, 0, FAKE, 1, ctypes.byref(f), None) == UNSUPPORTED
         assert lib.tpa_factor_proj(ctypes.byref(d), FAKE, 1, 1, v, FAKE, 1, ctypes.byref(f), None) == INVALID
         assert lib.tpa_rope_b(ctypes.byref(d), FAKE, v, v, 2, 0, None) == UNSUPPORTED
+
+
+def test_decode_noalloc_rejects_partials_beyond_its_scratch():
+    """600 sequences at h 256, d_h 32 need 600 * 256 * 34 * 4 bytes of partials
+    (20.9 MB) on the general kernel's plan, beyond the 16 MiB scratch: refused
+    before anything touches a device."""
+    lib = T.library()
+    assert lib.tpa_decode_noalloc_max_bytes() == 16 << 20
+    d = dims(d_model=512, n_heads=256, head_dim=32, rank_q=2, rank_k=2, rank_v=2)
+    q = T.tpa_factors(FAKE, FAKE, None, None, None, None, 0, 0)
+    c = T.tpa_cache(FAKE, FAKE, FAKE, FAKE, 600, 4)
+    st = lib.tpa_decode_attn_noalloc(ctypes.byref(d), ctypes.byref(q), ctypes.byref(c), 600, 1, FAKE, None)
+    assert st == WORKSPACE
+    assert "scratch" in lib.tpa_last_error().decode()
+    st = lib.tpa_decode_attn_noalloc(ctypes.byref(d), ctypes.byref(q), ctypes.byref(c), 601, 1, FAKE, None)
+    assert st == CAPACITY
