@@ -514,10 +514,10 @@ def cpu_baseline():
     one-head sub-problems on a thread pool (numpy releases the interpreter lock
     in its array operations; BLAS is held to one thread per worker).
 
-    decode: one of the 8 sequences of the long-context decode step (the new
-    token's projection, rotation and cache write, then attention over 131073
-    keys, every head); a step of the whole batch takes 8 such sequences, so
-    tok/s = 1 / time.  prefill: 1024 seeded query rows of one of the 32
+    decode: the long-context decode step for all 8 sequences (the new token's
+    projection, rotation and cache write, then attention over 131073 keys,
+    every head), one sequence after another, so tok/s = 8 / time.  prefill:
+    2048 seeded query rows of one of the 32
     sequences of the KV-only prefill (16384 keys, every head), rated by the
     algorithmic flops of those rows (4 * d_h * (p + 1) per row and head)."""
     import concurrent.futures as cf
@@ -529,40 +529,43 @@ def cpu_baseline():
     n_thr = cpu_threads()
     res = {}
     with threadpool_limits(limits=1):
-        # ---- decode sample
+        # ---- decode: the whole step of the batch, one sequence after another
         wl = I.WORKLOADS["decode_b8_ctx128k"]
         s = wl.shape
         od = O.Dims(s.d_model, s.n_heads, s.head_dim, s.rank_q, s.rank_k, s.rank_v, s.rope_base)
         ctx = wl.seq + 1
-        kv = I.factors(s, 1, wl.seq, seed=2002, dtype="bf16", with_query=False)
-        cache = O.cache_new(od, 1, ctx)
-        for k in ("a_k", "b_k", "a_v", "b_v"):
-            cache[k][:, :wl.seq] = I.to_f64(kv[k])
-        del kv
         w = {k: I.to_f64(v) for k, v in I.weights(s, seed=2002, dtype="bf16").items()}
-        x_new = I.to_f64(I.activations(1, 1, s.d_model, seed=2002, dtype="bf16", stream="x_new"))
-        t0 = time.perf_counter()
-        f = O.rotate_factors(O.project(x_new, w, od), ctx - 1, od)
-        O.cache_append(cache, f, ctx - 1)
+        t_dec = 0.0
+        for b in range(wl.batch):
+            kv = I.factors(s, 1, wl.seq, seed=2002, dtype="bf16", with_query=False, salt=b)
+            cache = O.cache_new(od, 1, ctx)
+            for k in ("a_k", "b_k", "a_v", "b_v"):
+                cache[k][:, :wl.seq] = I.to_f64(kv[k])
+            del kv
+            x_new = I.to_f64(I.activations(1, 1, s.d_model, seed=2002, dtype="bf16", stream="x_new", salt=b))
+            t0 = time.perf_counter()
+            f = O.rotate_factors(O.project(x_new, w, od), ctx - 1, od)
+            O.cache_append(cache, f, ctx - 1)
 
-        def dec_head(hh):
-            od1, q1, c1 = _one_head(od, f, cache, hh)
-            return O.decode(q1, c1, od1, 1, ctx)
+            def dec_head(hh):
+                od1, q1, c1 = _one_head(od, f, cache, hh)
+                return O.decode(q1, c1, od1, 1, ctx)
 
-        with cf.ThreadPoolExecutor(n_thr) as ex:
-            outs = list(ex.map(dec_head, range(s.n_heads)))
-        t_dec = time.perf_counter() - t0
-        assert all(np.all(np.isfinite(o)) for o in outs)
-        nbytes = ctx * (s.n_heads + s.head_dim) * (s.rank_k + s.rank_v) * 2
-        res["value"] = round(1.0 / t_dec, 3)
+            with cf.ThreadPoolExecutor(n_thr) as ex:
+                outs = list(ex.map(dec_head, range(s.n_heads)))
+            t_dec += time.perf_counter() - t0
+            assert all(np.all(np.isfinite(o)) for o in outs)
+            del cache, outs
+        nbytes = wl.batch * ctx * (s.n_heads + s.head_dim) * (s.rank_k + s.rank_v) * 2
+        res["value"] = round(wl.batch / t_dec, 3)
         res["unit"] = "tok/s"
         res["cores"] = n_thr
         res["kind"] = "oracle"
         res["GBps_equivalent"] = round(nbytes / t_dec / 1e9, 4)
-        res["sample"] = (f"decode_b8_ctx128k: 1 of 8 sequences of the decode step (projection of the new token, "
-                         f"rotation, cache write, attention over {ctx} keys, all {s.n_heads} heads), fp64 numpy, "
-                         f"one head per thread on {n_thr} threads, {t_dec:.1f} s; a whole step is 8 such sequences")
-        del cache, outs
+        res["sample"] = (f"decode_b8_ctx128k: one whole decode step of the 8 sequences (projection of the new "
+                         f"token, rotation, cache write, attention over {ctx} keys, all {s.n_heads} heads), fp64 "
+                         f"numpy, one head per thread on {n_thr} threads, {t_dec:.1f} s of timed work (cache "
+                         f"draws excluded)")
         # ---- prefill sample
         wl = I.WORKLOADS["kvonly_b32_ctx16k"]
         s = wl.shape
@@ -573,7 +576,7 @@ def cpu_baseline():
         for k in ("a_k", "b_k", "a_v", "b_v"):
             cache[k][:, :S] = I.to_f64(kv[k])
         fq = {"q": I.to_f64(kv["q"])}
-        rows = np.sort(np.random.default_rng(2003).choice(S, 1024, replace=False))
+        rows = np.sort(np.random.default_rng(2003).choice(S, 2048, replace=False))
         t0 = time.perf_counter()
 
         def pre_head(hh):
@@ -586,7 +589,7 @@ def cpu_baseline():
         assert all(np.all(np.isfinite(o[:, rows])) for o in outs)
         flop = float(sum(4.0 * s.head_dim * (int(p) + 1) for p in rows)) * s.n_heads
         res["prefill"] = {"tflops": round(flop / t_pre / 1e12, 6), "unit": "TFLOP/s", "seconds": round(t_pre, 2),
-                          "sample": f"kvonly_b32_ctx16k: 1024 seeded query rows of 1 of 32 sequences, all "
+                          "sample": f"kvonly_b32_ctx16k: 2048 seeded query rows of 1 of 32 sequences, all "
                                     f"{s.n_heads} heads, causal over up to {S} keys; rate of those rows' "
                                     f"algorithmic flops"}
     return res

@@ -83,6 +83,8 @@ PROJ_CASES = [
     (16, 1, 1024, 16, 64, 6, 2, 2, 4096),       # decode batch: few-token kernel
     (40, 1, 1536, 24, 64, 0, 4, 4, 16384),
     (3, 150, 1536, 24, 64, 0, 4, 4, 0),          # KV-only, many tokens
+    (2, 4500, 1536, 24, 64, 0, 4, 4, 7),         # 256 x 128 matrix-core tiles, ragged in M and N
+    (4, 4096, 1024, 16, 64, 6, 2, 2, 0),         # the prefill workload's projection (128 x 128 tiles)
     # the dims limits: every rank and head_dim at their maximum; the most heads
     # (n_heads * head_dim = 8192); the smallest dims
     (1, 5, 64, 32, 256, 64, 64, 64, 7),
