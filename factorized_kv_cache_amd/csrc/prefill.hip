@@ -152,8 +152,13 @@ static hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t st) {
 
 bool prefill_mfma_supported(int dtype, const AttnArgs& a);
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t st);
+bool prefill_mfma32_supported(int dtype, const AttnArgs& a);
+hipError_t launch_prefill_mfma32(const AttnArgs& a, hipStream_t st);
 
+// d_h = 64 runs on the 32x32x16 matrix-core kernel, d_h = 128 on the 16x16x32
+// one, every other shape (and fp32) on the general kernel.
 hipError_t launch_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
+  if (prefill_mfma32_supported(dtype, a)) return launch_prefill_mfma32(a, st);
   if (prefill_mfma_supported(dtype, a)) return launch_prefill_mfma(a, st);
   return dtype == kF32 ? launch_prefill_t<float>(a, st) : launch_prefill_t<bf16_t>(a, st);
 }

@@ -1,0 +1,400 @@
+// Causal prefill attention at d_h = 64 on v_mfma_f32_32x32x16_bf16 (on gfx950
+// this form sustains about twice the rate of the 16x16x32 one), with keys and
+// values rebuilt from the cached factors in LDS.
+//
+// Arithmetic as the general prefill kernel ("Tensor Product Attention Is All
+// You Need" review on coreui.cn: Q_t/K_t/V_t equations of 核心机制总结 and the
+// masked softmax attention of the code walk-through 前向传播).  A workgroup owns
+// 256 queries of one head of one sequence; each of its four waves owns 64 of
+// them as two 32-query tiles.  For every key block (32 keys; 64 at rank 1,
+// whose factors take half the registers; at rank 2 the 64-key blocks spill and
+// measured 297 against 277 us for 4 x 4096 tokens):
+//
+//  * rebuild: the whole workgroup forms k_t = sum_r A_K[t,h,r] B~_K[t,r,:] and
+//    v_t likewise (rank pairs through v_dot2_f32_bf16, fp32 sums) and stores
+//    both row-major in LDS as bf16, 16 bytes per store.  Two buffers: block
+//    i+1 is rebuilt (from factors loaded a block earlier) while block i is
+//    multiplied, so each block costs one barrier;
+//  * scores, transposed: S^T[t, q] = K[t,:] . Q[q,:], K as the A operand (LDS,
+//    16-byte reads of rows padded to 72 elements) and Q^T as the B operand
+//    (registers, formed once); each lane's 16 scores of a tile belong to one
+//    query, and the two lanes that share a query swap once per block for the
+//    block maximum;
+//  * online softmax per query in base 2 (the scale log2(e) / (R_Q R_K sqrt(d_h))
+//    is folded into Q); the running maximum moves only when a block's maximum
+//    exceeds it by more than 8, so most blocks skip the rescale; masking only
+//    on blocks that reach past a query; a wave skips blocks that lie wholly
+//    after its queries;
+//  * values, transposed: O^T[d, q] += V^T[d, t] P^T[t, q].  The score tiles'
+//    output registers, rounded to bf16, are the B operand as they are (k-slot
+//    j of lane half g is key 4g+j for j<4, 8+4g+(j-4) for j>=4, of a 16-key
+//    step); the matching V^T operand comes straight from the row-major V tile
+//    with two ds_read_b64_tr_b16 (each gives the lanes of a 16-lane group four
+//    consecutive keys of their own column d);
+//  * the softmax denominators are the sums of the same bf16 probabilities
+//    (v_dot2 against ones), accumulated per lane and joined at the end.
+//    (Taking them on the matrix cores with a ones row, and starting the score
+//    accumulators from -m to drop the subtraction, both measured slower.)
+//
+// Query blocks are scheduled heaviest (most keys) first, evenly across XCDs.
+#include "kernels.h"
+#include "mfma.h"
+#include "rebuild.h"
+
+namespace tpa {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+__device__ __forceinline__ f32x16_t mfma32_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed LDS read: the 16 lanes of a group each name an 8-byte piece (4
+// bf16) of a 4 x 16 block; lane i receives element i of each of the four rows.
+__device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// max of x over the lanes l and l ^ 32
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_nn(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
+template <int R>
+struct Pf32Cfg {
+  static constexpr int DH = 64;
+  static constexpr int QT = 2;                 // 32-query tiles per wave
+  static constexpr int BM = 4 * 32 * QT;       // queries per workgroup
+  static constexpr int BN = R == 1 ? 64 : 32;  // keys per block
+  static constexpr int KT = BN / 32;           // 32-key tiles of the score product
+  static constexpr int KS = BN / 16;           // 16-key steps of the value product
+  static constexpr int LD = DH + 8;            // LDS row stride (bf16) of K and V
+  static constexpr int TILE = BN * LD;         // bf16 elements of one K or V buffer
+  static constexpr int IT = BN * (DH / 8) / 256;   // rebuild items per thread
+  static constexpr size_t kLds = (size_t)4 * TILE * sizeof(bf16_t);
+  static constexpr float kRescaleSlack = 8.f;  // log2 units
+};
+
+// The cached factors one thread needs for its rebuild items of one key block:
+// item = (key, 8-wide d slice), consecutive lanes on consecutive slices of one
+// key, so each rank row of B~_K / B_V is read as whole cache lines.
+template <int R>
+struct Rebuild32 {
+  static constexpr int IT = Pf32Cfg<R>::IT;
+  uint4 bk[IT][R];
+  uint4 bv[IT][R];
+  typename RankWordP<R>::type ak[IT];
+  typename RankWordP<R>::type av[IT];
+};
+
+// Keys past kend are clamped to the last valid key: they are masked out of
+// every score, so only finiteness matters.
+template <int R>
+__device__ __forceinline__ void load_rebuild32(Rebuild32<R>& g, const AttnArgs& a, int64_t seq0, int hh, int64_t k0,
+                                               int64_t kend) {
+  typedef typename RankWordP<R>::type W;
+  const bf16_t* AK = reinterpret_cast<const bf16_t*>(a.c_ak);
+  const bf16_t* BK = reinterpret_cast<const bf16_t*>(a.c_bk);
+  const bf16_t* AV = reinterpret_cast<const bf16_t*>(a.c_av);
+  const bf16_t* BV = reinterpret_cast<const bf16_t*>(a.c_bv);
+#pragma unroll
+  for (int it = 0; it < Rebuild32<R>::IT; ++it) {
+    const int item = threadIdx.x + 256 * it;
+    const int key = item >> 3, d0 = (item & 7) * 8;
+    int64_t t = k0 + key;
+    t = t < kend ? t : kend - 1;
+    const int64_t row = seq0 + t;
+    g.ak[it] = *reinterpret_cast<const W*>(AK + (row * a.h + hh) * R);
+    g.av[it] = *reinterpret_cast<const W*>(AV + (row * a.h + hh) * R);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      g.bk[it][r] = *reinterpret_cast<const uint4*>(BK + (row * R + r) * 64 + d0);
+      g.bv[it][r] = *reinterpret_cast<const uint4*>(BV + (row * R + r) * 64 + d0);
+    }
+  }
+}
+
+template <int R>
+__device__ __forceinline__ void store_rebuild32(const Rebuild32<R>& g, bf16_t* k_lds, bf16_t* v_lds) {
+  constexpr int LD = Pf32Cfg<R>::LD;
+#pragma unroll
+  for (int it = 0; it < Rebuild32<R>::IT; ++it) {
+    const int item = threadIdx.x + 256 * it;
+    const int key = item >> 3, d0 = (item & 7) * 8;
+    float kv[8], vv[8];
+    factor_combine<R>(g.ak[it], g.bk[it], kv);
+    factor_combine<R>(g.av[it], g.bv[it], vv);
+    *reinterpret_cast<bf16x8_t*>(k_lds + key * LD + d0) = pack8(kv);
+    *reinterpret_cast<bf16x8_t*>(v_lds + key * LD + d0) = pack8(vv);
+  }
+}
+
+// One key block for this wave's QT x 32 queries (positions wpos0 ..).
+template <int R>
+__device__ __forceinline__ void attend_block32(const bf16_t* k_lds, const bf16_t* v_lds, int64_t k0, int64_t kend,
+                                               int64_t wpos0, bool causal, int lane,
+                                               const bf16x8_t (&qop)[Pf32Cfg<R>::QT][4],
+                                               float (&m_run)[Pf32Cfg<R>::QT], float (&lsum)[Pf32Cfg<R>::QT],
+                                               f32x16_t (&oacc)[Pf32Cfg<R>::QT][2]) {
+  using C = Pf32Cfg<R>;
+  constexpr int QT = C::QT, KT = C::KT, KS = C::KS, LD = C::LD, BN = C::BN;
+  const int l32 = lane & 31, lh = lane >> 5;
+
+  // ---- scores S^T[key, query] for the block's 32-key tiles
+  f32x16_t sacc[KT][QT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    bf16x8_t kf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kf[ks] = *reinterpret_cast<const bf16x8_t*>(k_lds + (kt * 32 + l32) * LD + ks * 16 + lh * 8);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      f32x16_t acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma32_bf16(kf[ks], qop[qt][ks], acc);
+      sacc[kt][qt] = acc;
+    }
+  }
+
+  // ---- mask (only where the block reaches past a query of this wave, or
+  //      past the keys); value e of a tile is key 8*(e/4) + 4*lh + e%4
+  const bool need_mask = (causal && k0 + BN - 1 > wpos0) || (k0 + BN > kend);
+  if (need_mask) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t t = k0 + kt * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+          const int64_t p = wpos0 + 32 * qt + l32;
+          const bool ok = t < kend && (!causal || t <= p);
+          if (!ok) sacc[kt][qt][e] = -INFINITY;
+        }
+  }
+
+  // ---- online softmax per query (lazy rescale), P^T operands, row sums
+  constexpr uint32_t kOnes = 0x3f803f80u;   // (1, 1) in bf16
+  bf16x8_t pop[QT][KS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) bmax = max_nn(bmax, sacc[kt][qt][e]);
+    bmax = half_swap_max(bmax);
+    const bool grow = bmax > m_run[qt] + C::kRescaleSlack;
+    if (__any(grow)) {
+      const float m_new = grow ? bmax : m_run[qt];
+      const float alpha = fast_exp2(m_run[qt] - m_new);   // 0 on the first block, 1 where m stays
+      m_run[qt] = m_new;
+      lsum[qt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) oacc[qt][dt] *= alpha;
+    }
+    // a query with no visible key yet keeps m = -inf; its probabilities are 0
+    const float m_use = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(sacc[s >> 1][qt][8 * (s & 1) + j] - m_use);
+      pop[qt][s] = pack8(pv);
+      const uint4 w = __builtin_bit_cast(uint4, pop[qt][s]);
+      float l = lsum[qt];
+      l = dot2_bf16(w.x, kOnes, l);
+      l = dot2_bf16(w.y, kOnes, l);
+      l = dot2_bf16(w.z, kOnes, l);
+      l = dot2_bf16(w.w, kOnes, l);
+      lsum[qt] = l;
+    }
+  }
+
+  // ---- O^T += V^T P^T.  Lane l of a 16-lane group reads the piece at key row
+  //      4*lh + (l%16)/4 (+8 for the second half of the k-slots), columns
+  //      16*((l/16)%2) + 4*(l%4) .. of the d tile.
+  const int grp = lane & 15;
+  const bf16_t* vbase = v_lds + (4 * lh + (grp >> 2)) * LD + 16 * ((lane >> 4) & 1) + 4 * (grp & 3);
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16_t* vp = vbase + s * 16 * LD + dt * 32;
+      const uint2 lo = lds_read_tr16(vp);
+      const uint2 hi = lds_read_tr16(vp + 8 * LD);
+      const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) oacc[qt][dt] = mfma32_bf16(vf, pop[qt][s], oacc[qt][dt]);
+    }
+  }
+}
+
+template <int R>
+__global__ void __launch_bounds__(256, 2) prefill_mfma32_kernel(AttnArgs a, int n_qblocks) {
+  using C = Pf32Cfg<R>;
+  constexpr int DH = 64, QT = C::QT, BM = C::BM, BN = C::BN, TILE = C::TILE;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16_t* const lds = reinterpret_cast<bf16_t*>(smem);
+  // buffer i: K at lds + i*TILE, V at lds + (2 + i)*TILE
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, lh = lane >> 5;
+  // One-dimensional grid.  Work items (query block, head, sequence) in order of
+  // decreasing key count are numbered by the linear workgroup id; since
+  // workgroups go to the XCDs round-robin by that id, every XCD gets an equal
+  // share of every query block, heaviest first.  When the (sequence, head)
+  // pairs split evenly over the eight XCDs, XCD x takes the x-th contiguous
+  // range of them (sequence-major), so the factors it reads span as few
+  // sequences as possible and stay in its L2.
+  const int h = a.h;
+  const int64_t hb = (int64_t)h * a.n_batch;
+  const int64_t L = blockIdx.x;
+  const int qb = n_qblocks - 1 - (int)(L / hb);
+  int64_t u = L % hb;
+  if (hb % 8 == 0) u = (u & 7) * (hb >> 3) + (u >> 3);
+  const int hh = (int)(u % h);
+  const int64_t b = u / h;
+  const int64_t q0 = (int64_t)qb * BM;
+  const int64_t seq0 = b * a.max_seq;
+  const int64_t last_q = (q0 + BM < a.S ? q0 + BM : a.S) - 1;
+  const int64_t kend = a.causal ? a.start_pos + last_q + 1 : a.start_pos + a.S;
+  const int nblk = (int)((kend + BN - 1) / BN);
+
+  // The first key block's factors go out before anything else.
+  Rebuild32<R> rg;
+  load_rebuild32<R>(rg, a, seq0, hh, 0, kend);
+
+  // ---- query operand: lane (query q0 + 64*wave + 32*qt + l32, d slice
+  //      16*ks + 8*lh .. +8), pre-scaled
+  bf16x8_t qop[QT][4];
+  {
+    const bf16_t* AQ = reinterpret_cast<const bf16_t*>(a.a_q);
+    const bf16_t* BQ = reinterpret_cast<const bf16_t*>(a.b_q);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int64_t s = q0 + 64 * wave + 32 * qt + l32;
+      const int64_t tok = b * a.q_bstride_tok + (s < a.S ? s : a.S - 1);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int d0 = ks * 16 + lh * 8;
+        float v[8];
+        if (a.rq == 0) {
+          const bf16x8_t e = as_bf16x8(*reinterpret_cast<const uint4*>(BQ + (tok * h + hh) * DH + d0));
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = (float)e[j] * a.q_scale;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = 0.f;
+          for (int r = 0; r < a.rq; ++r) {
+            const float ar = bf16_to_f32(AQ[(tok * h + hh) * a.rq + r]);
+            const bf16x8_t e = as_bf16x8(*reinterpret_cast<const uint4*>(BQ + (tok * a.rq + r) * DH + d0));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = fmaf(ar, (float)e[j], v[j]);
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] *= a.q_scale;
+        }
+        qop[qt][ks] = pack8(v);
+      }
+    }
+  }
+
+  float m_run[QT], lsum[QT];   // lsum: this lane's half of each row sum
+  f32x16_t oacc[QT][2];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = -INFINITY;
+    lsum[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[qt][dt][e] = 0.f;
+  }
+
+  const int64_t wpos0 = a.start_pos + q0 + 64 * wave;   // position of this wave's first query
+  const bool causal = a.causal != 0;
+  // Block i is rebuilt into buffer i & 1 while block i - 1 is attended to; its
+  // factors were loaded a block earlier.
+  store_rebuild32<R>(rg, lds, lds + 2 * TILE);
+  if (nblk > 1) load_rebuild32<R>(rg, a, seq0, hh, BN, kend);
+  __syncthreads();
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int64_t k0 = (int64_t)blk * BN;
+    // a block wholly after every query of this wave contributes nothing
+    if (!causal || k0 <= wpos0 + 63)
+      attend_block32<R>(lds + (blk & 1) * TILE, lds + (2 + (blk & 1)) * TILE, k0, kend, wpos0, causal, lane, qop,
+                        m_run, lsum, oacc);
+    if (blk + 1 < nblk) {
+      store_rebuild32<R>(rg, lds + ((blk + 1) & 1) * TILE, lds + (2 + ((blk + 1) & 1)) * TILE);
+      if (blk + 2 < nblk) load_rebuild32<R>(rg, a, seq0, hh, k0 + 2 * BN, kend);
+    }
+    __syncthreads();
+  }
+
+  // ---- normalise and store: value e of tile (qt, dt) is d = 32*dt + 8*(e/4)
+  //      + 4*lh + e%4 of query l32; its two lanes (l32, l32 + 32) hold the
+  //      halves of its row sum
+  bf16_t* out = reinterpret_cast<bf16_t*>(a.out);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum[qt]), __float_as_uint(lsum[qt]), false,
+                                                     false);
+    const float lrow = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const float inv = a.v_scale / lrow;
+    const int64_t s = q0 + 64 * wave + 32 * qt + l32;
+    if (s < a.S) {
+      bf16_t* orow = out + ((b * a.S + s) * h + hh) * (int64_t)DH;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16_t o = oacc[qt][dt];
+          const uint2 w = make_uint2(pack_bf16x2(o[4 * g] * inv, o[4 * g + 1] * inv),
+                                     pack_bf16x2(o[4 * g + 2] * inv, o[4 * g + 3] * inv));
+          *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * g + 4 * lh) = w;
+        }
+    }
+  }
+}
+
+// LDS a workgroup may allocate on the current device.
+static size_t lds_per_block32() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 0;
+  return (size_t)v;
+}
+
+bool prefill_mfma32_supported(int dtype, const AttnArgs& a) {
+  if (dtype != kBF16 || a.d_h != 64) return false;
+  if (a.rk != a.rv || !(a.rk == 1 || a.rk == 2 || a.rk == 4)) return false;
+  if (Pf32Cfg<4>::kLds > lds_per_block32() || Pf32Cfg<2>::kLds > lds_per_block32()) return false;
+  constexpr int bm = Pf32Cfg<2>::BM;
+  if ((a.S + bm - 1) / bm * (int64_t)a.h * a.n_batch >= ((int64_t)1 << 31)) return false;
+  const void* ptrs[4] = {a.b_q, a.c_bk, a.c_bv, a.out};   // read/written 8 or 16 bytes at a time
+  for (int i = 0; i < 4; ++i)
+    if (((uintptr_t)ptrs[i]) % 16) return false;
+  return true;
+}
+
+hipError_t launch_prefill_mfma32(const AttnArgs& a, hipStream_t st) {
+  constexpr int bm = Pf32Cfg<2>::BM;
+  const int nqb = (int)((a.S + bm - 1) / bm);
+  const dim3 grid((unsigned)((int64_t)nqb * a.h * a.n_batch));
+  if (a.rk == 1)
+    hipLaunchKernelGGL((prefill_mfma32_kernel<1>), grid, dim3(256), (Pf32Cfg<1>::kLds), st, a, nqb);
+  else if (a.rk == 2)
+    hipLaunchKernelGGL((prefill_mfma32_kernel<2>), grid, dim3(256), (Pf32Cfg<2>::kLds), st, a, nqb);
+  else
+    hipLaunchKernelGGL((prefill_mfma32_kernel<4>), grid, dim3(256), (Pf32Cfg<4>::kLds), st, a, nqb);
+  return hipGetLastError();
+}
+
+}  // namespace tpa
