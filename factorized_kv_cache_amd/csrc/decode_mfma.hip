@@ -12,9 +12,10 @@
 //    q^T held in registers for the whole kernel as a bf16 hi + lo pair (two
 //    products; the cache rows are bf16 already, so the scores carry
 //    fp32-level accuracy: a bf16 query alone costs ~2^-9 of each score, which
-//    sharp heads at long context turn into output errors near 5e-3).  Each
-//    lane loads one contiguous d_h/4 slice of its row; the same k-slot mapping
-//    is used for q, so the contraction is unchanged.
+//    sharp heads at long context turn into output errors near 5e-3).  In
+//    k-step ks lane group lg loads d = 32*ks + 8*lg .. +7 of its row, so each
+//    load instruction reads whole 64-byte pieces of 16 rows; the same k-slot
+//    mapping is used for q, so the contraction is unchanged.
 //  * the head factor: every lane's 4 output rows of a tile are R whole tokens'
 //    ranks (R in {1,2,4}), so s_t = sum_r A_K[t,head,r] P[(t,r),head] is
 //    lane-local; the block maximum per head crosses the four lane groups with
@@ -27,7 +28,12 @@
 //
 // At d_h = 64 (up to 32 heads, 16 at rank 1) each wave keeps two blocks' loads
 // in flight, both issued before the query is formed; at d_h = 128 or with more
-// heads the registers go to a second resident wave instead.
+// heads the registers go to a second resident wave instead, and the single
+// register set is reloaded with the wave's next block part by part as soon as
+// the current block has consumed a part (B_V once it is in LDS; where the
+// registers allow, B~_K after the score products and the head factors after
+// the softmax), so the wave keeps loads in flight through its compute: at
+// 8 x 131073 keys, h 32, d_h 128 the call went from 260-263 to 255 us.
 // The four waves of a workgroup merge their (m, l, O) through LDS in a fixed
 // order and write one partial per head to the workspace; the combine pass,
 // shared with the general kernel, merges the chunks in index order.  (Merging
@@ -104,7 +110,16 @@ struct DecodeMfmaCfg {
   static constexpr size_t kLoopBytes = 4 * 32 * LROW * sizeof(bf16_t);
   // the query's lo half in LDS instead of registers (lane-major, 16 bytes a
   // lane per (head tile, k-step)) where the registers would spill
-  static constexpr bool kQloLds = (DH == 64 && HT == 4) || (DH == 128 && R == 1 && HT == 2);
+  static constexpr bool kQloLds = (DH == 64 && HT == 4) || (DH == 128 && HT == 2);
+  // which parts of the next block are loaded during the current one's compute
+  // (each keeps its registers live through the rest of the block)
+  // (bit 0: B_V, bit 1: B~_K, bit 2: head factors; chosen so none spills).
+  // Only where a wave has a single register set: with two sets in flight the
+  // rolling loads measured no better (147 against 146 us at 32 x 16385 keys).
+  static constexpr int kRoll = kPrefetch ? 0
+                               : DH == 128 ? (HT == 2 ? (R == 1 ? 0 : R == 2 ? 1 : 7) : 7)
+                               : (R == 1 && HT == 3 ? 1 : 7);
+  static constexpr bool kRollBV = kRoll & 1, kRollBK = kRoll & 2, kRollHeads = kRoll & 4;
   static constexpr size_t kQloBytes = kQloLds ? (size_t)4 * HT * KS * 64 * 16 : 0;   // four waves
   static constexpr size_t kMergeBytes = (8 * HP + 2 * HP * OST) * sizeof(float);
   static constexpr size_t kLds =
@@ -136,11 +151,11 @@ struct ChunkBase {
   const bf16_t* bv;
 };
 
+// The three parts of a value block's loads: B_V (40% of the bytes at R = 2),
+// the B~_K operand slices, the head factors.  Rows past `last` are clamped to
+// it (their scores are masked).
 template <int DH, int R, int HT>
-__device__ __forceinline__ void load_block(BlockRegs<DH, R, HT>& g, const ChunkBase& cb, int h, int tb, int last,
-                                           int lane) {
-  using C = DecodeMfmaCfg<DH, R, HT>;
-  const int li = lane & 15, lg = lane >> 4;
+__device__ __forceinline__ void load_bv(BlockRegs<DH, R, HT>& g, const ChunkBase& cb, int tb, int last, int lane) {
   // B_V rows of the block, 16-byte piece u*64 + lane of the block's 64*DH
   // bytes: every load instruction reads whole contiguous cache lines.
 #pragma unroll
@@ -151,15 +166,31 @@ __device__ __forceinline__ void load_block(BlockRegs<DH, R, HT>& g, const ChunkB
     tok = tok < last ? tok : last;
     g.bv[u] = *reinterpret_cast<const uint4*>(cb.bv + ((tok * R + row % R) * DH + col));
   }
+}
+
+template <int DH, int R, int HT>
+__device__ __forceinline__ void load_bk(BlockRegs<DH, R, HT>& g, const ChunkBase& cb, int tb, int last, int lane) {
+  using C = DecodeMfmaCfg<DH, R, HT>;
+  const int li = lane & 15, lg = lane >> 4;
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     const int row = st * 16 + li;
     int tok = tb + row / R;
     tok = tok < last ? tok : last;
-    const uint4* src = reinterpret_cast<const uint4*>(cb.bk + ((tok * R + row % R) * DH + lg * (DH / 4)));
+    // k-step ks takes d = 32*ks .. 32*ks + 31, lane group lg its 8-wide slice
+    // 8*lg: one load instruction reads 64 contiguous bytes of each of the
+    // tile's 16 rows
+    const bf16_t* src = cb.bk + ((tok * R + row % R) * DH + 8 * lg);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) g.bk[st][ks] = src[ks];
+    for (int ks = 0; ks < C::KS; ++ks) g.bk[st][ks] = *reinterpret_cast<const uint4*>(src + 32 * ks);
   }
+}
+
+template <int DH, int R, int HT>
+__device__ __forceinline__ void load_heads(BlockRegs<DH, R, HT>& g, const ChunkBase& cb, int h, int tb, int last,
+                                           int lane) {
+  using C = DecodeMfmaCfg<DH, R, HT>;
+  const int li = lane & 15, lg = lane >> 4;
   typedef typename RankWord<R>::type W;
 #pragma unroll
   for (int st = 0; st < 2; ++st)
@@ -178,7 +209,25 @@ __device__ __forceinline__ void load_block(BlockRegs<DH, R, HT>& g, const ChunkB
 }
 
 template <int DH, int R, int HT>
-__device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf16_t* lbv, int tb, int last,
+__device__ __forceinline__ void load_block(BlockRegs<DH, R, HT>& g, const ChunkBase& cb, int h, int tb, int last,
+                                           int lane) {
+  load_bv<DH, R, HT>(g, cb, tb, last, lane);
+  load_bk<DH, R, HT>(g, cb, tb, last, lane);
+  load_heads<DH, R, HT>(g, cb, h, tb, last, lane);
+}
+
+// Where the next value block's loads come from, for the rolling prefetch:
+// each part of the block's registers is reloaded with the next block as soon
+// as the current block has consumed it.
+struct NextBlock {
+  bool valid;
+  ChunkBase cb;
+  int tb, last;
+};
+
+template <int DH, int R, int HT>
+__device__ __forceinline__ void compute_block(BlockRegs<DH, R, HT>& g, bf16_t* lbv, int tb, int last,
+                                              const NextBlock& nx, int h,
                                               int lane, const bf16x8_t (&qop)[HT][DecodeMfmaCfg<DH, R, HT>::KS],
                                               const bf16x8_t (&qlo)[HT][DecodeMfmaCfg<DH, R, HT>::KS],
                                               const bf16x8_t* qlo_lds,
@@ -197,6 +246,7 @@ __device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf1
     dst[0] = make_uint2(g.bv[u].x, g.bv[u].y);
     dst[1] = make_uint2(g.bv[u].z, g.bv[u].w);
   }
+  if (C::kRollBV && nx.valid) load_bv<DH, R, HT>(g, nx.cb, nx.tb, nx.last, lane);
 
   // scores on the matrix cores
   f32x4_t sacc[2][HT];
@@ -219,6 +269,7 @@ __device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf1
       }
       sacc[st][ht] = kTwoChains ? acch + accl : acch;
     }
+  if (C::kRollBK && nx.valid) load_bk<DH, R, HT>(g, nx.cb, nx.tb, nx.last, lane);
 
   // online softmax per head, and the value-product operand C
   bf16x8_t cop[HT];
@@ -262,6 +313,7 @@ __device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf1
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[ht][dt] *= alpha;
   }
+  if (C::kRollHeads && nx.valid) load_heads<DH, R, HT>(g, nx.cb, h, nx.tb, nx.last, lane);
 
   // value product: A operand = B_V^T read from LDS in the k-slot order
   wave_lds_fence();
@@ -279,6 +331,12 @@ __device__ __forceinline__ void compute_block(const BlockRegs<DH, R, HT>& g, bf1
     for (int ht = 0; ht < HT; ++ht) oacc[ht][dt] = mfma_bf16(bvop, cop[ht], oacc[ht][dt]);
   }
   wave_lds_fence();
+  // the parts of the next block not loaded above
+  if (nx.valid) {
+    if constexpr (!C::kRollBV) load_bv<DH, R, HT>(g, nx.cb, nx.tb, nx.last, lane);
+    if constexpr (!C::kRollBK) load_bk<DH, R, HT>(g, nx.cb, nx.tb, nx.last, lane);
+    if constexpr (!C::kRollHeads) load_heads<DH, R, HT>(g, nx.cb, h, nx.tb, nx.last, lane);
+  }
 }
 
 // PAGED: cache rows through the block table, and per-sequence key counts.
@@ -323,6 +381,25 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
     }
   };
   const int nvb = (last + VBT) / VBT;
+  // The load source of value block vb (valid when the block exists).
+  auto next_of = [&](int vb) {
+    NextBlock nx;
+    nx.valid = vb < nvb;
+    if constexpr (PAGED) {
+      const int64_t row = paged_row(a.pm, b, t0 + (int64_t)(nx.valid ? vb : 0) * VBT);
+      nx.cb = {reinterpret_cast<const bf16_t*>(a.c_ak) + row * h * R,
+               reinterpret_cast<const bf16_t*>(a.c_bk) + row * R * DH,
+               reinterpret_cast<const bf16_t*>(a.c_av) + row * h * R,
+               reinterpret_cast<const bf16_t*>(a.c_bv) + row * R * DH};
+      nx.tb = 0;
+      nx.last = last - vb * VBT;
+    } else {
+      nx.cb = cb;
+      nx.tb = vb * VBT;
+      nx.last = last;
+    }
+    return nx;
+  };
 
   // The first blocks' loads go out before the query is formed (two blocks per
   // wave at d_h = 64, one at d_h = 128).
@@ -357,7 +434,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
       const int head = ht * 16 + li;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int d0 = lg * (DH / 4) + 8 * ks;
+        const int d0 = 32 * ks + 8 * lg;   // the slot mapping of the B~_K operand
         float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = 0.f;
@@ -401,21 +478,30 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
   }
 
   bf16_t* lbv = reinterpret_cast<bf16_t*>(smem) + wave * 32 * LROW;
+  // Each register set is reloaded with its next block part by part while the
+  // current block is computed (compute_block), so loads stay in flight.
+  const NextBlock none = {false, cb, 0, 0};
   if constexpr (C::kPrefetch) {
     // two register sets in flight: blocks vb and vb+4 of this wave
     for (int vb = wave; vb < nvb; vb += 8) {
-      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
+      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
       if (vb + 8 < nvb) load(r0, vb + 8);
       if (vb + 4 < nvb) {
-        compute_block<DH, R, HT>(r1, lbv, (vb + 4) * VBT, last, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
+        compute_block<DH, R, HT>(r1, lbv, (vb + 4) * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run,
+                                 oacc);
         if (vb + 12 < nvb) load(r1, vb + 12);
       }
     }
-  } else {
+  } else if constexpr (C::kRoll == 0) {
     for (int vb = wave; vb < nvb; vb += 4) {
       if (vb != wave) load(r0, vb);
-      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
+      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
     }
+  } else {
+    // one register set, reloaded with the wave's next block part by part
+    for (int vb = wave; vb < nvb; vb += 4)
+      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, next_of(vb + 4), h, lane, qop, qlo, qlo_lds, m_run, l_run,
+                               oacc);
   }
 
   // ---- merge the four waves (fixed order) and write this chunk's partial
