@@ -22,8 +22,11 @@
 // 16 (w % 4) .. + 15 of each block and a group of 16-column tiles (w / 4).
 // The products run transposed on the matrix cores,
 //   G^T[(h, r), t] = sum_i alpha[h,r,i] cos(t th_i) + beta[h,r,i] sin(t th_i),
-// with each lane forming its key's angle features in registers (fp64 angles,
-// as in every rotation here; features and alpha/beta both as hi + lo, three
+// with each lane forming its key's angle features in registers as one complex
+// product each: the wave's anchor (cos, sin)(t0 th_i) at its first key t0 of
+// the block (one fp64-reduced angle per lane per block, in a wave-private LDS
+// slot) turned by (cos, sin)(j th_i) for the key's offset j < 16 from a table
+// built once per workgroup (features and alpha/beta both as hi + lo, three
 // products: fp32-level accuracy).  Lane (li, lg) then holds key li and the four
 // consecutive columns 16 n0 + 4 lg .. + 3 of tile n0.  Columns are numbered
 // head * RKP + rank, RKP in {1, 2, 4} the smallest power of two >= R_K (ranks
@@ -48,13 +51,21 @@ typedef uint32_t sh_u32x4 __attribute__((ext_vector_type(4)));
 
 // LDS carve of the decode kernel (in bytes from the start).
 struct SharedLds {
-  size_t rev, stage, bhi, blo, end;
+  size_t rev, stage, bhi, blo, rot, anch, end;
   int np, nt, ldb;
 };
 
+// Keys per wave of a block: the features of key t0 + j (j < kShSub) are the
+// wave's anchor (cos, sin)(t0 th_i) turned by (cos, sin)(j th_i) from a table
+// laid out [pair i][j] with rows of kShRotLd entries: the 16 lanes of a lane
+// group read one row's 128 contiguous bytes, and the four groups' rows (4
+// pairs apart) start 16 banks apart.
+constexpr int kShSub = 16;
+constexpr int kShRotLd = 18;
+
 __host__ __device__ inline int shared_rkp(int rk) { return rk <= 1 ? 1 : (rk <= 2 ? 2 : 4); }
 
-__host__ __device__ inline SharedLds shared_carve(int h, int dh, int rq, int rk) {
+__host__ __device__ inline SharedLds shared_carve(int h, int dh, int rq, int rk, int waves) {
   SharedLds c;
   c.np = dh / 2;
   c.nt = (h * shared_rkp(rk) + 15) / 16;   // 16-column tiles of G^T
@@ -70,6 +81,8 @@ __host__ __device__ inline SharedLds shared_carve(int h, int dh, int rq, int rk)
   o = (o + 15) / 16 * 16;
   c.bhi = o; o += sizeof(bf16_t) * c.nt * 16 * c.ldb;
   c.blo = o; o += sizeof(bf16_t) * c.nt * 16 * c.ldb;
+  c.rot = o; o += sizeof(float) * 2 * kShRotLd * c.np;   // [i][j] (cos, sin)(j th_i)
+  c.anch = o; o += sizeof(float) * 2 * waves * c.np;     // [wave][i] (cos, sin)(t0 th_i)
   c.end = o;
   return c;
 }
@@ -153,6 +166,13 @@ struct TileFactors {
   }
 };
 
+// LDS written by lanes of a wave made visible to the other lanes of that wave.
+__device__ __forceinline__ void shared_wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // x = hi + lo as bf16 pairs (round to nearest even each).
 __device__ __forceinline__ void split_pair8(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
   float h[8], l[8];
@@ -178,7 +198,7 @@ __global__ void __launch_bounds__(WIDE ? 256 : 64 * 4 * kShMaxG, WIDE ? 3 : 1) s
   using TF = TileFactors<T, HPL, MRV>;
   extern __shared__ __align__(16) unsigned char shb[];
   const int h = a.h, dh = a.d_h, rk = a.rk, rv = a.rv, rq = a.rq > 0 ? a.rq : 1;
-  const SharedLds L = shared_carve(h, dh, a.rq, rk);
+  const SharedLds L = shared_carve(h, dh, a.rq, rk, blockDim.x >> 6);
   const int np = L.np, nt = L.nt, ldb = L.ldb;
   double* s_rev = reinterpret_cast<double*>(shb + L.rev);
   float* s_aq = reinterpret_cast<float*>(shb + L.stage);     // [h][R_Q]
@@ -187,6 +207,7 @@ __global__ void __launch_bounds__(WIDE ? 256 : 64 * 4 * kShMaxG, WIDE ? 3 : 1) s
   float* s_red = reinterpret_cast<float*>(shb + L.stage);      // [4][h][2 + MRV] after the loop
   bf16_t* bhi = reinterpret_cast<bf16_t*>(shb + L.bhi);        // [nt*16][d_h + 8] alpha/beta rows, hi
   bf16_t* blo = reinterpret_cast<bf16_t*>(shb + L.blo);        //                                  lo
+  float2* s_rot = reinterpret_cast<float2*>(shb + L.rot);      // [np][kShRotLd]
   const int c = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int64_t t0 = (int64_t)c * chunk;
@@ -214,6 +235,15 @@ __global__ void __launch_bounds__(WIDE ? 256 : 64 * 4 * kShMaxG, WIDE ? 3 : 1) s
   }
   for (int idx = threadIdx.x; idx < rk * dh; idx += blockDim.x) s_bk[idx] = ldf(BK, idx);
   __syncthreads();
+  // ---- the key-offset rotations (cos, sin)(j th_i), j < kShSub, angles
+  //      reduced in fp64 as everywhere
+  for (int idx = threadIdx.x; idx < kShSub * np; idx += blockDim.x) {
+    const int i = idx / kShSub, j = idx - i * kShSub;
+    double turns = (double)j * s_rev[i];
+    turns -= rint(turns);
+    const float ang = (float)turns;
+    s_rot[i * kShRotLd + j] = make_float2(__builtin_amdgcn_cosf(ang), __builtin_amdgcn_sinf(ang));
+  }
   // ---- alpha/beta rows, column n = head RKP + r, feature 2i (alpha_i) and
   //      2i+1 (beta_i), as bf16 hi + lo; columns with r >= R_K or past the last
   //      head are zero.  The query pair (scaled by log2(e) / (R_Q R_K sqrt(d_h)))
@@ -257,9 +287,21 @@ __global__ void __launch_bounds__(WIDE ? 256 : 64 * 4 * kShMaxG, WIDE ? 3 : 1) s
       for (int r = 0; r < MRV; ++r) w[k][j][r] = 0.f;
     }
   const int ksn = dh / 32;
+  float2* s_anch = reinterpret_cast<float2*>(shb + L.anch) + wave * np;   // this wave's anchors
+  const float2* rot_j = s_rot + li;                                       // key offset li
   for (int64_t blk0 = t0; blk0 < t1; blk0 += kShB) {
     const int64_t key = blk0 + 16 * mt + li;
     const bool valid = key < t1;
+    // the wave's anchors (cos, sin)(t0 th_i) at its first key t0 = blk0 + 16 mt,
+    // one pair per lane (the previous block's reads are done first)
+    shared_wave_lds_fence();
+    for (int i = lane; i < np; i += 64) {
+      double turns = (double)(blk0 + 16 * mt) * s_rev[i];
+      turns -= rint(turns);
+      const float ang = (float)turns;
+      s_anch[i] = make_float2(__builtin_amdgcn_cosf(ang), __builtin_amdgcn_sinf(ang));
+    }
+    shared_wave_lds_fence();
     // the head factors of the lane's key go out first; the products hide them
     TF cur[NT];
 #pragma unroll
@@ -268,8 +310,8 @@ __global__ void __launch_bounds__(WIDE ? 256 : 64 * 4 * kShMaxG, WIDE ? 3 : 1) s
       if (n0 < nt && valid) cur[k].load(AK, AV, row0 + key, (16 * n0 + 4 * lg) / RKP, h, rk, rv, vk, vv);
     }
     // ---- per k-step: the features of key li, 32 ks + 8 lg .. + 7 = (cos, sin)
-    //      of pairs 16 ks + 4 lg .. + 3, then that step of every tile's product
-    const double pos = (double)key;
+    //      of pairs 16 ks + 4 lg .. + 3 (the anchor turned by li th_i: one
+    //      complex product each), then that step of every tile's product
     f32x4_t acc[NT];
 #pragma unroll
     for (int k = 0; k < NT; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -277,13 +319,12 @@ __global__ void __launch_bounds__(WIDE ? 256 : 64 * 4 * kShMaxG, WIDE ? 3 : 1) s
     for (int ks = 0; ks < kShMaxKS; ++ks) {
       if (ks >= ksn) break;
       float x[8];
+      const int p0 = 16 * ks + 4 * lg;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        double turns = pos * s_rev[16 * ks + 4 * lg + e];
-        turns -= rint(turns);
-        const float ang = (float)turns;
-        x[2 * e] = __builtin_amdgcn_cosf(ang);
-        x[2 * e + 1] = __builtin_amdgcn_sinf(ang);
+        const float2 an = s_anch[p0 + e], ro = rot_j[(p0 + e) * kShRotLd];
+        x[2 * e] = fmaf(an.x, ro.x, -an.y * ro.y);       // cos((t0 + li) th)
+        x[2 * e + 1] = fmaf(an.y, ro.x, an.x * ro.y);    // sin((t0 + li) th)
       }
       bf16x8_t fh, fl;
       split_pair8(x, fh, fl);
@@ -489,7 +530,7 @@ SharedPlan plan_shared_decode(int dtype, const AttnArgs& a, int64_t ctx_len) {
   const bool wide = s.groups == 1 && shared_wide(dtype == kF32 ? 4 : 2, s.nt_max, s.hpl, s.mrv);
   const int groups = s.groups > 0 ? s.groups : 1;
   int64_t per_cu = wide ? 3 : 4 / groups;
-  const size_t lds = shared_carve(a.h, a.d_h, a.rq, a.rk).end;
+  const size_t lds = shared_carve(a.h, a.d_h, a.rq, a.rk, 4 * groups).end;
   const size_t cu_lds = shared_device_lds();
   if (lds > 0 && cu_lds > 0 && (int64_t)(cu_lds / lds) < per_cu) per_cu = (int64_t)(cu_lds / lds);
   if (per_cu < 1) per_cu = 1;
@@ -506,8 +547,9 @@ SharedPlan plan_shared_decode(int dtype, const AttnArgs& a, int64_t ctx_len) {
 // up to 4; the per-query alpha/beta rows must fit the device's LDS.
 bool shared_decode_supported(int dtype, const AttnArgs& a) {
   if (a.d_h % 32 || a.d_h > 32 * kShMaxKS || a.rk < 1 || a.rk > 4 || a.rv < 1 || a.rv > 4) return false;
-  if (shared_shape(dtype, a).groups == 0) return false;
-  return shared_carve(a.h, a.d_h, a.rq, a.rk).end <= shared_device_lds();
+  const SharedShape sh = shared_shape(dtype, a);
+  if (sh.groups == 0) return false;
+  return shared_carve(a.h, a.d_h, a.rq, a.rk, 4 * sh.groups).end <= shared_device_lds();
 }
 
 size_t shared_decode_workspace_bytes(const SharedPlan& p, const AttnArgs& a) {
@@ -524,7 +566,7 @@ static void launch_shared_t(const AttnArgs& a, const RopeTable& tab, int64_t ctx
     if (WIDE && groups != 1) return;
     const dim3 grid((unsigned)p.n_chunks, (unsigned)a.n_batch);
     hipLaunchKernelGGL((shared_decode_kernel<T, NT, HPL, MRV, WIDE>), grid, dim3(256 * groups),
-                       shared_carve(a.h, a.d_h, a.rq, a.rk).end, st, a, tab, ctx_len, p.chunk_tokens,
+                       shared_carve(a.h, a.d_h, a.rq, a.rk, 4 * groups).end, st, a, tab, ctx_len, p.chunk_tokens,
                        (int)p.n_chunks, ws);
     hipLaunchKernelGGL((shared_combine_kernel<T, MRV>),
                        dim3((unsigned)((a.h + kShCombWaves - 1) / kShCombWaves), (unsigned)a.n_batch),
