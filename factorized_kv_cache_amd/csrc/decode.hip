@@ -18,6 +18,7 @@
 #include <mutex>
 
 #include "kernels.h"
+#include "mfma.h"
 
 namespace tpa {
 
@@ -155,10 +156,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_generic_kernel(AttnArgs
 // Log-sum-exp merge of the chunk partials of one (head, sequence); one
 // workgroup per (head, sequence).  Thread (d, g) sums the chunks c = g, g+G, ...
 // of element d (G = 256 / d_h groups) in that order, loading 32 of its
-// partial values at a time (the first 32 together with the chunk maxima and
-// sums), so that the merge costs one memory round trip per 32 chunks of a
-// group (loaded one by one, the 32 chunks of a group at 8 x 131073 keys and
-// d_h 128 took 10.8 us); groups are then added in order g = 0..G-1.
+// partial values at a time, so that the merge costs one memory round trip per
+// 32 chunks of a group (loaded one by one, the 32 chunks of a group at
+// 8 x 131073 keys and d_h 128 took 10.8 us); groups are then added in order
+// g = 0..G-1.  The chunk maxima and sums are loaded first, so waiting for them
+// leaves the partial values in flight, and the overall maximum M and the sum
+// L = sum_c 2^(m_c - M) l_c are wave reductions (every wave forms the same
+// bits: the pairing order is fixed).
 constexpr int kCombineThreads = 256;
 constexpr int kCombineRegs = 32;
 constexpr int kCombineMaxChunks = 2048;   // LDS: maxima and sums of the chunks
@@ -176,26 +180,40 @@ __global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(AttnArg
   const int64_t cstride = (int64_t)h * (dh + 2);
   const int G = kCombineThreads / dh;
   const int d = threadIdx.x % dh, g = threadIdx.x / dh;
+  const int lane = threadIdx.x & 63;
   const bool active = g < G;
   const int nc = (int)n_chunks;
 
+  float m0 = -INFINITY, l0 = 0.f;
+  if ((int)threadIdx.x < nc) {
+    m0 = P[(int64_t)threadIdx.x * cstride];
+    l0 = P[(int64_t)threadIdx.x * cstride + 1];
+  }
   float accv[kCombineRegs];
 #pragma unroll
   for (int j = 0; j < kCombineRegs; ++j) {
     const int c = g + G * j;
     accv[j] = (active && c < nc) ? P[(int64_t)c * cstride + 2 + d] : 0.f;
   }
-  for (int c = threadIdx.x; c < nc; c += blockDim.x) {
+  if ((int)threadIdx.x < nc) {
+    mloc[threadIdx.x] = m0;
+    lloc[threadIdx.x] = l0;
+  }
+  for (int c = threadIdx.x + blockDim.x; c < nc; c += blockDim.x) {
     mloc[c] = P[(int64_t)c * cstride];
     lloc[c] = P[(int64_t)c * cstride + 1];
   }
   __syncthreads();
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, mloc[c]);
+  float mx = -INFINITY;
+  for (int c = lane; c < nc; c += 64) mx = fmaxf(mx, mloc[c]);
+  const float M = wave_max(mx);
   if (M == -INFINITY) {   // every chunk empty: a sequence without keys
-    if (threadIdx.x < dh) stf(reinterpret_cast<T*>(a.out), (b * h + hh) * dh + threadIdx.x, 0.f);
+    if ((int)threadIdx.x < dh) stf(reinterpret_cast<T*>(a.out), (b * h + hh) * dh + threadIdx.x, 0.f);
     return;
   }
+  float lp = 0.f;
+  for (int c = lane; c < nc; c += 64) lp = fmaf(fast_exp2(mloc[c] - M), lloc[c], lp);
+  const float L = wave_sum(lp);
   float O = 0.f;
 #pragma unroll
   for (int j = 0; j < kCombineRegs; ++j) {
@@ -216,9 +234,7 @@ __global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(AttnArg
   }
   part[threadIdx.x] = O;
   __syncthreads();
-  if (threadIdx.x < dh) {
-    float L = 0.f;
-    for (int c = 0; c < nc; ++c) L = fmaf(fast_exp2(mloc[c] - M), lloc[c], L);
+  if ((int)threadIdx.x < dh) {
     float tot = 0.f;
     for (int gg = 0; gg < G; ++gg) tot += part[gg * dh + d];
     T* out = reinterpret_cast<T*>(a.out);

@@ -103,7 +103,9 @@ struct DecodeMfmaCfg {
   static constexpr int NT = 4 / R;       // tokens per lane per score tile
   static constexpr int VBT = 32 / R;     // tokens per value block
   static constexpr int HP = HT * 16;     // padded head count
-  static constexpr int LROW = DH + 4;    // LDS row stride (bf16): 4 rows apart = 8 banks apart
+  // LDS row stride (bf16): 16-byte aligned rows, and the four rows one lane
+  // group reads with a transposed read fall on disjoint banks
+  static constexpr int LROW = DH + 16;
   static constexpr int OST = DH + 4;     // LDS row stride (f32) of the merge buffer
   // a second block in flight (its registers spill beyond these sizes)
   static constexpr bool kPrefetch = DH == 64 && (R == 1 ? HT == 1 : HT <= 2);
@@ -119,7 +121,6 @@ struct DecodeMfmaCfg {
   static constexpr int kRoll = kPrefetch ? 0
                                : DH == 128 ? (HT == 2 ? (R == 1 ? 0 : R == 2 ? 1 : 7) : 7)
                                : (R == 1 && HT == 3 ? 1 : 7);
-  static constexpr bool kRollBV = kRoll & 1, kRollBK = kRoll & 2, kRollHeads = kRoll & 4;
   static constexpr size_t kQloBytes = kQloLds ? (size_t)4 * HT * KS * 64 * 16 : 0;   // four waves
   static constexpr size_t kMergeBytes = (8 * HP + 2 * HP * OST) * sizeof(float);
   static constexpr size_t kLds =
@@ -225,7 +226,7 @@ struct NextBlock {
   int tb, last;
 };
 
-template <int DH, int R, int HT>
+template <int DH, int R, int HT, int ROLL>
 __device__ __forceinline__ void compute_block(BlockRegs<DH, R, HT>& g, bf16_t* lbv, int tb, int last,
                                               const NextBlock& nx, int h,
                                               int lane, const bf16x8_t (&qop)[HT][DecodeMfmaCfg<DH, R, HT>::KS],
@@ -237,16 +238,14 @@ __device__ __forceinline__ void compute_block(BlockRegs<DH, R, HT>& g, bf16_t* l
   constexpr int KS = C::KS, DT = C::DT, NT = C::NT, LROW = C::LROW;
   const int li = lane & 15, lg = lane >> 4;
 
-  // B_V pieces -> wave-private LDS tile
+  // B_V pieces -> wave-private LDS tile, one 16-byte store each
 #pragma unroll
   for (int u = 0; u < DH / 16; ++u) {
     const int piece = u * 64 + lane;
     const int row = piece / (DH / 8), col = (piece % (DH / 8)) * 8;
-    uint2* dst = reinterpret_cast<uint2*>(lbv + row * LROW + col);
-    dst[0] = make_uint2(g.bv[u].x, g.bv[u].y);
-    dst[1] = make_uint2(g.bv[u].z, g.bv[u].w);
+    *reinterpret_cast<bf16x8_t*>(lbv + row * LROW + col) = as_bf16x8(g.bv[u]);
   }
-  if (C::kRollBV && nx.valid) load_bv<DH, R, HT>(g, nx.cb, nx.tb, nx.last, lane);
+  if ((ROLL & 1) && nx.valid) load_bv<DH, R, HT>(g, nx.cb, nx.tb, nx.last, lane);
 
   // scores on the matrix cores
   f32x4_t sacc[2][HT];
@@ -269,7 +268,7 @@ __device__ __forceinline__ void compute_block(BlockRegs<DH, R, HT>& g, bf16_t* l
       }
       sacc[st][ht] = kTwoChains ? acch + accl : acch;
     }
-  if (C::kRollBK && nx.valid) load_bk<DH, R, HT>(g, nx.cb, nx.tb, nx.last, lane);
+  if ((ROLL & 2) && nx.valid) load_bk<DH, R, HT>(g, nx.cb, nx.tb, nx.last, lane);
 
   // online softmax per head, and the value-product operand C
   bf16x8_t cop[HT];
@@ -313,29 +312,27 @@ __device__ __forceinline__ void compute_block(BlockRegs<DH, R, HT>& g, bf16_t* l
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[ht][dt] *= alpha;
   }
-  if (C::kRollHeads && nx.valid) load_heads<DH, R, HT>(g, nx.cb, h, nx.tb, nx.last, lane);
+  if ((ROLL & 4) && nx.valid) load_heads<DH, R, HT>(g, nx.cb, h, nx.tb, nx.last, lane);
 
-  // value product: A operand = B_V^T read from LDS in the k-slot order
+  // value product: A operand = B_V^T in the k-slot order of the C operand
+  // (slot j of lane group lg: row 4*lg + j for j < 4, row 16 + 4*lg + j - 4
+  // after), two transposed reads of four rows at column 16*dt + li each
   wave_lds_fence();
+  const bf16_t* vrow = lbv + (4 * lg + (li >> 2)) * LROW + 4 * (li & 3);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    const int d = dt * 16 + li;
-    u16x8_t e;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = (j < 4) ? 4 * lg + j : 16 + 4 * lg + (j - 4);
-      e[j] = lbv[row * LROW + d];
-    }
-    const bf16x8_t bvop = __builtin_bit_cast(bf16x8_t, e);
+    const uint2 lo = lds_read_tr16(vrow + dt * 16);
+    const uint2 hi = lds_read_tr16(vrow + 16 * LROW + dt * 16);
+    const bf16x8_t bvop = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) oacc[ht][dt] = mfma_bf16(bvop, cop[ht], oacc[ht][dt]);
   }
   wave_lds_fence();
   // the parts of the next block not loaded above
   if (nx.valid) {
-    if constexpr (!C::kRollBV) load_bv<DH, R, HT>(g, nx.cb, nx.tb, nx.last, lane);
-    if constexpr (!C::kRollBK) load_bk<DH, R, HT>(g, nx.cb, nx.tb, nx.last, lane);
-    if constexpr (!C::kRollHeads) load_heads<DH, R, HT>(g, nx.cb, h, nx.tb, nx.last, lane);
+    if constexpr (!(ROLL & 1)) load_bv<DH, R, HT>(g, nx.cb, nx.tb, nx.last, lane);
+    if constexpr (!(ROLL & 2)) load_bk<DH, R, HT>(g, nx.cb, nx.tb, nx.last, lane);
+    if constexpr (!(ROLL & 4)) load_heads<DH, R, HT>(g, nx.cb, h, nx.tb, nx.last, lane);
   }
 }
 
@@ -478,29 +475,32 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
   }
 
   bf16_t* lbv = reinterpret_cast<bf16_t*>(smem) + wave * 32 * LROW;
+  // the paged form's page lookups leave no registers for a rolled B_V at
+  // d_h = 128 with two head tiles and rank 2
+  constexpr int kRoll = (PAGED && DH == 128 && HT == 2 && R == 2) ? 0 : C::kRoll;
   // Each register set is reloaded with its next block part by part while the
   // current block is computed (compute_block), so loads stay in flight.
   const NextBlock none = {false, cb, 0, 0};
   if constexpr (C::kPrefetch) {
     // two register sets in flight: blocks vb and vb+4 of this wave
     for (int vb = wave; vb < nvb; vb += 8) {
-      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
+      compute_block<DH, R, HT, kRoll>(r0, lbv, vb * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
       if (vb + 8 < nvb) load(r0, vb + 8);
       if (vb + 4 < nvb) {
-        compute_block<DH, R, HT>(r1, lbv, (vb + 4) * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run,
+        compute_block<DH, R, HT, kRoll>(r1, lbv, (vb + 4) * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run,
                                  oacc);
         if (vb + 12 < nvb) load(r1, vb + 12);
       }
     }
-  } else if constexpr (C::kRoll == 0) {
+  } else if constexpr (kRoll == 0) {
     for (int vb = wave; vb < nvb; vb += 4) {
       if (vb != wave) load(r0, vb);
-      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
+      compute_block<DH, R, HT, kRoll>(r0, lbv, vb * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
     }
   } else {
     // one register set, reloaded with the wave's next block part by part
     for (int vb = wave; vb < nvb; vb += 4)
-      compute_block<DH, R, HT>(r0, lbv, vb * VBT, last, next_of(vb + 4), h, lane, qop, qlo, qlo_lds, m_run, l_run,
+      compute_block<DH, R, HT, kRoll>(r0, lbv, vb * VBT, last, next_of(vb + 4), h, lane, qop, qlo, qlo_lds, m_run, l_run,
                                oacc);
   }
 

@@ -24,6 +24,17 @@ __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) 
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// Transposed LDS read (ds_read_b64_tr_b16): the 16 lanes of a group each name
+// an 8-byte piece (4 bf16) of a 4 x 16 block, lane 4r + c the piece at row r,
+// columns 4c .. 4c + 3; lane i receives column i of each of the four rows.
+__device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 __device__ __forceinline__ bf16x8_t pack8(const float* v) {
   const uint4 u = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                              pack_bf16x2(v[6], v[7]));

@@ -44,18 +44,9 @@
 namespace tpa {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 __device__ __forceinline__ f32x16_t mfma32_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Transposed LDS read: the 16 lanes of a group each name an 8-byte piece (4
-// bf16) of a 4 x 16 block; lane i receives element i of each of the four rows.
-__device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
-  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
-  return __builtin_bit_cast(uint2, v);
 }
 
 // max of x over the lanes l and l ^ 32
