@@ -266,10 +266,7 @@ static DecodePlan plan_generic(int64_t ctx_len) {
 // instead left a one-unit chunk per sequence, whose workgroups ran as a nearly
 // empty second round (measured 21.5 -> 19.9 us at 16 x 4097 keys, 169 -> 142
 // us at 32 x 16,385 KV-only, unchanged at 8 x 131,073).
-#ifndef TPA_DECODE_TARGET_WGS
-#define TPA_DECODE_TARGET_WGS 512
-#endif
-constexpr int64_t kDecodeTargetWorkgroups = TPA_DECODE_TARGET_WGS;
+constexpr int64_t kDecodeTargetWorkgroups = 512;
 static DecodePlan plan_mfma(const AttnArgs& a, int64_t ctx_len) {
   DecodePlan p;
   p.kernel = 1;

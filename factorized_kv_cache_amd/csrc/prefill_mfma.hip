@@ -220,7 +220,7 @@ __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t*
 #pragma unroll
         for (int i = 0; i < 4; ++i) bmax = max_nn(bmax, sacc[kt][qt][i]);
       bmax = lane_group_max_nn(bmax);
-      const bool grow = bmax > m_run[qt] + (TPA_PF_LAZY ? C::kRescaleSlack : 0.f);
+      const bool grow = bmax > m_run[qt] + C::kRescaleSlack;
       if (__any(grow)) {
         const float m_new = grow ? bmax : m_run[qt];
         const float alpha = fast_exp2(m_run[qt] - m_new);   // 0 on the first block, 1 where m stays

@@ -6,9 +6,8 @@
 // You Need" review on coreui.cn: Q_t/K_t/V_t equations of 核心机制总结 and the
 // masked softmax attention of the code walk-through 前向传播).  A workgroup owns
 // 256 queries of one head of one sequence; each of its four waves owns 64 of
-// them as two 32-query tiles.  For every key block (32 keys; 64 at rank 1,
-// whose factors take half the registers; at rank 2 the 64-key blocks spill and
-// measured 297 against 277 us for 4 x 4096 tokens):
+// them as two 32-query tiles.  For every key block (64 keys at ranks 1 and 2;
+// 32 at rank 4, whose factors would spill registers at 64):
 //
 //  * rebuild: the whole workgroup forms k_t = sum_r A_K[t,h,r] B~_K[t,r,:] and
 //    v_t likewise (rank pairs through v_dot2_f32_bf16, fp32 sums) and stores
@@ -34,7 +33,10 @@
 //  * the softmax denominators are the sums of the same bf16 probabilities
 //    (v_dot2 against ones), accumulated per lane and joined at the end.
 //    (Taking them on the matrix cores with a ones row, and starting the score
-//    accumulators from -m to drop the subtraction, both measured slower.)
+//    accumulators from -m to drop the subtraction, both measured slower; so
+//    did forming the next block's scores a step ahead from a third buffer,
+//    with or without scheduling groups that interleave the matrix products
+//    with the softmax and rebuild: 4-9% slower at 4 x 4096 tokens.)
 //
 // Query blocks are scheduled heaviest (most keys) first, evenly across XCDs.
 #include "kernels.h"
@@ -60,7 +62,7 @@ struct Pf32Cfg {
   static constexpr int DH = 64;
   static constexpr int QT = 2;                 // 32-query tiles per wave
   static constexpr int BM = 4 * 32 * QT;       // queries per workgroup
-  static constexpr int BN = R == 1 ? 64 : 32;  // keys per block
+  static constexpr int BN = R == 4 ? 32 : 64;  // keys per block
   static constexpr int KT = BN / 32;           // 32-key tiles of the score product
   static constexpr int KS = BN / 16;           // 16-key steps of the value product
   static constexpr int LD = DH + 8;            // LDS row stride (bf16) of K and V
@@ -155,20 +157,26 @@ __device__ __forceinline__ void attend_block32(const bf16_t* k_lds, const bf16_t
   }
 
   // ---- mask (only where the block reaches past a query of this wave, or
-  //      past the keys); value e of a tile is key 8*(e/4) + 4*lh + e%4
+  //      past the keys; a uniform branch).  Value e of tile kt is the key at
+  //      offset 32*kt + 8*(e/4) + 4*lh + e%4 from k0; it is visible iff that
+  //      offset is at most both kend - 1 - k0 and, when causal, the query's
+  //      position - k0.  The offsets are small, so the limits are clamped to
+  //      32-bit values and each element costs one compare against a constant.
   const bool need_mask = (causal && k0 + BN - 1 > wpos0) || (k0 + BN > kend);
   if (need_mask) {
+    const int64_t krel = kend - 1 - k0, qrel = wpos0 - k0;
+    const int klim = (int)(krel < 2 * BN ? krel : 2 * BN);
+    const int qlim = (int)(qrel < 2 * BN ? (qrel > -2 * BN ? qrel : -2 * BN) : 2 * BN);
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int qt = 0; qt < QT; ++qt) {
+      int lim = causal ? min(klim, qlim + 32 * qt + l32) : klim;
+      lim -= 4 * lh;
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t t = k0 + kt * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-          const int64_t p = wpos0 + 32 * qt + l32;
-          const bool ok = t < kend && (!causal || t <= p);
-          if (!ok) sacc[kt][qt][e] = -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e)
+          if (32 * kt + 8 * (e >> 2) + (e & 3) > lim) sacc[kt][qt][e] = -INFINITY;
+    }
   }
 
   // ---- online softmax per query (lazy rescale), P^T operands, row sums
@@ -235,7 +243,9 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma32_kernel(AttnArgs a, int 
   extern __shared__ __align__(16) unsigned char smem[];
   bf16_t* const lds = reinterpret_cast<bf16_t*>(smem);
   // buffer i: K at lds + i*TILE, V at lds + (2 + i)*TILE
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: kept scalar, so the per-block tests on the
+  // wave's positions (skip, mask) are scalar branches
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, lh = lane >> 5;
   // One-dimensional grid.  Work items (query block, head, sequence) in order of
   // decreasing key count are numbered by the linear workgroup id; since

@@ -26,36 +26,12 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 // sum_r a_r * b_r[j] for the 8 elements j of one 16-byte slice per rank.
 // Ranks are paired: word w of rank r holds elements (2w, 2w+1); v_perm_b32
-// regroups them as (rank r, rank r+1) pairs for v_dot2_f32_bf16.
-#ifndef TPA_PF_DOT2
-#define TPA_PF_DOT2 1
-#endif
-#ifndef TPA_PF_LAZY
-#define TPA_PF_LAZY 1
-#endif
-
+// regroups them as (rank r, rank r+1) pairs for v_dot2_f32_bf16.  Rank 1 is a
+// plain product.
 template <int R>
 __device__ __forceinline__ void factor_combine(typename RankWordP<R>::type a, const uint4 (&b)[R], float (&out)[8]) {
-  if constexpr (R == 1 || !TPA_PF_DOT2) {
-    float ar[R];
-    if constexpr (R == 1) ar[0] = bf16_to_f32(a);
-    else if constexpr (R == 2) { ar[0] = __uint_as_float(a << 16); ar[1] = __uint_as_float(a & 0xffff0000u); }
-    else {
-      ar[0] = __uint_as_float(a.x << 16); ar[1] = __uint_as_float(a.x & 0xffff0000u);
-      ar[2] = __uint_as_float(a.y << 16); ar[3] = __uint_as_float(a.y & 0xffff0000u);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) out[j] = 0.f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t w[4] = {b[r].x, b[r].y, b[r].z, b[r].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        out[2 * q] = fmaf(ar[r], __uint_as_float(w[q] << 16), out[2 * q]);
-        out[2 * q + 1] = fmaf(ar[r], __uint_as_float(w[q] & 0xffff0000u), out[2 * q + 1]);
-      }
-    }
-  } else if constexpr (R == 1) {
+  static_assert(R == 1 || R == 2 || R == 4, "ranks 1, 2 and 4");
+  if constexpr (R == 1) {
     const uint32_t w[4] = {b[0].x, b[0].y, b[0].z, b[0].w};
     const float a0 = bf16_to_f32(a);
 #pragma unroll
