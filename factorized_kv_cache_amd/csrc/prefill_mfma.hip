@@ -194,20 +194,27 @@ __device__ __forceinline__ void attend_block(const bf16_t* ks_lds, const bf16_t*
         for (int kb = 0; kb < KB; ++kb) vfe[dt][kb] = read_vt(dt, kb);
     }
 
-    // ---- mask (only where the block reaches past a query of this wave)
+    // ---- mask (only where the block reaches past a query of this wave, or
+    //      past the keys; a uniform branch).  Value i of tile (kt, qt) is the
+    //      key at offset 16*kt + 4*lg + i from k0; it is visible iff that
+    //      offset is at most both kend - 1 - k0 and, when causal, the query's
+    //      position - k0 (limits clamped to 32-bit values: the offsets are
+    //      small).
     const bool need_mask = (causal && k0 + BN - 1 > wpos0) || (k0 + BN > kend);
     if (need_mask) {
+      const int64_t krel = kend - 1 - k0, qrel = wpos0 - k0;
+      const int klim = (int)(krel < 2 * BN ? krel : 2 * BN);
+      const int qlim = (int)(qrel < 2 * BN ? (qrel > -2 * BN ? qrel : -2 * BN) : 2 * BN);
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
+      for (int qt = 0; qt < QT; ++qt) {
+        int lim = causal ? min(klim, qlim + 16 * qt + li) : klim;
+        lim -= 4 * lg;
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t t = k0 + kt * 16 + 4 * lg + i;
-            const int64_t p = wpos0 + 16 * qt + li;
-            const bool ok = t < kend && (!causal || t <= p);
-            if (!ok) sacc[kt][qt][i] = -INFINITY;
-          }
+          for (int i = 0; i < 4; ++i)
+            if (kt * 16 + i > lim) sacc[kt][qt][i] = -INFINITY;
+      }
     }
 
     // ---- online softmax per query (lazy rescale), P^T operands
@@ -263,7 +270,9 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma_kernel(AttnArgs a, int n_
   // buffer i: K at lds + i*KTILE, V^T at lds + 2*KTILE + i*VTILE
 #define KS_BUF(i) (lds + (i) * C::KTILE)
 #define VT_BUF(i) (lds + 2 * C::KTILE + (i) * C::VTILE)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: kept scalar, so the per-block tests on the
+  // wave's positions (skip, mask) are scalar branches
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
   // One-dimensional grid.  Work items (query block, head, sequence) in order of
   // decreasing key count are numbered by the linear workgroup id; since
