@@ -336,6 +336,19 @@ __device__ __forceinline__ void compute_block(BlockRegs<DH, R, HT>& g, bf16_t* l
   }
 }
 
+// Issue priority by progress: a wave that has done fewer of its blocks than
+// the others keeps a higher priority, so the waves of a CU (two workgroups)
+// finish together.  With equal priorities the arbiter favours the oldest
+// waves, and the workgroups dispatched second on each CU ran about 18 %
+// behind the first ones, leaving a tail in which half the CU's waves stream.
+__device__ __forceinline__ void prio_by_progress(int done, int total) {
+  const int ph = (4 * done) / total;   // 0..3, uniform
+  if (ph == 0) __builtin_amdgcn_s_setprio(3);
+  else if (ph == 1) __builtin_amdgcn_s_setprio(2);
+  else if (ph == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // PAGED: cache rows through the block table, and per-sequence key counts.
 template <int DH, int R, int HT, bool PAGED>
 __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t ctx_len, int64_t chunk,
@@ -398,8 +411,24 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
     return nx;
   };
 
-  // The first blocks' loads go out before the query is formed (two blocks per
-  // wave at d_h = 64, one at d_h = 128).
+  // The query factors ([h][rq] then [rq][DH], or the plain Q [h][DH]) are
+  // staged in LDS.  Their first 1024 elements are loaded before the first
+  // cache blocks' loads (two blocks per wave at d_h = 64, one at d_h = 128), so
+  // they do not queue behind them; the rest after.
+  const bf16_t* AQ = reinterpret_cast<const bf16_t*>(a.a_q);
+  const bf16_t* BQ = reinterpret_cast<const bf16_t*>(a.b_q);
+  const int64_t qtok = b * a.q_bstride_tok;
+  const int rq = a.rq;
+  const int nqa = rq ? h * rq : h * DH, nq = nqa + (rq ? rq * DH : 0);
+  auto q_elem = [&](int i) {
+    return i < nqa ? (rq ? AQ[qtok * h * rq + i] : BQ[qtok * h * DH + i]) : BQ[qtok * rq * DH + (i - nqa)];
+  };
+  bf16_t qv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    qv[j] = i < nq ? q_elem(i) : bf16_t(0);
+  }
   BlockRegs<DH, R, HT> r0;
   BlockRegs<DH, R, HT> r1;
   if (wave < nvb) load(r0, wave);
@@ -413,18 +442,14 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
   // the wave's lo halves in LDS, past the loop's B_V tiles (not the staged factors)
   bf16x8_t* qlo_lds = reinterpret_cast<bf16x8_t*>(smem + C::kLoopBytes) + wave * HT * KS * 64;
   {
-    const bf16_t* AQ = reinterpret_cast<const bf16_t*>(a.a_q);
-    const bf16_t* BQ = reinterpret_cast<const bf16_t*>(a.b_q);
-    const int64_t tok = b * a.q_bstride_tok;
-    const int rq = a.rq;
     bf16_t* qa = reinterpret_cast<bf16_t*>(smem);     // [h][rq], or the plain Q [h][DH]
-    bf16_t* qb = qa + (rq ? h * rq : h * DH);          // [rq][DH]
-    if (rq == 0) {
-      for (int i = threadIdx.x; i < h * DH; i += blockDim.x) qa[i] = BQ[tok * h * DH + i];
-    } else {
-      for (int i = threadIdx.x; i < h * rq; i += blockDim.x) qa[i] = AQ[tok * h * rq + i];
-      for (int i = threadIdx.x; i < rq * DH; i += blockDim.x) qb[i] = BQ[tok * rq * DH + i];
+    bf16_t* qb = qa + nqa;                             // [rq][DH]
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      if (i < nq) qa[i] = qv[j];
     }
+    for (int i = threadIdx.x + 1024; i < nq; i += 256) qa[i] = q_elem(i);
     __syncthreads();
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -481,9 +506,11 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
   // Each register set is reloaded with its next block part by part while the
   // current block is computed (compute_block), so loads stay in flight.
   const NextBlock none = {false, cb, 0, 0};
+  const int wtotal = (nvb - wave + 3) >> 2;   // this wave's blocks (at least 1 where it has any)
   if constexpr (C::kPrefetch) {
     // two register sets in flight: blocks vb and vb+4 of this wave
     for (int vb = wave; vb < nvb; vb += 8) {
+      prio_by_progress((vb - wave) >> 2, wtotal);
       compute_block<DH, R, HT, kRoll>(r0, lbv, vb * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
       if (vb + 8 < nvb) load(r0, vb + 8);
       if (vb + 4 < nvb) {
@@ -494,16 +521,21 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
     }
   } else if constexpr (kRoll == 0) {
     for (int vb = wave; vb < nvb; vb += 4) {
+      // (not with a paged cache at d_h = 128, whose registers it would spill)
+      if constexpr (!(PAGED && DH == 128)) prio_by_progress((vb - wave) >> 2, wtotal);
       if (vb != wave) load(r0, vb);
       compute_block<DH, R, HT, kRoll>(r0, lbv, vb * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
     }
   } else {
     // one register set, reloaded with the wave's next block part by part
-    for (int vb = wave; vb < nvb; vb += 4)
-      compute_block<DH, R, HT, kRoll>(r0, lbv, vb * VBT, last, next_of(vb + 4), h, lane, qop, qlo, qlo_lds, m_run, l_run,
-                               oacc);
+    for (int vb = wave; vb < nvb; vb += 4) {
+      prio_by_progress((vb - wave) >> 2, wtotal);
+      compute_block<DH, R, HT, kRoll>(r0, lbv, vb * VBT, last, next_of(vb + 4), h, lane, qop, qlo, qlo_lds, m_run,
+                                      l_run, oacc);
+    }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- merge the four waves (fixed order) and write this chunk's partial
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
