@@ -24,6 +24,15 @@ __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) 
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// v_mfma_f32_32x32x16_bf16, D = A B + C for lane l (l32 = l % 32, lh = l / 32):
+//   A (32 x 16): 8 values A[l32][8*lh + j];  B (16 x 32): 8 values B[8*lh + j][l32]
+//   D (32 x 32): 16 values D[8*(i/4) + 4*lh + i%4][l32], i < 16
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma32_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 

@@ -45,12 +45,6 @@
 
 namespace tpa {
 
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ f32x16_t mfma32_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
 // max of x over the lanes l and l ^ 32
 __device__ __forceinline__ float half_swap_max(float x) {
   const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
