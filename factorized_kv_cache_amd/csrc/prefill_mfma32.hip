@@ -54,14 +54,17 @@ __device__ __forceinline__ float half_swap_max(float x) {
 template <int R>
 struct Pf32Cfg {
   static constexpr int DH = 64;
+  static constexpr int NW = 4;                 // waves per workgroup
+  static constexpr int NT = 64 * NW;           // threads per workgroup
+  static constexpr int OCC = 2;                // workgroups per CU the registers allow
   static constexpr int QT = 2;                 // 32-query tiles per wave
-  static constexpr int BM = 4 * 32 * QT;       // queries per workgroup
+  static constexpr int BM = NW * 32 * QT;      // queries per workgroup
   static constexpr int BN = R == 4 ? 32 : 64;  // keys per block
   static constexpr int KT = BN / 32;           // 32-key tiles of the score product
   static constexpr int KS = BN / 16;           // 16-key steps of the value product
   static constexpr int LD = DH + 8;            // LDS row stride (bf16) of K and V
   static constexpr int TILE = BN * LD;         // bf16 elements of one K or V buffer
-  static constexpr int IT = BN * (DH / 8) / 256;   // rebuild items per thread
+  static constexpr int IT = BN * (DH / 8) / NT;    // rebuild items per thread
   static constexpr size_t kLds = (size_t)4 * TILE * sizeof(bf16_t);
   static constexpr float kRescaleSlack = 8.f;  // log2 units
 };
@@ -90,7 +93,7 @@ __device__ __forceinline__ void load_rebuild32(Rebuild32<R>& g, const AttnArgs& 
   const bf16_t* BV = reinterpret_cast<const bf16_t*>(a.c_bv);
 #pragma unroll
   for (int it = 0; it < Rebuild32<R>::IT; ++it) {
-    const int item = threadIdx.x + 256 * it;
+    const int item = threadIdx.x + Pf32Cfg<R>::NT * it;
     const int key = item >> 3, d0 = (item & 7) * 8;
     int64_t t = k0 + key;
     t = t < kend ? t : kend - 1;
@@ -110,7 +113,7 @@ __device__ __forceinline__ void store_rebuild32(const Rebuild32<R>& g, bf16_t* k
   constexpr int LD = Pf32Cfg<R>::LD;
 #pragma unroll
   for (int it = 0; it < Rebuild32<R>::IT; ++it) {
-    const int item = threadIdx.x + 256 * it;
+    const int item = threadIdx.x + Pf32Cfg<R>::NT * it;
     const int key = item >> 3, d0 = (item & 7) * 8;
     float kv[8], vv[8];
     factor_combine<R>(g.ak[it], g.bk[it], kv);
@@ -231,7 +234,7 @@ __device__ __forceinline__ void attend_block32(const bf16_t* k_lds, const bf16_t
 }
 
 template <int R>
-__global__ void __launch_bounds__(256, 2) prefill_mfma32_kernel(AttnArgs a, int n_qblocks) {
+__global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma32_kernel(AttnArgs a, int n_qblocks) {
   using C = Pf32Cfg<R>;
   constexpr int DH = 64, QT = C::QT, BM = C::BM, BN = C::BN, TILE = C::TILE;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -266,7 +269,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma32_kernel(AttnArgs a, int 
   Rebuild32<R> rg;
   load_rebuild32<R>(rg, a, seq0, hh, 0, kend);
 
-  // ---- query operand: lane (query q0 + 64*wave + 32*qt + l32, d slice
+  // ---- query operand: lane (query q0 + 32*QT*wave + 32*qt + l32, d slice
   //      16*ks + 8*lh .. +8), pre-scaled
   bf16x8_t qop[QT][4];
   {
@@ -274,7 +277,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma32_kernel(AttnArgs a, int 
     const bf16_t* BQ = reinterpret_cast<const bf16_t*>(a.b_q);
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const int64_t s = q0 + 64 * wave + 32 * qt + l32;
+      const int64_t s = q0 + 32 * QT * wave + 32 * qt + l32;
       const int64_t tok = b * a.q_bstride_tok + (s < a.S ? s : a.S - 1);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -313,7 +316,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma32_kernel(AttnArgs a, int 
       for (int e = 0; e < 16; ++e) oacc[qt][dt][e] = 0.f;
   }
 
-  const int64_t wpos0 = a.start_pos + q0 + 64 * wave;   // position of this wave's first query
+  const int64_t wpos0 = a.start_pos + q0 + 32 * QT * wave;   // position of this wave's first query
   const bool causal = a.causal != 0;
   // Block i is rebuilt into buffer i & 1 while block i - 1 is attended to; its
   // factors were loaded a block earlier.
@@ -323,7 +326,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma32_kernel(AttnArgs a, int 
   for (int blk = 0; blk < nblk; ++blk) {
     const int64_t k0 = (int64_t)blk * BN;
     // a block wholly after every query of this wave contributes nothing
-    if (!causal || k0 <= wpos0 + 63)
+    if (!causal || k0 <= wpos0 + 32 * QT - 1)
       attend_block32<R>(lds + (blk & 1) * TILE, lds + (2 + (blk & 1)) * TILE, k0, kend, wpos0, causal, lane, qop,
                         m_run, lsum, oacc);
     if (blk + 1 < nblk) {
@@ -343,7 +346,7 @@ __global__ void __launch_bounds__(256, 2) prefill_mfma32_kernel(AttnArgs a, int 
                                                      false);
     const float lrow = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     const float inv = a.v_scale / lrow;
-    const int64_t s = q0 + 64 * wave + 32 * qt + l32;
+    const int64_t s = q0 + 32 * QT * wave + 32 * qt + l32;
     if (s < a.S) {
       bf16_t* orow = out + ((b * a.S + s) * h + hh) * (int64_t)DH;
 #pragma unroll
@@ -384,11 +387,11 @@ hipError_t launch_prefill_mfma32(const AttnArgs& a, hipStream_t st) {
   const int nqb = (int)((a.S + bm - 1) / bm);
   const dim3 grid((unsigned)((int64_t)nqb * a.h * a.n_batch));
   if (a.rk == 1)
-    hipLaunchKernelGGL((prefill_mfma32_kernel<1>), grid, dim3(256), (Pf32Cfg<1>::kLds), st, a, nqb);
+    hipLaunchKernelGGL((prefill_mfma32_kernel<1>), grid, dim3(Pf32Cfg<1>::NT), (Pf32Cfg<1>::kLds), st, a, nqb);
   else if (a.rk == 2)
-    hipLaunchKernelGGL((prefill_mfma32_kernel<2>), grid, dim3(256), (Pf32Cfg<2>::kLds), st, a, nqb);
+    hipLaunchKernelGGL((prefill_mfma32_kernel<2>), grid, dim3(Pf32Cfg<2>::NT), (Pf32Cfg<2>::kLds), st, a, nqb);
   else
-    hipLaunchKernelGGL((prefill_mfma32_kernel<4>), grid, dim3(256), (Pf32Cfg<4>::kLds), st, a, nqb);
+    hipLaunchKernelGGL((prefill_mfma32_kernel<4>), grid, dim3(Pf32Cfg<4>::NT), (Pf32Cfg<4>::kLds), st, a, nqb);
   return hipGetLastError();
 }
 
