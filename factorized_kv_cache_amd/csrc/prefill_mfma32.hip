@@ -56,7 +56,7 @@ struct Pf32Cfg {
   static constexpr int DH = 64;
   static constexpr int NW = 4;                 // waves per workgroup
   static constexpr int NT = 64 * NW;           // threads per workgroup
-  static constexpr int OCC = 2;                // workgroups per CU the registers allow
+  static constexpr int OCC = 2;                // waves per SIMD to fit (registers <= 512 / OCC)
   static constexpr int QT = 2;                 // 32-query tiles per wave
   static constexpr int BM = NW * 32 * QT;      // queries per workgroup
   static constexpr int BN = R == 4 ? 32 : 64;  // keys per block
