@@ -245,6 +245,7 @@ __global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(AttnArg
 bool decode_mfma_shape_ok(int dtype, const AttnArgs& a);
 bool decode_mfma_supported(int dtype, const AttnArgs& a);
 int64_t decode_mfma_wave_tokens(const AttnArgs& a);
+int64_t decode_mfma_target_workgroups(const AttnArgs& a);
 hipError_t launch_decode_mfma(const AttnArgs& a, int64_t ctx_len, int64_t chunk, int64_t n_chunks, float* ws,
                               hipStream_t st);
 
@@ -260,19 +261,19 @@ static DecodePlan plan_generic(int64_t ctx_len) {
 
 // Matrix-core plan: chunks are whole multiples of the tokens one workgroup
 // covers per step (a value block per wave).  Each sequence gets
-// floor(kDecodeTargetWorkgroups / B) chunks (at least one) and its units are
+// floor(target / B) chunks (at least one; the target is one round of resident
+// workgroups, decode_mfma_target_workgroups) and its units are
 // spread evenly over them, so no sequence ends in a sliver of a chunk: with
 // contexts of 2^k + 1 keys (the new token included) rounding the chunk length
 // instead left a one-unit chunk per sequence, whose workgroups ran as a nearly
 // empty second round (measured 21.5 -> 19.9 us at 16 x 4097 keys, 169 -> 142
 // us at 32 x 16,385 KV-only, unchanged at 8 x 131,073).
-constexpr int64_t kDecodeTargetWorkgroups = 512;
 static DecodePlan plan_mfma(const AttnArgs& a, int64_t ctx_len) {
   DecodePlan p;
   p.kernel = 1;
   const int64_t vw = decode_mfma_wave_tokens(a);
   const int64_t units = (ctx_len + vw - 1) / vw;
-  int64_t per_seq = kDecodeTargetWorkgroups / a.n_batch;
+  int64_t per_seq = decode_mfma_target_workgroups(a) / a.n_batch;
   if (per_seq < 1) per_seq = 1;
   int64_t cu = (units + per_seq - 1) / per_seq;
   if ((units + cu - 1) / cu > kCombineMaxChunks) cu = (units + kCombineMaxChunks - 1) / kCombineMaxChunks;
@@ -293,7 +294,7 @@ size_t decode_plan_bytes(const DecodePlan& p, const AttnArgs& a) { return partia
 
 // Workspace: partials for either plan the shape allows, so the size does not
 // depend on pointer alignment.  (The matrix-core plan exists only for the
-// shapes that kernel takes: its block of tokens per wave is 4 * (32 / R_K).)
+// shapes that kernel takes: a workgroup step covers waves * (32 / R_K) tokens.)
 size_t decode_workspace_bytes(int dtype, const AttnArgs& a) {
   const int64_t ctx_len = a.start_pos + 1;
   const size_t n = partial_bytes(plan_generic(ctx_len), a);

@@ -96,8 +96,17 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Waves per workgroup.  At d_h = 128 one eight-wave workgroup per CU, so that
+// all the waves of a CU start together: two four-wave workgroups on a CU ran
+// unevenly (the one dispatched second fell behind), and eight waves measured
+// 241 against 245 us at 8 x 131,073 keys.  At d_h = 64 two four-wave
+// workgroups (eight waves measured 146 against 141 us at 32 x 16,385 keys).
+__host__ __device__ constexpr int decode_waves(int dh) { return dh == 128 ? 8 : 4; }
+
 template <int DH, int R, int HT>
 struct DecodeMfmaCfg {
+  static constexpr int NW = decode_waves(DH);
+  static constexpr int THREADS = 64 * NW;
   static constexpr int KS = DH / 32;     // k-steps of the score product
   static constexpr int DT = DH / 16;     // 16-wide d tiles of the value product
   static constexpr int NT = 4 / R;       // tokens per lane per score tile
@@ -109,7 +118,7 @@ struct DecodeMfmaCfg {
   static constexpr int OST = DH + 4;     // LDS row stride (f32) of the merge buffer
   // a second block in flight (its registers spill beyond these sizes)
   static constexpr bool kPrefetch = DH == 64 && (R == 1 ? HT == 1 : HT <= 2);
-  static constexpr size_t kLoopBytes = 4 * 32 * LROW * sizeof(bf16_t);
+  static constexpr size_t kLoopBytes = (size_t)NW * 32 * LROW * sizeof(bf16_t);
   // the query's lo half in LDS instead of registers (lane-major, 16 bytes a
   // lane per (head tile, k-step)) where the registers would spill
   static constexpr bool kQloLds = (DH == 64 && HT == 4) || (DH == 128 && HT == 2);
@@ -121,8 +130,8 @@ struct DecodeMfmaCfg {
   static constexpr int kRoll = kPrefetch ? 0
                                : DH == 128 ? (HT == 2 ? (R == 1 ? 0 : R == 2 ? 1 : 7) : 7)
                                : (R == 1 && HT == 3 ? 1 : 7);
-  static constexpr size_t kQloBytes = kQloLds ? (size_t)4 * HT * KS * 64 * 16 : 0;   // four waves
-  static constexpr size_t kMergeBytes = (8 * HP + 2 * HP * OST) * sizeof(float);
+  static constexpr size_t kQloBytes = kQloLds ? (size_t)NW * HT * KS * 64 * 16 : 0;
+  static constexpr size_t kMergeBytes = (2 * NW * HP + 2 * HP * OST) * sizeof(float);
   static constexpr size_t kLds =
       kLoopBytes + kQloBytes > kMergeBytes ? kLoopBytes + kQloBytes : kMergeBytes;
   static_assert(kLds <= 160 * 1024, "LDS per workgroup (gfx950: 160 KB)");
@@ -351,7 +360,7 @@ __device__ __forceinline__ void prio_by_progress(int done, int total) {
 
 // PAGED: cache rows through the block table, and per-sequence key counts.
 template <int DH, int R, int HT, bool PAGED>
-__global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t ctx_len, int64_t chunk,
+__global__ void __launch_bounds__(64 * decode_waves(DH), 2) decode_mfma_kernel(AttnArgs a, int64_t ctx_len, int64_t chunk,
                                                           int64_t n_chunks, float* ws) {
   using C = DecodeMfmaCfg<DH, R, HT>;
   constexpr int KS = C::KS, DT = C::DT, VBT = C::VBT, HP = C::HP, LROW = C::LROW, OST = C::OST;
@@ -412,7 +421,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
   };
 
   // The query factors ([h][rq] then [rq][DH], or the plain Q [h][DH]) are
-  // staged in LDS.  Their first 1024 elements are loaded before the first
+  // staged in LDS.  Their first 4 * THREADS elements are loaded before the first
   // cache blocks' loads (two blocks per wave at d_h = 64, one at d_h = 128), so
   // they do not queue behind them; the rest after.
   const bf16_t* AQ = reinterpret_cast<const bf16_t*>(a.a_q);
@@ -426,14 +435,14 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
   bf16_t qv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int i = threadIdx.x + 256 * j;
+    const int i = threadIdx.x + C::THREADS * j;
     qv[j] = i < nq ? q_elem(i) : bf16_t(0);
   }
   BlockRegs<DH, R, HT> r0;
   BlockRegs<DH, R, HT> r1;
   if (wave < nvb) load(r0, wave);
   if constexpr (C::kPrefetch) {
-    if (wave + 4 < nvb) load(r1, wave + 4);
+    if (wave + C::NW < nvb) load(r1, wave + C::NW);
   }
 
   // ---- query operand, via the query factors staged in LDS (one round trip).
@@ -446,10 +455,10 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
     bf16_t* qb = qa + nqa;                             // [rq][DH]
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int i = threadIdx.x + 256 * j;
+      const int i = threadIdx.x + C::THREADS * j;
       if (i < nq) qa[i] = qv[j];
     }
-    for (int i = threadIdx.x + 1024; i < nq; i += 256) qa[i] = q_elem(i);
+    for (int i = threadIdx.x + 4 * C::THREADS; i < nq; i += C::THREADS) qa[i] = q_elem(i);
     __syncthreads();
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -506,45 +515,45 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
   // Each register set is reloaded with its next block part by part while the
   // current block is computed (compute_block), so loads stay in flight.
   const NextBlock none = {false, cb, 0, 0};
-  const int wtotal = (nvb - wave + 3) >> 2;   // this wave's blocks (at least 1 where it has any)
+  const int wtotal = (nvb - wave + C::NW - 1) / C::NW;   // this wave's blocks (at least 1 where it has any)
   if constexpr (C::kPrefetch) {
     // two register sets in flight: blocks vb and vb+4 of this wave
-    for (int vb = wave; vb < nvb; vb += 8) {
-      prio_by_progress((vb - wave) >> 2, wtotal);
+    for (int vb = wave; vb < nvb; vb += 2 * C::NW) {
+      prio_by_progress((vb - wave) / C::NW, wtotal);
       compute_block<DH, R, HT, kRoll>(r0, lbv, vb * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
-      if (vb + 8 < nvb) load(r0, vb + 8);
-      if (vb + 4 < nvb) {
-        compute_block<DH, R, HT, kRoll>(r1, lbv, (vb + 4) * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run,
+      if (vb + 2 * C::NW < nvb) load(r0, vb + 2 * C::NW);
+      if (vb + C::NW < nvb) {
+        compute_block<DH, R, HT, kRoll>(r1, lbv, (vb + C::NW) * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run,
                                  oacc);
-        if (vb + 12 < nvb) load(r1, vb + 12);
+        if (vb + 3 * C::NW < nvb) load(r1, vb + 3 * C::NW);
       }
     }
   } else if constexpr (kRoll == 0) {
-    for (int vb = wave; vb < nvb; vb += 4) {
+    for (int vb = wave; vb < nvb; vb += C::NW) {
       // (not with a paged cache at d_h = 128, whose registers it would spill)
-      if constexpr (!(PAGED && DH == 128)) prio_by_progress((vb - wave) >> 2, wtotal);
+      if constexpr (!(PAGED && DH == 128)) prio_by_progress((vb - wave) / C::NW, wtotal);
       if (vb != wave) load(r0, vb);
       compute_block<DH, R, HT, kRoll>(r0, lbv, vb * VBT, last, none, h, lane, qop, qlo, qlo_lds, m_run, l_run, oacc);
     }
   } else {
     // one register set, reloaded with the wave's next block part by part
-    for (int vb = wave; vb < nvb; vb += 4) {
-      prio_by_progress((vb - wave) >> 2, wtotal);
-      compute_block<DH, R, HT, kRoll>(r0, lbv, vb * VBT, last, next_of(vb + 4), h, lane, qop, qlo, qlo_lds, m_run,
+    for (int vb = wave; vb < nvb; vb += C::NW) {
+      prio_by_progress((vb - wave) / C::NW, wtotal);
+      compute_block<DH, R, HT, kRoll>(r0, lbv, vb * VBT, last, next_of(vb + C::NW), h, lane, qop, qlo, qlo_lds, m_run,
                                       l_run, oacc);
     }
   }
 
   __builtin_amdgcn_s_setprio(0);
-  // ---- merge the four waves (fixed order) and write this chunk's partial
+  // ---- merge the waves (fixed order) and write this chunk's partial
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     l_run[ht] = lane_group_sum(l_run[ht]);
   }
   __syncthreads();
-  float* mbuf = reinterpret_cast<float*>(smem);  // [4][HP]
-  float* lbuf = mbuf + 4 * HP;                    // [4][HP]
-  float* obuf = lbuf + 4 * HP;                    // [2][HP][OST]
+  float* mbuf = reinterpret_cast<float*>(smem);  // [NW][HP]
+  float* lbuf = mbuf + C::NW * HP;                // [NW][HP]
+  float* obuf = lbuf + C::NW * HP;                // [2][HP][OST]
   if (lg == 0) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -558,30 +567,27 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
     const int head = ht * 16 + li;
     float M = mbuf[head];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, mbuf[w * HP + head]);
+    for (int w = 1; w < C::NW; ++w) M = fmaxf(M, mbuf[w * HP + head]);
     const float sc = fast_exp2(m_run[ht] - M);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[ht][dt] *= sc;
   }
+  // the waves' accumulators summed in a fixed order: waves 0 and 1 write the
+  // two slots, then each further pair of waves adds to them in turn
   const int slot = wave & 1;
-  if (wave < 2) {
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
+  for (int pair = 0; pair < C::NW / 2; ++pair) {
+    if ((wave >> 1) == pair) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<f32x4_t*>(obuf + (slot * HP + ht * 16 + li) * OST + dt * 16 + lg * 4) = oacc[ht][dt];
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          f32x4_t* p = reinterpret_cast<f32x4_t*>(obuf + (slot * HP + ht * 16 + li) * OST + dt * 16 + lg * 4);
+          *p = pair == 0 ? oacc[ht][dt] : *p + oacc[ht][dt];
+        }
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (wave >= 2) {
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        f32x4_t* p = reinterpret_cast<f32x4_t*>(obuf + (slot * HP + ht * 16 + li) * OST + dt * 16 + lg * 4);
-        *p = *p + oacc[ht][dt];
-      }
-  }
-  __syncthreads();
   const int64_t cstride = (int64_t)h * (DH + 2);
   float* P = ws + (b * n_chunks + c) * cstride;
   for (int idx = threadIdx.x; idx < h * DH; idx += blockDim.x) {
@@ -590,9 +596,9 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(AttnArgs a, int64_t
   }
   for (int head = threadIdx.x; head < h; head += blockDim.x) {
     float M = mbuf[head];
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, mbuf[w * HP + head]);
+    for (int w = 1; w < C::NW; ++w) M = fmaxf(M, mbuf[w * HP + head]);
     float L = 0.f;
-    for (int w = 0; w < 4; ++w) L = fmaf(fast_exp2(mbuf[w * HP + head] - M), lbuf[w * HP + head], L);
+    for (int w = 0; w < C::NW; ++w) L = fmaf(fast_exp2(mbuf[w * HP + head] - M), lbuf[w * HP + head], L);
     P[head * (DH + 2)] = M;
     P[head * (DH + 2) + 1] = L;
   }
@@ -623,7 +629,11 @@ bool decode_mfma_supported(int dtype, const AttnArgs& a) {
 }
 
 // Tokens one workgroup covers per step (one value block per wave).
-int64_t decode_mfma_wave_tokens(const AttnArgs& a) { return 4 * (32 / a.rk); }
+int64_t decode_mfma_wave_tokens(const AttnArgs& a) { return decode_waves(a.d_h) * (32 / a.rk); }
+
+// Workgroups the plan aims for: one round of the CUs' resident waves (eight
+// per CU).
+int64_t decode_mfma_target_workgroups(const AttnArgs& a) { return 2048 / decode_waves(a.d_h); }
 
 template <int DH, int R, int HT>
 static void launch_cfg(const AttnArgs& a, int64_t ctx_len, int64_t chunk, int64_t n_chunks, float* ws,
@@ -632,10 +642,10 @@ static void launch_cfg(const AttnArgs& a, int64_t ctx_len, int64_t chunk, int64_
   static_assert(C::kLds >= kDecodeMfmaQueryLds, "LDS area of the staged query factors");
   const dim3 grid((unsigned)n_chunks, (unsigned)a.n_batch);
   if (a.pm.block_table)
-    hipLaunchKernelGGL((decode_mfma_kernel<DH, R, HT, true>), grid, dim3(256), C::kLds, st, a, ctx_len, chunk,
+    hipLaunchKernelGGL((decode_mfma_kernel<DH, R, HT, true>), grid, dim3(C::THREADS), C::kLds, st, a, ctx_len, chunk,
                        n_chunks, ws);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<DH, R, HT, false>), grid, dim3(256), C::kLds, st, a, ctx_len, chunk,
+    hipLaunchKernelGGL((decode_mfma_kernel<DH, R, HT, false>), grid, dim3(C::THREADS), C::kLds, st, a, ctx_len, chunk,
                        n_chunks, ws);
 }
 
