@@ -131,7 +131,7 @@ struct DecodeMfmaCfg {
                                : DH == 128 ? (HT == 2 ? (R == 1 ? 0 : R == 2 ? 1 : 7) : 7)
                                : (R == 1 && HT == 3 ? 1 : 7);
   static constexpr size_t kQloBytes = kQloLds ? (size_t)NW * HT * KS * 64 * 16 : 0;
-  static constexpr size_t kMergeBytes = (2 * NW * HP + 2 * HP * OST) * sizeof(float);
+  static constexpr size_t kMergeBytes = (2 * NW * HP + (size_t)NW * HP * OST) * sizeof(float);
   static constexpr size_t kLds =
       kLoopBytes + kQloBytes > kMergeBytes ? kLoopBytes + kQloBytes : kMergeBytes;
   static_assert(kLds <= 160 * 1024, "LDS per workgroup (gfx950: 160 KB)");
@@ -553,7 +553,7 @@ __global__ void __launch_bounds__(64 * decode_waves(DH), 2) decode_mfma_kernel(A
   __syncthreads();
   float* mbuf = reinterpret_cast<float*>(smem);  // [NW][HP]
   float* lbuf = mbuf + C::NW * HP;                // [NW][HP]
-  float* obuf = lbuf + C::NW * HP;                // [2][HP][OST]
+  float* obuf = lbuf + C::NW * HP;                // [NW][HP][OST]
   if (lg == 0) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -572,27 +572,22 @@ __global__ void __launch_bounds__(64 * decode_waves(DH), 2) decode_mfma_kernel(A
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[ht][dt] *= sc;
   }
-  // the waves' accumulators summed in a fixed order: waves 0 and 1 write the
-  // two slots, then each further pair of waves adds to them in turn
-  const int slot = wave & 1;
+  // every wave's accumulators to its own slot; the partial is their sum in
+  // wave order
 #pragma unroll
-  for (int pair = 0; pair < C::NW / 2; ++pair) {
-    if ((wave >> 1) == pair) {
+  for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          f32x4_t* p = reinterpret_cast<f32x4_t*>(obuf + (slot * HP + ht * 16 + li) * OST + dt * 16 + lg * 4);
-          *p = pair == 0 ? oacc[ht][dt] : *p + oacc[ht][dt];
-        }
-    }
-    __syncthreads();
-  }
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4_t*>(obuf + (wave * HP + ht * 16 + li) * OST + dt * 16 + lg * 4) = oacc[ht][dt];
+  __syncthreads();
   const int64_t cstride = (int64_t)h * (DH + 2);
   float* P = ws + (b * n_chunks + c) * cstride;
   for (int idx = threadIdx.x; idx < h * DH; idx += blockDim.x) {
     const int head = idx / DH, d = idx - head * DH;
-    P[head * (DH + 2) + 2 + d] = obuf[head * OST + d] + obuf[(HP + head) * OST + d];
+    float o = obuf[head * OST + d];
+#pragma unroll
+    for (int w = 1; w < C::NW; ++w) o += obuf[(w * HP + head) * OST + d];
+    P[head * (DH + 2) + 2 + d] = o;
   }
   for (int head = threadIdx.x; head < h; head += blockDim.x) {
     float M = mbuf[head];
