@@ -24,7 +24,8 @@
 //    C = p_t * A_V[t,head,r].  The score tiles' output registers already sit
 //    in the B-operand layout of this product (k-slot j of lane group g is row
 //    4g+j of tile 0 for j<4, of tile 1 for j>=4); B_V goes through a
-//    wave-private LDS tile to be read transposed.
+//    wave-private LDS tile (16-byte stores of whole-line loads) and comes back
+//    as the A operand with ds_read_b64_tr_b16.
 //
 // At d_h = 64 (up to 32 heads, 16 at rank 1) each wave keeps two blocks' loads
 // in flight, both issued before the query is formed; at d_h = 128 or with more
@@ -34,8 +35,9 @@
 // registers allow, B~_K after the score products and the head factors after
 // the softmax), so the wave keeps loads in flight through its compute: at
 // 8 x 131073 keys, h 32, d_h 128 the call went from 260-263 to 255 us.
-// The four waves of a workgroup merge their (m, l, O) through LDS in a fixed
-// order and write one partial per head to the workspace; the combine pass,
+// The waves of a workgroup (eight at d_h = 128, four at 64) merge their
+// (m, l, O) through LDS in a fixed order and write one partial per head to the
+// workspace; the combine pass,
 // shared with the general kernel, merges the chunks in index order.  (Merging
 // in the last workgroup to finish would need an agent-scope release per
 // workgroup, which writes back the whole L2 of its XCD: far slower than a
