@@ -440,6 +440,30 @@ def decode_shared(fq: Dict[str, np.ndarray], cache_a: Dict[str, np.ndarray], bas
     return out
 
 
+def prefill_shared(fq: Dict[str, np.ndarray], cache_a: Dict[str, np.ndarray], basis: Dict[str, np.ndarray],
+                   dims: Dims, batch: int, seq: int, start_pos: int, causal: bool = True,
+                   rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Attention of seq queries (positions start_pos..start_pos+seq-1) over keys
+    0..start_pos+seq-1 of a shared-basis cache (cache_a and basis as for
+    decode_shared; the block's own head factors already appended).  Keys and
+    values are those of shared_keys_values; the attention is the standard
+    masked softmax of prefill().  Returns out [B, S, h*d_h]; with `rows` given,
+    only those query rows are computed (the others stay NaN)."""
+    h, dh = dims.n_heads, dims.head_dim
+    T = start_pos + seq
+    Q = queries(fq, dims)                                           # [B, S, h, d_h]
+    out = np.full((batch, seq, h * dh), np.nan)
+    sel = np.arange(seq) if rows is None else np.asarray(rows, dtype=np.int64)
+    q_pos = positions(start_pos, seq)[sel]
+    for b in range(batch):
+        k, v = shared_keys_values(cache_a["a_k"][b], cache_a["a_v"][b], basis["b_k"], basis["b_v"],
+                                  dims.rope_base, T)
+        for hh in range(h):
+            out[b, sel, hh * dh:(hh + 1) * dh] = attend_head(Q[b, sel, hh, :], k[:, hh, :], v[:, hh, :], q_pos,
+                                                             causal)
+    return out
+
+
 def layer_forward(x: np.ndarray, w: Dict[str, np.ndarray], dims: Dims, cache: Dict[str, np.ndarray],
                   start_pos: int, causal: bool = True, rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """The whole TPA attention path for one block of tokens, without the output

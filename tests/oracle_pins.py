@@ -20,9 +20,10 @@ What pins what:
   backward_*           the written-out gradients against central finite
                        differences of the forward oracle; the inverse rotation
                        against the adjoint identity
-  shared_*             the shared-basis decode against its own scalar brute force,
-                       against the standard decode over per-token rotated copies
-                       of the basis, and with constant values
+  shared_*             the shared-basis decode and prefill against their scalar
+                       brute force, against the standard decode / prefill over
+                       per-token rotated copies of the basis, and with constant
+                       values
 """
 import math
 
@@ -585,11 +586,65 @@ def shared_constant_values():
         _close(out[b], want, what="constant shared values")
 
 
+SHARED_PREFILL_CASES = [
+    # h, d, rq, rk, rv, base, B, S, start_pos, causal
+    (2, 4, 2, 2, 1, 10000.0, 2, 4, 3, True),
+    (3, 6, 0, 1, 3, 100.0, 1, 5, 0, True),     # KV-only query
+    (1, 8, 1, 3, 2, 10.0, 2, 3, 4, False),     # large angles, every key visible
+]
+
+
+def _shared_prefill_case(ci, seed, std=0.8):
+    h, d, rq, rk, rv, base, B, S, sp, causal = SHARED_PREFILL_CASES[ci]
+    rng = np.random.default_rng(seed)
+    dims = O.Dims(8, h, d, rq, rk, rv, base)
+    fq = {"q": rng.normal(0, std, (B, S, h, d))} if dims.kv_only else \
+        {"a_q": rng.normal(0, std, (B, S, h, rq)), "b_q": rng.normal(0, std, (B, S, rq, d))}
+    n = sp + S + 2
+    cache_a = {"a_k": rng.normal(0, std, (B, n, h, rk)), "a_v": rng.normal(0, std, (B, n, h, rv))}
+    basis = {"b_k": rng.normal(0, std, (rk, d)), "b_v": rng.normal(0, std, (rv, d))}
+    return dims, fq, cache_a, basis, B, S, sp, causal
+
+
+def shared_prefill_brute_force():
+    """Shared-basis prefill, row by row, against the scalar brute force: row s
+    (position start_pos + s) attends over keys 0 .. start_pos + s (causal) or
+    over every key."""
+    for ci in range(len(SHARED_PREFILL_CASES)):
+        dims, fq, cache_a, basis, B, S, sp, causal = _shared_prefill_case(ci, 760 + ci)
+        got = O.prefill_shared(fq, cache_a, basis, dims, B, S, sp, causal)
+        Q = O.queries(fq, dims)
+        for b in range(B):
+            for s_ in range(S):
+                n = sp + s_ + 1 if causal else sp + S
+                want = brute_force.shared_decode(Q[b, s_].tolist(), cache_a["a_k"][b, :n].tolist(),
+                                                 cache_a["a_v"][b, :n].tolist(), basis["b_k"].tolist(),
+                                                 basis["b_v"].tolist(), dims.rope_base)
+                _close(got[b, s_], np.array(want), what=f"shared prefill case {ci} seq {b} row {s_}")
+
+
+def shared_prefill_equals_standard_with_rotated_copies():
+    """The standard prefill over a factor cache holding, for every token t, the
+    shared basis rotated at t gives the same rows as the shared-basis prefill."""
+    for ci in range(len(SHARED_PREFILL_CASES)):
+        dims, fq, cache_a, basis, B, S, sp, causal = _shared_prefill_case(ci, 780 + ci)
+        n = cache_a["a_k"].shape[1]
+        cache = O.cache_new(dims, B, n)
+        cache["a_k"][:] = cache_a["a_k"]
+        cache["a_v"][:] = cache_a["a_v"]
+        bk = np.broadcast_to(basis["b_k"], (B, n) + basis["b_k"].shape)
+        cache["b_k"][:] = O.rope(bk, O.positions(0, n), dims.rope_base)
+        cache["b_v"][:] = basis["b_v"]
+        _close(O.prefill_shared(fq, cache_a, basis, dims, B, S, sp, causal),
+               O.prefill(fq, cache, dims, B, S, sp, causal), what=f"shared prefill vs standard case {ci}")
+
+
 ALL_PINS = [
     brute_force_causal, brute_force_noncausal, textbook_mha, textbook_mqa, textbook_gqa,
     rope_identities, rope_textbook, commute_rope_factor_sum, commute_code_order_attention,
     softmax_rows, closed_form_two_tokens, closed_form_special_cases, incremental_decode,
     incremental_chunked_prefill, paged_ragged_brute_force, paged_permutation_invariance,
     backward_finite_differences, backward_rope_adjoint, shared_brute_force,
-    shared_equals_standard_with_rotated_copies, shared_constant_values,
+    shared_equals_standard_with_rotated_copies, shared_constant_values, shared_prefill_brute_force,
+    shared_prefill_equals_standard_with_rotated_copies,
 ]
