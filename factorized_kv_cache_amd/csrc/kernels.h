@@ -151,6 +151,9 @@ constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
 hipError_t decode_scratch(void** ptr);
 
 hipError_t launch_prefill(int dtype, const AttnArgs& a, hipStream_t st);
+// Prefill over a shared-basis cache: c_bk / c_bv are the bases B_K [R_K, d_h]
+// (unrotated) and B_V [R_V, d_h]; key t is rotated at position t with tab.
+hipError_t launch_prefill_shared(int dtype, const AttnArgs& a, const RopeTable& tab, hipStream_t st);
 
 // ---- shared-basis variant: decode over a cache of head factors ------------------
 // AttnArgs as for the decode, except c_bk / c_bv are the bases shared by every

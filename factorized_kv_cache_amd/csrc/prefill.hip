@@ -21,9 +21,22 @@ __device__ __forceinline__ float rebuild(const T* A, const T* Bm, int64_t tok, i
   return v;
 }
 
-template <typename T, int BM, int BN>
-__global__ void __launch_bounds__(kPrefillThreads) prefill_generic_kernel(AttnArgs a) {
+// SHARED: the shared-basis cache.  a.c_bk / a.c_bv then point at the basis
+// B_K [R_K, d_h] (unrotated) and B_V [R_V, d_h], and key t is rebuilt from its
+// head factors and the basis, then rotated at its own position t.
+template <typename T>
+__device__ __forceinline__ float rebuild_basis(const T* A, const T* Bm, int64_t tok, int hh, int h, int R, int dh,
+                                               int d) {
+  float v = 0.f;
+  for (int r = 0; r < R; ++r) v = fmaf(ldf(A, (tok * h + hh) * R + r), ldf(Bm, (int64_t)r * dh + d), v);
+  return v;
+}
+
+template <typename T, int BM, int BN, bool SHARED>
+__global__ void __launch_bounds__(kPrefillThreads) prefill_generic_kernel(AttnArgs a, RopeTable tab) {
   extern __shared__ float smem[];
+  __shared__ double s_rev[SHARED ? kMaxRopePairs : 1];
+  if constexpr (SHARED) rope_stage(tab, a.d_h >> 1, s_rev);   // visible after the next barrier
   constexpr int kOut = 16;  // BM * d_h / threads, at most (BM=32,d_h=128 or BM=16,d_h=256)
   const int h = a.h, dh = a.d_h;
   float* qs = smem;              // [BM][d_h]
@@ -68,16 +81,40 @@ __global__ void __launch_bounds__(kPrefillThreads) prefill_generic_kernel(AttnAr
   const int64_t kend = a.causal ? a.start_pos + last_q + 1 : n_keys;
 
   for (int64_t k0 = 0; k0 < kend; k0 += BN) {
-    for (int idx = threadIdx.x; idx < BN * dh; idx += blockDim.x) {
-      const int j = idx / dh, d = idx - j * dh;
-      const int64_t t = k0 + j;
-      float kv = 0.f, vv = 0.f;
-      if (t < kend) {
-        kv = rebuild(AK, BK, seq0 + t, hh, h, a.rk, dh, d);
-        vv = rebuild(AV, BV, seq0 + t, hh, h, a.rv, dh, d);
+    if constexpr (SHARED) {
+      // one rotary pair (2i, 2i+1) of one key per item
+      const int np = dh >> 1;
+      for (int idx = threadIdx.x; idx < BN * np; idx += blockDim.x) {
+        const int j = idx / np, i = idx - j * np;
+        const int64_t t = k0 + j;
+        float k0v = 0.f, k1v = 0.f, v0 = 0.f, v1 = 0.f;
+        if (t < kend) {
+          const float x0 = rebuild_basis(AK, BK, seq0 + t, hh, h, a.rk, dh, 2 * i);
+          const float x1 = rebuild_basis(AK, BK, seq0 + t, hh, h, a.rk, dh, 2 * i + 1);
+          float c, sn;
+          rope_cos_sin(s_rev, t, i, c, sn);
+          k0v = x0 * c - x1 * sn;
+          k1v = x0 * sn + x1 * c;
+          v0 = rebuild_basis(AV, BV, seq0 + t, hh, h, a.rv, dh, 2 * i);
+          v1 = rebuild_basis(AV, BV, seq0 + t, hh, h, a.rv, dh, 2 * i + 1);
+        }
+        ks[j * dh + 2 * i] = k0v;
+        ks[j * dh + 2 * i + 1] = k1v;
+        vs[j * dh + 2 * i] = v0;
+        vs[j * dh + 2 * i + 1] = v1;
       }
-      ks[idx] = kv;
-      vs[idx] = vv;
+    } else {
+      for (int idx = threadIdx.x; idx < BN * dh; idx += blockDim.x) {
+        const int j = idx / dh, d = idx - j * dh;
+        const int64_t t = k0 + j;
+        float kv = 0.f, vv = 0.f;
+        if (t < kend) {
+          kv = rebuild(AK, BK, seq0 + t, hh, h, a.rk, dh, d);
+          vv = rebuild(AV, BV, seq0 + t, hh, h, a.rv, dh, d);
+        }
+        ks[idx] = kv;
+        vs[idx] = vv;
+      }
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < BM * BN; idx += blockDim.x) {
@@ -134,18 +171,18 @@ __global__ void __launch_bounds__(kPrefillThreads) prefill_generic_kernel(AttnAr
   }
 }
 
-template <typename T>
-static hipError_t launch_prefill_t(const AttnArgs& a, hipStream_t st) {
+template <typename T, bool SHARED>
+static hipError_t launch_prefill_t(const AttnArgs& a, const RopeTable& tab, hipStream_t st) {
   if (a.d_h <= 128) {
     constexpr int BM = 32, BN = 32;
     const size_t lds = sizeof(float) * ((size_t)(BM + 2 * BN) * a.d_h + BM * BN + 3 * BM);
     dim3 grid((unsigned)((a.S + BM - 1) / BM), (unsigned)a.h, (unsigned)a.n_batch);
-    hipLaunchKernelGGL((prefill_generic_kernel<T, BM, BN>), grid, dim3(kPrefillThreads), lds, st, a);
+    hipLaunchKernelGGL((prefill_generic_kernel<T, BM, BN, SHARED>), grid, dim3(kPrefillThreads), lds, st, a, tab);
   } else {
     constexpr int BM = 16, BN = 16;
     const size_t lds = sizeof(float) * ((size_t)(BM + 2 * BN) * a.d_h + BM * BN + 3 * BM);
     dim3 grid((unsigned)((a.S + BM - 1) / BM), (unsigned)a.h, (unsigned)a.n_batch);
-    hipLaunchKernelGGL((prefill_generic_kernel<T, BM, BN>), grid, dim3(kPrefillThreads), lds, st, a);
+    hipLaunchKernelGGL((prefill_generic_kernel<T, BM, BN, SHARED>), grid, dim3(kPrefillThreads), lds, st, a, tab);
   }
   return hipGetLastError();
 }
@@ -154,13 +191,22 @@ bool prefill_mfma_supported(int dtype, const AttnArgs& a);
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t st);
 bool prefill_mfma32_supported(int dtype, const AttnArgs& a);
 hipError_t launch_prefill_mfma32(const AttnArgs& a, hipStream_t st);
+hipError_t launch_prefill_mfma32_shared(const AttnArgs& a, const RopeTable& tab, hipStream_t st);
 
 // d_h = 64 runs on the 32x32x16 matrix-core kernel, d_h = 128 on the 16x16x32
 // one, every other shape (and fp32) on the general kernel.
 hipError_t launch_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
   if (prefill_mfma32_supported(dtype, a)) return launch_prefill_mfma32(a, st);
   if (prefill_mfma_supported(dtype, a)) return launch_prefill_mfma(a, st);
-  return dtype == kF32 ? launch_prefill_t<float>(a, st) : launch_prefill_t<bf16_t>(a, st);
+  static const RopeTable unused = {};
+  return dtype == kF32 ? launch_prefill_t<float, false>(a, unused, st) : launch_prefill_t<bf16_t, false>(a, unused, st);
+}
+
+// Shared-basis cache: the 32x32x16 matrix-core kernel where it takes the shape
+// (bf16, d_h = 64, R_K = R_V in {1, 2, 4}), the general kernel otherwise.
+hipError_t launch_prefill_shared(int dtype, const AttnArgs& a, const RopeTable& tab, hipStream_t st) {
+  if (prefill_mfma32_supported(dtype, a)) return launch_prefill_mfma32_shared(a, tab, st);
+  return dtype == kF32 ? launch_prefill_t<float, true>(a, tab, st) : launch_prefill_t<bf16_t, true>(a, tab, st);
 }
 
 }  // namespace tpa

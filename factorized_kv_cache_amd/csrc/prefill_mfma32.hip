@@ -83,7 +83,7 @@ struct Rebuild32 {
 
 // Keys past kend are clamped to the last valid key: they are masked out of
 // every score, so only finiteness matters.
-template <int R>
+template <int R, bool SHARED = false>
 __device__ __forceinline__ void load_rebuild32(Rebuild32<R>& g, const AttnArgs& a, int64_t seq0, int hh, int64_t k0,
                                                int64_t kend) {
   typedef typename RankWordP<R>::type W;
@@ -100,16 +100,37 @@ __device__ __forceinline__ void load_rebuild32(Rebuild32<R>& g, const AttnArgs& 
     const int64_t row = seq0 + t;
     g.ak[it] = *reinterpret_cast<const W*>(AK + (row * a.h + hh) * R);
     g.av[it] = *reinterpret_cast<const W*>(AV + (row * a.h + hh) * R);
+    if constexpr (!SHARED) {   // (the shared bases are loaded once, by load_basis32)
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      g.bk[it][r] = *reinterpret_cast<const uint4*>(BK + (row * R + r) * 64 + d0);
-      g.bv[it][r] = *reinterpret_cast<const uint4*>(BV + (row * R + r) * 64 + d0);
+      for (int r = 0; r < R; ++r) {
+        g.bk[it][r] = *reinterpret_cast<const uint4*>(BK + (row * R + r) * 64 + d0);
+        g.bv[it][r] = *reinterpret_cast<const uint4*>(BV + (row * R + r) * 64 + d0);
+      }
     }
   }
 }
 
+// The shared bases' slices of this thread: every rebuild item of a thread has
+// the same 8-wide d slice (items differ by multiples of 8), so one load each.
 template <int R>
-__device__ __forceinline__ void store_rebuild32(const Rebuild32<R>& g, bf16_t* k_lds, bf16_t* v_lds) {
+__device__ __forceinline__ void load_basis32(Rebuild32<R>& g, const AttnArgs& a) {
+  const bf16_t* BK = reinterpret_cast<const bf16_t*>(a.c_bk);
+  const bf16_t* BV = reinterpret_cast<const bf16_t*>(a.c_bv);
+  const int d0 = (threadIdx.x & 7) * 8;
+#pragma unroll
+  for (int it = 0; it < Rebuild32<R>::IT; ++it)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      g.bk[it][r] = *reinterpret_cast<const uint4*>(BK + r * 64 + d0);
+      g.bv[it][r] = *reinterpret_cast<const uint4*>(BV + r * 64 + d0);
+    }
+}
+
+// SHARED: k0 is the block's first key (= its position) and s_rev the rotary
+// frequencies; each key is rotated at its own position after the rank sum.
+template <int R, bool SHARED = false>
+__device__ __forceinline__ void store_rebuild32(const Rebuild32<R>& g, bf16_t* k_lds, bf16_t* v_lds, int64_t k0 = 0,
+                                                const double* s_rev = nullptr) {
   constexpr int LD = Pf32Cfg<R>::LD;
 #pragma unroll
   for (int it = 0; it < Rebuild32<R>::IT; ++it) {
@@ -118,6 +139,16 @@ __device__ __forceinline__ void store_rebuild32(const Rebuild32<R>& g, bf16_t* k
     float kv[8], vv[8];
     factor_combine<R>(g.ak[it], g.bk[it], kv);
     factor_combine<R>(g.av[it], g.bv[it], vv);
+    if constexpr (SHARED) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float c, sn;
+        rope_cos_sin(s_rev, k0 + key, (d0 >> 1) + q, c, sn);
+        const float x0 = kv[2 * q], x1 = kv[2 * q + 1];
+        kv[2 * q] = x0 * c - x1 * sn;
+        kv[2 * q + 1] = x0 * sn + x1 * c;
+      }
+    }
     *reinterpret_cast<bf16x8_t*>(k_lds + key * LD + d0) = pack8(kv);
     *reinterpret_cast<bf16x8_t*>(v_lds + key * LD + d0) = pack8(vv);
   }
@@ -233,8 +264,11 @@ __device__ __forceinline__ void attend_block32(const bf16_t* k_lds, const bf16_t
   }
 }
 
-template <int R>
-__global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma32_kernel(AttnArgs a, int n_qblocks) {
+// SHARED: the shared-basis cache (c_bk / c_bv are the bases; keys rotated at
+// their positions with tab).
+template <int R, bool SHARED>
+__global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma32_kernel(AttnArgs a, int n_qblocks,
+                                                                                       RopeTable tab) {
   using C = Pf32Cfg<R>;
   constexpr int DH = 64, QT = C::QT, BM = C::BM, BN = C::BN, TILE = C::TILE;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -267,7 +301,12 @@ __global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma3
 
   // The first key block's factors go out before anything else.
   Rebuild32<R> rg;
-  load_rebuild32<R>(rg, a, seq0, hh, 0, kend);
+  __shared__ double s_rev[SHARED ? 32 : 1];   // d_h = 64: 32 rotary pairs
+  if constexpr (SHARED) {
+    rope_stage(tab, 32, s_rev);
+    load_basis32<R>(rg, a);
+  }
+  load_rebuild32<R, SHARED>(rg, a, seq0, hh, 0, kend);
 
   // ---- query operand: lane (query q0 + 32*QT*wave + 32*qt + l32, d slice
   //      16*ks + 8*lh .. +8), pre-scaled
@@ -320,8 +359,9 @@ __global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma3
   const bool causal = a.causal != 0;
   // Block i is rebuilt into buffer i & 1 while block i - 1 is attended to; its
   // factors were loaded a block earlier.
-  store_rebuild32<R>(rg, lds, lds + 2 * TILE);
-  if (nblk > 1) load_rebuild32<R>(rg, a, seq0, hh, BN, kend);
+  if constexpr (SHARED) __syncthreads();   // the staged frequencies are visible
+  store_rebuild32<R, SHARED>(rg, lds, lds + 2 * TILE, 0, s_rev);
+  if (nblk > 1) load_rebuild32<R, SHARED>(rg, a, seq0, hh, BN, kend);
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
     const int64_t k0 = (int64_t)blk * BN;
@@ -330,8 +370,8 @@ __global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma3
       attend_block32<R>(lds + (blk & 1) * TILE, lds + (2 + (blk & 1)) * TILE, k0, kend, wpos0, causal, lane, qop,
                         m_run, lsum, oacc);
     if (blk + 1 < nblk) {
-      store_rebuild32<R>(rg, lds + ((blk + 1) & 1) * TILE, lds + (2 + ((blk + 1) & 1)) * TILE);
-      if (blk + 2 < nblk) load_rebuild32<R>(rg, a, seq0, hh, k0 + 2 * BN, kend);
+      store_rebuild32<R, SHARED>(rg, lds + ((blk + 1) & 1) * TILE, lds + (2 + ((blk + 1) & 1)) * TILE, k0 + BN, s_rev);
+      if (blk + 2 < nblk) load_rebuild32<R, SHARED>(rg, a, seq0, hh, k0 + 2 * BN, kend);
     }
     __syncthreads();
   }
@@ -382,17 +422,30 @@ bool prefill_mfma32_supported(int dtype, const AttnArgs& a) {
   return true;
 }
 
-hipError_t launch_prefill_mfma32(const AttnArgs& a, hipStream_t st) {
+template <bool SHARED>
+static hipError_t launch_pf32(const AttnArgs& a, const RopeTable& tab, hipStream_t st) {
   constexpr int bm = Pf32Cfg<2>::BM;
   const int nqb = (int)((a.S + bm - 1) / bm);
   const dim3 grid((unsigned)((int64_t)nqb * a.h * a.n_batch));
   if (a.rk == 1)
-    hipLaunchKernelGGL((prefill_mfma32_kernel<1>), grid, dim3(Pf32Cfg<1>::NT), (Pf32Cfg<1>::kLds), st, a, nqb);
+    hipLaunchKernelGGL((prefill_mfma32_kernel<1, SHARED>), grid, dim3(Pf32Cfg<1>::NT), (Pf32Cfg<1>::kLds), st, a, nqb,
+                       tab);
   else if (a.rk == 2)
-    hipLaunchKernelGGL((prefill_mfma32_kernel<2>), grid, dim3(Pf32Cfg<2>::NT), (Pf32Cfg<2>::kLds), st, a, nqb);
+    hipLaunchKernelGGL((prefill_mfma32_kernel<2, SHARED>), grid, dim3(Pf32Cfg<2>::NT), (Pf32Cfg<2>::kLds), st, a, nqb,
+                       tab);
   else
-    hipLaunchKernelGGL((prefill_mfma32_kernel<4>), grid, dim3(Pf32Cfg<4>::NT), (Pf32Cfg<4>::kLds), st, a, nqb);
+    hipLaunchKernelGGL((prefill_mfma32_kernel<4, SHARED>), grid, dim3(Pf32Cfg<4>::NT), (Pf32Cfg<4>::kLds), st, a, nqb,
+                       tab);
   return hipGetLastError();
+}
+
+hipError_t launch_prefill_mfma32(const AttnArgs& a, hipStream_t st) {
+  static const RopeTable unused = {};
+  return launch_pf32<false>(a, unused, st);
+}
+
+hipError_t launch_prefill_mfma32_shared(const AttnArgs& a, const RopeTable& tab, hipStream_t st) {
+  return launch_pf32<true>(a, tab, st);
 }
 
 }  // namespace tpa

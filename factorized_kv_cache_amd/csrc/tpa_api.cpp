@@ -199,14 +199,18 @@ int64_t tpa_cache_elems_per_token(const tpa_dims* d) {
   return ((int64_t)d->n_heads + d->head_dim) * ((int64_t)d->rank_k + d->rank_v);
 }
 
-tpa_status tpa_factor_proj(const tpa_dims* d, const void* x, int64_t n_batch, int64_t seq_len, int64_t start_pos,
-                           const void* w_packed, int32_t fuse_rope, const tpa_factors* out, void* stream) {
+// The projection shared by both cache forms.  shared != 0: the packed weight
+// has no dim-factor rows for K and V (their bases are parameters), so the
+// outputs are the query factors and the key/value head factors only.
+static tpa_status factor_proj(const tpa_dims* d, const void* x, int64_t n_batch, int64_t seq_len, int64_t start_pos,
+                              const void* w_packed, int32_t fuse_rope, const tpa_factors* out, void* stream,
+                              bool shared, const char* what) {
   tpa_status st = check_dims(d);
   if (st != TPA_OK) return st;
   if (!x || !w_packed) return fail(TPA_ERR_INVALID_ARGUMENT, "x or w_packed is NULL");
   if (!out) return fail(TPA_ERR_INVALID_ARGUMENT, "out factors are NULL");
   if ((st = check_query(d, out)) != TPA_OK) return st;
-  if (!out->a_k || !out->b_k || !out->a_v || !out->b_v)
+  if (!out->a_k || !out->a_v || (!shared && (!out->b_k || !out->b_v)))
     return fail(TPA_ERR_INVALID_ARGUMENT, "a key/value output tensor is NULL");
   if (n_batch < 1 || seq_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and seq_len must be >= 1");
   if (!token_count_ok(n_batch, seq_len)) return fail(TPA_ERR_UNSUPPORTED, "n_batch * seq_len must be < 2^31");
@@ -223,7 +227,7 @@ tpa_status tpa_factor_proj(const tpa_dims* d, const void* x, int64_t n_batch, in
   a.w = w_packed;
   a.M = n_batch * seq_len;
   a.K = d->d_model;
-  a.N = tpa_packed_weight_rows(d);
+  a.N = shared ? tpa_shared_packed_weight_rows(d) : tpa_packed_weight_rows(d);
   a.S = seq_len;
   a.start_pos = start_pos;
   a.head_dim = dh;
@@ -238,8 +242,10 @@ tpa_status tpa_factor_proj(const tpa_dims* d, const void* x, int64_t n_batch, in
   } else {
     segs[n++] = {h * dh, out->b_q, qs};
   }
-  segs[n++] = {d->rank_k * dh, out->b_k, kvs};
-  segs[n++] = {d->rank_v * dh, out->b_v, kvs};
+  if (!shared) {
+    segs[n++] = {d->rank_k * dh, out->b_k, kvs};
+    segs[n++] = {d->rank_v * dh, out->b_v, kvs};
+  }
   if (d->rank_q > 0) segs[n++] = {h * d->rank_q, out->a_q, qs};
   segs[n++] = {h * d->rank_k, out->a_k, kvs};
   segs[n++] = {h * d->rank_v, out->a_v, kvs};
@@ -253,12 +259,33 @@ tpa_status tpa_factor_proj(const tpa_dims* d, const void* x, int64_t n_batch, in
     col += segs[e].width;
   }
   a.seg_begin[n] = col;
-  a.rot_cols = fuse_rope ? (segs[0].width + segs[1].width) : 0;
+  // the rotated columns: the query dim factors, and the key dim factors unless
+  // they are the shared basis
+  a.rot_cols = fuse_rope ? (shared ? segs[0].width : segs[0].width + segs[1].width) : 0;
   a.vec8 = dh % 8 == 0;
   for (int e = 0; e < n; ++e)
     if (a.seg_begin[e] % 8 || a.width[e] % 8 || a.bstride[e] % 8 || ((uintptr_t)a.dst[e] & 15)) a.vec8 = 0;
   a.rope = rope_table(d);
-  return hip_status(tpa::launch_factor_proj(d->dtype, a, (hipStream_t)stream), "tpa_factor_proj");
+  return hip_status(tpa::launch_factor_proj(d->dtype, a, (hipStream_t)stream), what);
+}
+
+tpa_status tpa_factor_proj(const tpa_dims* d, const void* x, int64_t n_batch, int64_t seq_len, int64_t start_pos,
+                           const void* w_packed, int32_t fuse_rope, const tpa_factors* out, void* stream) {
+  return factor_proj(d, x, n_batch, seq_len, start_pos, w_packed, fuse_rope, out, stream, false, "tpa_factor_proj");
+}
+
+int64_t tpa_shared_packed_weight_rows(const tpa_dims* d) {
+  if (check_dims(d) != TPA_OK) return -1;
+  const int64_t h = d->n_heads, dh = d->head_dim;
+  const int64_t q = d->rank_q > 0 ? h * d->rank_q + d->rank_q * dh : h * dh;
+  return q + h * ((int64_t)d->rank_k + d->rank_v);
+}
+
+tpa_status tpa_shared_factor_proj(const tpa_dims* d, const void* x, int64_t n_batch, int64_t seq_len,
+                                  int64_t start_pos, const void* w_packed, int32_t fuse_rope, const tpa_factors* out,
+                                  void* stream) {
+  return factor_proj(d, x, n_batch, seq_len, start_pos, w_packed, fuse_rope, out, stream, true,
+                     "tpa_shared_factor_proj");
 }
 
 tpa_status tpa_rope_b(const tpa_dims* d, void* b, int64_t n_batch, int64_t seq_len, int32_t rows, int64_t start_pos,
@@ -640,6 +667,31 @@ tpa_status tpa_shared_decode_attn(const tpa_dims* d, const tpa_factors* q, const
   return hip_status(tpa::launch_shared_decode(d->dtype, a, rope_table(d), ctx_len, p, workspace,
                                               (hipStream_t)stream),
                     "tpa_shared_decode_attn");
+}
+
+tpa_status tpa_shared_prefill_attn(const tpa_dims* d, const tpa_factors* q, const tpa_shared_cache* c,
+                                   int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
+                                   void* stream) {
+  tpa_status st = check_dims(d);
+  if (st != TPA_OK) return st;
+  if ((st = check_query(d, q)) != TPA_OK) return st;
+  if ((st = check_shared(c)) != TPA_OK) return st;
+  if (!out) return fail(TPA_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (n_batch < 1 || seq_len < 1) return fail(TPA_ERR_INVALID_ARGUMENT, "n_batch and seq_len must be >= 1");
+  if (n_batch > 65535) return fail(TPA_ERR_UNSUPPORTED, "n_batch must be <= 65535");
+  if (start_pos < 0) return fail(TPA_ERR_INVALID_ARGUMENT, "start_pos must be >= 0");
+  if (n_batch > c->max_batch)
+    return fail(TPA_ERR_CAPACITY, "n_batch %lld exceeds max_batch %lld", (long long)n_batch,
+                (long long)c->max_batch);
+  if (seq_len > c->max_seq || start_pos > c->max_seq - seq_len)
+    return fail(TPA_ERR_CAPACITY, "start_pos %lld + seq_len %lld exceeds max_seq %lld", (long long)start_pos,
+                (long long)seq_len, (long long)c->max_seq);
+  int64_t qs;
+  if ((st = resolve_stride(q->q_batch_stride, seq_len, "q_batch_stride", &qs)) != TPA_OK) return st;
+  const tpa_cache cc = shared_as_cache(c);
+  const tpa::AttnArgs a = attn_args(d, q, qs, &cc, n_batch, seq_len, start_pos, causal, out);
+  return hip_status(tpa::launch_prefill_shared(d->dtype, a, rope_table(d), (hipStream_t)stream),
+                    "tpa_shared_prefill_attn");
 }
 
 // Takes an int: a C caller may pass any int, and a value outside the enum's

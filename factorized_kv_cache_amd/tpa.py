@@ -85,6 +85,10 @@ def _load():
                                                  vp, vp, ctypes.c_size_t, vp]),
         "tpa_shared_cache_append": (ctypes.c_int, [P(tpa_dims), P(tpa_shared_cache), P(tpa_factors), i64, i64, i64,
                                                    vp]),
+        "tpa_shared_packed_weight_rows": (i64, [P(tpa_dims)]),
+        "tpa_shared_factor_proj": (ctypes.c_int, [P(tpa_dims), vp, i64, i64, i64, vp, i32, P(tpa_factors), vp]),
+        "tpa_shared_prefill_attn": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_shared_cache), i64, i64, i64,
+                                                   i32, vp, vp]),
         "tpa_shared_decode_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64]),
         "tpa_shared_decode_attn": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_shared_cache), i64, i64, vp, vp,
                                                   ctypes.c_size_t, vp]),
@@ -104,7 +108,8 @@ EXPORTED = ("tpa_packed_weight_rows", "tpa_cache_elems_per_token", "tpa_factor_p
             "tpa_decode_noalloc_max_bytes", "tpa_decode_attn_noalloc",
             "tpa_prefill_backward_workspace_bytes", "tpa_prefill_attn_backward", "tpa_rope_b_backward",
             "tpa_paged_cache_append", "tpa_paged_decode_workspace_bytes", "tpa_paged_decode_attn",
-            "tpa_shared_cache_append", "tpa_shared_decode_workspace_bytes", "tpa_shared_decode_attn",
+            "tpa_shared_cache_append", "tpa_shared_packed_weight_rows", "tpa_shared_factor_proj",
+            "tpa_shared_prefill_attn", "tpa_shared_decode_workspace_bytes", "tpa_shared_decode_attn",
             "tpa_status_string", "tpa_last_error")
 
 
@@ -416,6 +421,36 @@ def tpa_shared_cache_append(dims: Dims, cache: SharedCache, kv: Factors, start_p
     B, S = kv.a_k.shape[0], kv.a_k.shape[1]
     _check(_lib.tpa_shared_cache_append(ctypes.byref(dims.c()), ctypes.byref(cache.c()), ctypes.byref(kv.c()), B, S,
                                         start_pos, _stream(stream)))
+
+
+def pack_shared_weights(w: dict, kv_only: bool) -> torch.Tensor:
+    """Stack the per-factor weights of a shared-basis layer in the library's row
+    order: W_B_q, W_A_q, W_A_k, W_A_v (KV-only: W_Q, W_A_k, W_A_v)."""
+    order = (["w_q"] if kv_only else ["w_b_q", "w_a_q"]) + ["w_a_k", "w_a_v"]
+    return torch.cat([w[k] for k in order], dim=0).contiguous()
+
+
+def tpa_shared_packed_weight_rows(dims: Dims) -> int:
+    return int(_lib.tpa_shared_packed_weight_rows(ctypes.byref(dims.c())))
+
+
+def tpa_shared_factor_proj(dims: Dims, x: torch.Tensor, w_packed: torch.Tensor, out: Factors, start_pos: int = 0,
+                           fuse_rope: bool = True, stream=None) -> Factors:
+    """Query factors and key/value head factors (out.b_k, out.b_v are ignored)."""
+    B, S = x.shape[0], x.shape[1]
+    _check(_lib.tpa_shared_factor_proj(ctypes.byref(dims.c()), _ptr(x), B, S, start_pos, _ptr(w_packed),
+                                       1 if fuse_rope else 0, ctypes.byref(out.c()), _stream(stream)))
+    return out
+
+
+def tpa_shared_prefill_attn(dims: Dims, q: Factors, cache: SharedCache, start_pos: int, causal: bool = True,
+                            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    B, S = q.b_q.shape[0], q.b_q.shape[1]
+    if out is None:
+        out = torch.empty(B, S, dims.n_heads * dims.head_dim, dtype=dims.torch_dtype, device=q.b_q.device)
+    _check(_lib.tpa_shared_prefill_attn(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B, S,
+                                        start_pos, 1 if causal else 0, _ptr(out), _stream(stream)))
+    return out
 
 
 def tpa_shared_decode_workspace_bytes(dims: Dims, batch: int, ctx_len: int) -> int:

@@ -362,6 +362,39 @@ typedef struct {
 tpa_status tpa_shared_cache_append(const tpa_dims* dims, const tpa_shared_cache* cache, const tpa_factors* kv,
                                    int64_t n_batch, int64_t seq_len, int64_t start_pos, void* stream);
 
+/* Number of rows of the packed projection weight for a shared-basis layer:
+ * h*R_Q + R_Q*d_h + h*R_K + h*R_V (KV-only: h*d_h instead of the query
+ * terms); the key/value dim factors are the shared bases, not projections.
+ * Returns -1 for invalid dims. */
+int64_t tpa_shared_packed_weight_rows(const tpa_dims* dims);
+
+/* Factor projection of a shared-basis layer: as tpa_factor_proj, with
+ * w_packed [n_out, d_model] stacking W_B_q, W_A_q, W_A_k, W_A_v (KV-only: W_Q,
+ * W_A_k, W_A_v) and out->b_k / out->b_v ignored; only the query dim factors
+ * (KV-only: Q) are rotated.  out->a_k / a_v with kv_batch_stride = max_seq
+ * can point at cache slot start_pos of a tpa_shared_cache.
+ *   Passage: the A and B projections of the code walk-through (前向传播), with
+ *   the dim factors of K and V shared (优点与创新 item 5; the reading above).
+ * Errors: as tpa_factor_proj. */
+tpa_status tpa_shared_factor_proj(const tpa_dims* dims, const void* x, int64_t n_batch, int64_t seq_len,
+                                  int64_t start_pos, const void* w_packed, int32_t fuse_rope,
+                                  const tpa_factors* out, void* stream);
+
+/* Prefill attention over a shared-basis cache: S query tokens per sequence at
+ * positions start_pos .. start_pos+S-1 (q as for tpa_prefill_attn) over the
+ * keys 0 .. start_pos+S-1 (the caller appends this block's head factors
+ * first), causal or full as tpa_prefill_attn; out [B, S, h*d_h].  Key t is
+ * rebuilt from its head factors and the basis and rotated at position t;
+ * keys and values are never written to memory.  bf16 with d_h = 64 and
+ * R_K = R_V in {1, 2, 4} runs on the matrix cores (the basis slice each
+ * thread rebuilds is loaded once), every other shape on the general kernel.
+ *   Passage: the Q_t/K_t/V_t equations (核心机制总结) with the dim factors of
+ *   K and V shared, and the masked attention of the code walk-through.
+ * Errors: as tpa_prefill_attn. */
+tpa_status tpa_shared_prefill_attn(const tpa_dims* dims, const tpa_factors* q, const tpa_shared_cache* cache,
+                                   int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
+                                   void* stream);
+
 /* Device workspace for tpa_shared_decode_attn: float32 partials
  * (max, sum, R_V weights) per sequence, key chunk and head; 0 for dims or
  * sizes as tpa_decode_workspace_bytes. */

@@ -209,6 +209,34 @@ def test_shared_validation():
     assert app(1, 1, 0, k=T.tpa_factors(None, None, None, None, FAKE, None, 0, 0)) == INVALID
 
 
+@pytest.mark.parametrize("kw,n_out", [
+    (dict(), 16 * 6 + 6 * 64 + 16 * (2 + 2)),                       # W_B_q, W_A_q, W_A_k, W_A_v
+    (dict(d_model=1536, n_heads=24, head_dim=64, rank_q=0, rank_k=4, rank_v=4), 24 * 64 + 24 * 8),
+])
+def test_shared_projection_and_prefill_validation(kw, n_out):
+    lib = T.library()
+    d = dims(**kw)
+    assert lib.tpa_shared_packed_weight_rows(ctypes.byref(d)) == n_out
+    assert lib.tpa_shared_packed_weight_rows(ctypes.byref(dims(head_dim=63))) == -1
+    # the projection needs the query factors and the key/value head factors only
+    f = T.tpa_factors(FAKE, FAKE, FAKE, None, FAKE, None, 0, 0)
+    proj = lambda B, S, sp, x=FAKE, ff=f: lib.tpa_shared_factor_proj(ctypes.byref(d), x, B, S, sp, FAKE, 1,
+                                                                       ctypes.byref(ff), None)
+    assert proj(1, 0, 0) == INVALID
+    assert proj(1, 1, -1) == INVALID
+    assert proj(1, 1, 0, x=None) == INVALID
+    assert proj(1, 1, 0, ff=T.tpa_factors(FAKE, FAKE, None, None, FAKE, None, 0, 0)) == INVALID   # no a_k
+    sc = T.tpa_shared_cache(FAKE, FAKE, FAKE, FAKE, 4, 4096)
+    q = T.tpa_factors(FAKE, FAKE, None, None, None, None, 0, 0)
+    pre = lambda B, S, sp, c=sc: lib.tpa_shared_prefill_attn(ctypes.byref(d), ctypes.byref(q), ctypes.byref(c), B, S,
+                                                             sp, 1, FAKE, None)
+    assert pre(5, 1, 0) == CAPACITY
+    assert pre(1, 4096, 1) == CAPACITY
+    assert pre(1, 0, 0) == INVALID
+    assert pre(1, 1, -1) == INVALID
+    assert pre(1, 1, 0, c=T.tpa_shared_cache(FAKE, FAKE, FAKE, None, 4, 4096)) == INVALID   # no value basis
+
+
 def test_status_strings():
     lib = T.library()
     for s in range(6):
