@@ -452,6 +452,45 @@ def run_prefill(reps: int = 50):
     }
 
 
+def run_shared_prefill(reps: int = 50):
+    """The prefill workload's shapes (4 x 4096 tokens, d_model 1024, h 16, d_h 64,
+    R_Q 6, R 2) with a shared basis: the head-factor-only projection, the
+    head-factor append and the attention over the shared-basis cache."""
+    wl = I.WORKLOADS["prefill_b4_s4k"]
+    d = dims_of(wl)
+    s = wl.shape
+    B, S = wl.batch, wl.seq
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1013)
+    x = torch.randn(B, S, d.d_model, generator=g, device="cuda").to(torch.bfloat16)
+    w = I.weights(s, seed=1013, dtype="bf16")
+    wp = T.pack_shared_weights({k: v.cuda() for k, v in w.items()}, d.kv_only)
+    std = I.factor_std(s)
+    rnd = lambda *shape: (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+    cache = T.new_shared_cache(d, B, S, rnd(s.rank_k, s.head_dim), rnd(s.rank_v, s.head_dim))
+    f = T.new_factors(d, B, S)
+    f = T.Factors(f.a_q, f.b_q, f.a_k, None, f.a_v, None)
+    out = torch.empty(B, S, d.n_heads * d.head_dim, dtype=torch.bfloat16, device="cuda")
+    T.tpa_shared_factor_proj(d, x, wp, f, start_pos=0)
+    st = {
+        "proj": stats_ms(time_calls(lambda: T.tpa_shared_factor_proj(d, x, wp, f, start_pos=0), reps)),
+        "append": stats_ms(time_calls(lambda: T.tpa_shared_cache_append(d, cache, f, 0), reps)),
+        "attn": stats_ms(time_calls(lambda: T.tpa_shared_prefill_attn(d, f, cache, 0, True, out=out), reps)),
+    }
+    attn_flop = 4.0 * B * d.n_heads * d.head_dim * S * (S + 1) / 2
+    proj_flop = 2.0 * B * S * d.d_model * T.tpa_shared_packed_weight_rows(d)
+    a, p = st["attn"]["mean"], st["proj"]["mean"]
+    return {
+        "workload": wl.name + " (shared basis)", "batch": B, "seq": S,
+        "attn_us": us(st["attn"]), "attn_tflops": round(attn_flop / a / 1e9, 1),
+        "attn_frac_bf16_peak": round(attn_flop / a / 1e9 / BF16_PEAK_TFLOPS, 4),
+        "proj_us": us(st["proj"]), "proj_tflops": round(proj_flop / p / 1e9, 1),
+        "proj_frac_bf16_peak": round(proj_flop / p / 1e9 / BF16_PEAK_TFLOPS, 4),
+        "append_us": us(st["append"]),
+        "step_ms": round((a + p + st["append"]["mean"]), 4),
+    }
+
+
 def run_prefill_backward(reps: int = 5):
     """Backward of the prefill attention at prefill_b4_s4k: gradients of all six
     factor tensors from a seeded dO.  Algorithmic work: the usual 2.5x the
@@ -613,7 +652,7 @@ def calibrate_copy(tokens: int = 26214, batch: int = 16):
                       "launches": 5}), flush=True)
 
 
-PARTS = ("headline", "kvonly", "b16", "prefill", "backward", "shared_long")
+PARTS = ("headline", "kvonly", "b16", "prefill", "backward", "shared_long", "shared_prefill")
 
 
 def main():
@@ -642,7 +681,8 @@ def main():
     if args.only and args.only != "headline":
         fn = {"kvonly": lambda: dict(zip(("prefill", "decode"), run_kvonly())),
               "b16": lambda: run_decode_b16()[0], "prefill": run_prefill,
-              "backward": run_prefill_backward, "shared_long": run_shared_long}[args.only]
+              "backward": run_prefill_backward, "shared_long": run_shared_long,
+              "shared_prefill": run_shared_prefill}[args.only]
         print(json.dumps({args.only: fn()}), flush=True)
         return
 
@@ -686,6 +726,8 @@ def main():
     result["shared_decode_long"] = run_shared_long()
     log("[bench] prefill workload")
     result["prefill"] = run_prefill()
+    log("[bench] shared-basis prefill")
+    result["shared_prefill"] = run_shared_prefill()
     log("[bench] prefill backward")
     result["prefill_backward"] = run_prefill_backward()
     if not args.no_cpu_baseline:
