@@ -165,7 +165,15 @@ __device__ __forceinline__ void attend_block32(const bf16_t* k_lds, const bf16_t
   constexpr int QT = C::QT, KT = C::KT, KS = C::KS, LD = C::LD, BN = C::BN;
   const int l32 = lane & 31, lh = lane >> 5;
 
-  // ---- scores S^T[key, query] for the block's 32-key tiles
+  // ---- scores S^T[key, query] for the block's 32-key tiles.  With two key
+  //      tiles (BN 64) each product starts from minus the query's running
+  //      maximum (0 while it has none): one start block per query tile serves
+  //      both key tiles, so the exponentials below need no subtraction.  With
+  //      one key tile the start block would cost as many moves as it saves.
+  constexpr bool kFromMinusM = KT > 1;
+  float m_use[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) m_use[qt] = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
   f32x16_t sacc[KT][QT];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
@@ -177,7 +185,7 @@ __device__ __forceinline__ void attend_block32(const bf16_t* k_lds, const bf16_t
     for (int qt = 0; qt < QT; ++qt) {
       f32x16_t acc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+      for (int e = 0; e < 16; ++e) acc[e] = kFromMinusM ? -m_use[qt] : 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) acc = mfma32_bf16(kf[ks], qop[qt][ks], acc);
       sacc[kt][qt] = acc;
@@ -217,23 +225,39 @@ __device__ __forceinline__ void attend_block32(const bf16_t* k_lds, const bf16_t
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) bmax = max_nn(bmax, sacc[kt][qt][e]);
-    bmax = half_swap_max(bmax);
-    const bool grow = bmax > m_run[qt] + C::kRescaleSlack;
+    bmax = half_swap_max(bmax);   // kFromMinusM: relative to m_use
+    // The first visible key sets the maximum; later it moves only past the slack.
+    bool grow;
+    if constexpr (kFromMinusM)
+      grow = bmax > (m_run[qt] == -INFINITY ? -INFINITY : C::kRescaleSlack);
+    else
+      grow = bmax > m_run[qt] + C::kRescaleSlack;
     if (__any(grow)) {
-      const float m_new = grow ? bmax : m_run[qt];
-      const float alpha = fast_exp2(m_run[qt] - m_new);   // 0 on the first block, 1 where m stays
+      const float m_new = grow ? (kFromMinusM ? m_use[qt] + bmax : bmax) : m_run[qt];
+      const float alpha = grow ? fast_exp2(m_run[qt] - m_new) : 1.f;   // 0 on the first block
       m_run[qt] = m_new;
       lsum[qt] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) oacc[qt][dt] *= alpha;
+      if constexpr (kFromMinusM) {
+        const float shift = grow ? bmax : 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sacc[kt][qt][e] -= shift;
+      }
     }
-    // a query with no visible key yet keeps m = -inf; its probabilities are 0
-    const float m_use = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
+    // A query with no visible key yet keeps m = -inf: its scores are -inf and
+    // its probabilities 0.
+    const float m_sub = kFromMinusM ? 0.f : (m_run[qt] == -INFINITY ? 0.f : m_run[qt]);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       float pv[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(sacc[s >> 1][qt][8 * (s & 1) + j] - m_use);
+      for (int j = 0; j < 8; ++j) {
+        const float x = sacc[s >> 1][qt][8 * (s & 1) + j];
+        pv[j] = fast_exp2(kFromMinusM ? x : x - m_sub);
+      }
       pop[qt][s] = pack8(pv);
       const uint4 w = __builtin_bit_cast(uint4, pop[qt][s]);
       float l = lsum[qt];
