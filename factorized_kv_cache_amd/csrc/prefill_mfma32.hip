@@ -81,30 +81,46 @@ struct Rebuild32 {
   typename RankWordP<R>::type av[IT];
 };
 
-// Keys past kend are clamped to the last valid key: they are masked out of
-// every score, so only finiteness matters.
+// The factor rows of one (sequence, head), as uniform bases: a key's
+// addresses are then one 32 x 32 -> 64-bit multiply-add from its index.
+struct RebuildBase32 {
+  const bf16_t* ak;    // A_K row of key 0, head hh
+  const bf16_t* av;
+  const bf16_t* bk;    // B~_K row of key 0 (in the shared mode, unused)
+  const bf16_t* bv;
+  uint32_t a_stride;   // elements per key of A_K / A_V (h * R)
+};
+
+template <int R>
+__device__ __forceinline__ RebuildBase32 rebuild_base32(const AttnArgs& a, int64_t seq0, int hh) {
+  RebuildBase32 r;
+  r.ak = reinterpret_cast<const bf16_t*>(a.c_ak) + (seq0 * a.h + hh) * R;
+  r.av = reinterpret_cast<const bf16_t*>(a.c_av) + (seq0 * a.h + hh) * R;
+  r.bk = reinterpret_cast<const bf16_t*>(a.c_bk) + seq0 * R * 64;
+  r.bv = reinterpret_cast<const bf16_t*>(a.c_bv) + seq0 * R * 64;
+  r.a_stride = (uint32_t)(a.h * R);
+  return r;
+}
+
+// Keys past klast (the last valid key) are clamped to it: they are masked out
+// of every score, so only finiteness matters.  Key indices are below 2^31.
 template <int R, bool SHARED = false>
-__device__ __forceinline__ void load_rebuild32(Rebuild32<R>& g, const AttnArgs& a, int64_t seq0, int hh, int64_t k0,
-                                               int64_t kend) {
+__device__ __forceinline__ void load_rebuild32(Rebuild32<R>& g, const RebuildBase32& p, int k0, int klast) {
   typedef typename RankWordP<R>::type W;
-  const bf16_t* AK = reinterpret_cast<const bf16_t*>(a.c_ak);
-  const bf16_t* BK = reinterpret_cast<const bf16_t*>(a.c_bk);
-  const bf16_t* AV = reinterpret_cast<const bf16_t*>(a.c_av);
-  const bf16_t* BV = reinterpret_cast<const bf16_t*>(a.c_bv);
 #pragma unroll
   for (int it = 0; it < Rebuild32<R>::IT; ++it) {
     const int item = threadIdx.x + Pf32Cfg<R>::NT * it;
     const int key = item >> 3, d0 = (item & 7) * 8;
-    int64_t t = k0 + key;
-    t = t < kend ? t : kend - 1;
-    const int64_t row = seq0 + t;
-    g.ak[it] = *reinterpret_cast<const W*>(AK + (row * a.h + hh) * R);
-    g.av[it] = *reinterpret_cast<const W*>(AV + (row * a.h + hh) * R);
+    const uint32_t t = (uint32_t)min(k0 + key, klast);
+    const uint64_t aoff = (uint64_t)t * p.a_stride;
+    g.ak[it] = *reinterpret_cast<const W*>(p.ak + aoff);
+    g.av[it] = *reinterpret_cast<const W*>(p.av + aoff);
     if constexpr (!SHARED) {   // (the shared bases are loaded once, by load_basis32)
+      const uint64_t boff = (uint64_t)t * (R * 64) + (uint32_t)d0;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        g.bk[it][r] = *reinterpret_cast<const uint4*>(BK + (row * R + r) * 64 + d0);
-        g.bv[it][r] = *reinterpret_cast<const uint4*>(BV + (row * R + r) * 64 + d0);
+        g.bk[it][r] = *reinterpret_cast<const uint4*>(p.bk + boff + r * 64);
+        g.bv[it][r] = *reinterpret_cast<const uint4*>(p.bv + boff + r * 64);
       }
     }
   }
@@ -330,7 +346,9 @@ __global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma3
     rope_stage(tab, 32, s_rev);
     load_basis32<R>(rg, a);
   }
-  load_rebuild32<R, SHARED>(rg, a, seq0, hh, 0, kend);
+  const RebuildBase32 rbase = rebuild_base32<R>(a, seq0, hh);
+  const int klast = (int)(kend - 1);
+  load_rebuild32<R, SHARED>(rg, rbase, 0, klast);
 
   // ---- query operand: lane (query q0 + 32*QT*wave + 32*qt + l32, d slice
   //      16*ks + 8*lh .. +8), pre-scaled
@@ -385,7 +403,7 @@ __global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma3
   // factors were loaded a block earlier.
   if constexpr (SHARED) __syncthreads();   // the staged frequencies are visible
   store_rebuild32<R, SHARED>(rg, lds, lds + 2 * TILE, 0, s_rev);
-  if (nblk > 1) load_rebuild32<R, SHARED>(rg, a, seq0, hh, BN, kend);
+  if (nblk > 1) load_rebuild32<R, SHARED>(rg, rbase, BN, klast);
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
     const int64_t k0 = (int64_t)blk * BN;
@@ -395,7 +413,7 @@ __global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma3
                         m_run, lsum, oacc);
     if (blk + 1 < nblk) {
       store_rebuild32<R, SHARED>(rg, lds + ((blk + 1) & 1) * TILE, lds + (2 + ((blk + 1) & 1)) * TILE, k0 + BN, s_rev);
-      if (blk + 2 < nblk) load_rebuild32<R, SHARED>(rg, a, seq0, hh, k0 + 2 * BN, kend);
+      if (blk + 2 < nblk) load_rebuild32<R, SHARED>(rg, rbase, (int)k0 + 2 * BN, klast);
     }
     __syncthreads();
   }
@@ -440,6 +458,8 @@ bool prefill_mfma32_supported(int dtype, const AttnArgs& a) {
   if (Pf32Cfg<4>::kLds > lds_per_block32() || Pf32Cfg<2>::kLds > lds_per_block32()) return false;
   constexpr int bm = Pf32Cfg<2>::BM;
   if ((a.S + bm - 1) / bm * (int64_t)a.h * a.n_batch >= ((int64_t)1 << 31)) return false;
+  // key indices, and a block's first key plus its width, stay 32-bit
+  if (a.start_pos + a.S > ((int64_t)1 << 31) - 256) return false;
   const void* ptrs[4] = {a.b_q, a.c_bk, a.c_bv, a.out};   // read/written 8 or 16 bytes at a time
   for (int i = 0; i < 4; ++i)
     if (((uintptr_t)ptrs[i]) % 16) return false;
