@@ -151,6 +151,12 @@ constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
 hipError_t decode_scratch(void** ptr);
 
 hipError_t launch_prefill(int dtype, const AttnArgs& a, hipStream_t st);
+// Prefill with a workspace for K and V formed once ([B][h][T][d_h], T =
+// start_pos + S): prefill_workspace_bytes is 0 where the shape takes no such
+// path; launch_prefill_ws with ws == nullptr, or on such a shape, is
+// launch_prefill.  ws holds at least prefill_workspace_bytes, 16-byte aligned.
+size_t prefill_workspace_bytes(int dtype, const AttnArgs& a);
+hipError_t launch_prefill_ws(int dtype, const AttnArgs& a, void* ws, hipStream_t st);
 // Prefill over a shared-basis cache: c_bk / c_bv are the bases B_K [R_K, d_h]
 // (unrotated) and B_V [R_V, d_h]; key t is rotated at position t with tab.
 hipError_t launch_prefill_shared(int dtype, const AttnArgs& a, const RopeTable& tab, hipStream_t st);

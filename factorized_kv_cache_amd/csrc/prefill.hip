@@ -192,6 +192,10 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t st);
 bool prefill_mfma32_supported(int dtype, const AttnArgs& a);
 hipError_t launch_prefill_mfma32(const AttnArgs& a, hipStream_t st);
 hipError_t launch_prefill_mfma32_shared(const AttnArgs& a, const RopeTable& tab, hipStream_t st);
+bool prefill_material_shape_ok(int dtype, const AttnArgs& a);
+bool prefill_material_supported(int dtype, const AttnArgs& a);
+size_t prefill_material_bytes(const AttnArgs& a);
+hipError_t launch_prefill_material(const AttnArgs& a, void* ws, hipStream_t st);
 
 // d_h = 64 runs on the 32x32x16 matrix-core kernel, d_h = 128 on the 16x16x32
 // one, every other shape (and fp32) on the general kernel.
@@ -200,6 +204,18 @@ hipError_t launch_prefill(int dtype, const AttnArgs& a, hipStream_t st) {
   if (prefill_mfma_supported(dtype, a)) return launch_prefill_mfma(a, st);
   static const RopeTable unused = {};
   return dtype == kF32 ? launch_prefill_t<float, false>(a, unused, st) : launch_prefill_t<bf16_t, false>(a, unused, st);
+}
+
+// With a workspace: where the 32x32x16 matrix-core kernel takes the shape, K
+// and V are formed once into the workspace and the attention reads them;
+// otherwise as launch_prefill.
+size_t prefill_workspace_bytes(int dtype, const AttnArgs& a) {
+  return prefill_material_shape_ok(dtype, a) ? prefill_material_bytes(a) : 0;
+}
+
+hipError_t launch_prefill_ws(int dtype, const AttnArgs& a, void* ws, hipStream_t st) {
+  if (ws && prefill_material_supported(dtype, a)) return launch_prefill_material(a, ws, st);
+  return launch_prefill(dtype, a, st);
 }
 
 // Shared-basis cache: the 32x32x16 matrix-core kernel where it takes the shape

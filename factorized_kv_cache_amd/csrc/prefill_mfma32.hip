@@ -32,13 +32,18 @@
 //    consecutive keys of their own column d);
 //  * the softmax denominators are the sums of the same bf16 probabilities
 //    (v_dot2 against ones), accumulated per lane and joined at the end.
-//    (Taking them on the matrix cores with a ones row, and starting the score
-//    accumulators from -m to drop the subtraction, both measured slower; so
-//    did forming the next block's scores a step ahead from a third buffer,
-//    with or without scheduling groups that interleave the matrix products
-//    with the softmax and rebuild: 4-9% slower at 4 x 4096 tokens.)
+//    (Taking them on the matrix cores with a ones row measured slower; so did
+//    forming the next block's scores a step ahead from a third buffer, with
+//    or without scheduling groups that interleave the matrix products with
+//    the softmax and rebuild: 4-9% slower at 4 x 4096 tokens.)
 //
 // Query blocks are scheduled heaviest (most keys) first, evenly across XCDs.
+//
+// The same kernel also reads K and V formed once for the whole call into a
+// workspace (kv_material32_kernel, same arithmetic and rounding as the
+// rebuild): each block is then two 16-byte loads and LDS stores per thread
+// instead of the rebuild's rank sums, which a 256-query workgroup would
+// otherwise repeat for every key it attends to.
 #include "kernels.h"
 #include "mfma.h"
 #include "rebuild.h"
@@ -167,6 +172,37 @@ __device__ __forceinline__ void store_rebuild32(const Rebuild32<R>& g, bf16_t* k
     }
     *reinterpret_cast<bf16x8_t*>(k_lds + key * LD + d0) = pack8(kv);
     *reinterpret_cast<bf16x8_t*>(v_lds + key * LD + d0) = pack8(vv);
+  }
+}
+
+// Materialised keys and values ([B][h][T][64] bf16, formed by
+// kv_material32_kernel): the thread's 16-byte row pieces of one 64-key block,
+// items as in the rebuild (consecutive lanes on consecutive slices of a row).
+struct KvRows32 {
+  static constexpr int IT = Pf32Cfg<2>::IT;
+  bf16x8_t k[IT];   // (native vectors: HIP's uint4 struct here went through scratch)
+  bf16x8_t v[IT];
+};
+
+__device__ __forceinline__ void load_kv32(KvRows32& g, const bf16_t* kb, const bf16_t* vb, int k0, int klast) {
+#pragma unroll
+  for (int it = 0; it < KvRows32::IT; ++it) {
+    const int item = threadIdx.x + Pf32Cfg<2>::NT * it;
+    const int key = item >> 3, d0 = (item & 7) * 8;
+    const uint64_t off = (uint64_t)(uint32_t)min(k0 + key, klast) * 64 + (uint32_t)d0;
+    g.k[it] = *reinterpret_cast<const bf16x8_t*>(kb + off);
+    g.v[it] = *reinterpret_cast<const bf16x8_t*>(vb + off);
+  }
+}
+
+__device__ __forceinline__ void store_kv32(const KvRows32& g, bf16_t* k_lds, bf16_t* v_lds) {
+  constexpr int LD = Pf32Cfg<2>::LD;
+#pragma unroll
+  for (int it = 0; it < KvRows32::IT; ++it) {
+    const int item = threadIdx.x + Pf32Cfg<2>::NT * it;
+    const int key = item >> 3, d0 = (item & 7) * 8;
+    *reinterpret_cast<bf16x8_t*>(k_lds + key * LD + d0) = g.k[it];
+    *reinterpret_cast<bf16x8_t*>(v_lds + key * LD + d0) = g.v[it];
   }
 }
 
@@ -304,11 +340,19 @@ __device__ __forceinline__ void attend_block32(const bf16_t* k_lds, const bf16_t
   }
 }
 
-// SHARED: the shared-basis cache (c_bk / c_bv are the bases; keys rotated at
-// their positions with tab).
-template <int R, bool SHARED>
-__global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma32_kernel(AttnArgs a, int n_qblocks,
-                                                                                       RopeTable tab) {
+// Where a block's keys and values come from: rebuilt from the cached factors,
+// rebuilt from a shared-basis cache (c_bk / c_bv are the bases; keys rotated at
+// their positions with tab), or read as formed by kv_material32_kernel (kmat,
+// vmat: mat_len keys per (sequence, head); instantiated with R = 2, whose
+// 64-key blocks it uses).
+enum KvSource : int { kFromFactors = 0, kFromSharedBasis = 1, kFromMaterial = 2 };
+
+template <int R, int SRC>
+__global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC)
+    prefill_mfma32_kernel(AttnArgs a, int n_qblocks, RopeTable tab, const bf16_t* kmat, const bf16_t* vmat,
+                          int64_t mat_len, int mat_group) {
+  constexpr bool SHARED = SRC == kFromSharedBasis, MAT = SRC == kFromMaterial;
+  static_assert(!MAT || R == 2, "materialised blocks use the 64-key configuration");
   using C = Pf32Cfg<R>;
   constexpr int DH = 64, QT = C::QT, BM = C::BM, BN = C::BN, TILE = C::TILE;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -325,12 +369,30 @@ __global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma3
   // pairs split evenly over the eight XCDs, XCD x takes the x-th contiguous
   // range of them (sequence-major), so the factors it reads span as few
   // sequences as possible and stay in its L2.
+  //
+  // Materialised K and V are per head.  With many query blocks per pair that
+  // order would leave every resident workgroup of an XCD on another pair, each
+  // reading its own K and V from HBM.  So (mat_group > 0) an XCD's range of
+  // pairs is taken in groups of mat_group pairs, one group after another, each
+  // group in the order above (query block major, heaviest first): a group's
+  // K and V are then read by about mat_group * n_qblocks workgroups that run
+  // together.  The host picks mat_group so that a group spans about two
+  // rounds of an XCD's resident workgroups (all of its pairs when they fit).
   const int h = a.h;
   const int64_t hb = (int64_t)h * a.n_batch;
   const int64_t L = blockIdx.x;
-  const int qb = n_qblocks - 1 - (int)(L / hb);
-  int64_t u = L % hb;
-  if (hb % 8 == 0) u = (u & 7) * (hb >> 3) + (u >> 3);
+  int qb;
+  int64_t u;
+  if (MAT && mat_group > 0 && hb % 8 == 0) {
+    const int64_t s = L >> 3, span = (int64_t)mat_group * n_qblocks;
+    const int64_t r = s % span;
+    qb = n_qblocks - 1 - (int)(r / mat_group);
+    u = (L & 7) * (hb >> 3) + s / span * mat_group + r % mat_group;
+  } else {
+    qb = n_qblocks - 1 - (int)(L / hb);
+    u = L % hb;
+    if (hb % 8 == 0) u = (u & 7) * (hb >> 3) + (u >> 3);
+  }
   const int hh = (int)(u % h);
   const int64_t b = u / h;
   const int64_t q0 = (int64_t)qb * BM;
@@ -339,16 +401,32 @@ __global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma3
   const int64_t kend = a.causal ? a.start_pos + last_q + 1 : a.start_pos + a.S;
   const int nblk = (int)((kend + BN - 1) / BN);
 
-  // The first key block's factors go out before anything else.
-  Rebuild32<R> rg;
+  // The first key block's loads go out before anything else.
+  typename std::conditional<MAT, KvRows32, Rebuild32<R>>::type rg;
   __shared__ double s_rev[SHARED ? 32 : 1];   // d_h = 64: 32 rotary pairs
   if constexpr (SHARED) {
     rope_stage(tab, 32, s_rev);
     load_basis32<R>(rg, a);
   }
   const RebuildBase32 rbase = rebuild_base32<R>(a, seq0, hh);
+  const bf16_t* const kb = MAT ? kmat + ((b * h + hh) * mat_len) * 64 : nullptr;
+  const bf16_t* const vb = MAT ? vmat + ((b * h + hh) * mat_len) * 64 : nullptr;
   const int klast = (int)(kend - 1);
-  load_rebuild32<R, SHARED>(rg, rbase, 0, klast);
+#define TPA_PF32_LOAD(k0)                       \
+  do {                                          \
+    if constexpr (MAT)                          \
+      load_kv32(rg, kb, vb, k0, klast);         \
+    else                                        \
+      load_rebuild32<R, SHARED>(rg, rbase, k0, klast); \
+  } while (0)
+#define TPA_PF32_STORE(k_lds, v_lds, k0)                       \
+  do {                                                         \
+    if constexpr (MAT)                                         \
+      store_kv32(rg, k_lds, v_lds);                            \
+    else                                                       \
+      store_rebuild32<R, SHARED>(rg, k_lds, v_lds, k0, s_rev); \
+  } while (0)
+  TPA_PF32_LOAD(0);
 
   // ---- query operand: lane (query q0 + 32*QT*wave + 32*qt + l32, d slice
   //      16*ks + 8*lh .. +8), pre-scaled
@@ -402,8 +480,8 @@ __global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma3
   // Block i is rebuilt into buffer i & 1 while block i - 1 is attended to; its
   // factors were loaded a block earlier.
   if constexpr (SHARED) __syncthreads();   // the staged frequencies are visible
-  store_rebuild32<R, SHARED>(rg, lds, lds + 2 * TILE, 0, s_rev);
-  if (nblk > 1) load_rebuild32<R, SHARED>(rg, rbase, BN, klast);
+  TPA_PF32_STORE(lds, lds + 2 * TILE, 0);
+  if (nblk > 1) TPA_PF32_LOAD(BN);
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
     const int64_t k0 = (int64_t)blk * BN;
@@ -412,11 +490,14 @@ __global__ void __launch_bounds__(Pf32Cfg<R>::NT, Pf32Cfg<R>::OCC) prefill_mfma3
       attend_block32<R>(lds + (blk & 1) * TILE, lds + (2 + (blk & 1)) * TILE, k0, kend, wpos0, causal, lane, qop,
                         m_run, lsum, oacc);
     if (blk + 1 < nblk) {
-      store_rebuild32<R, SHARED>(rg, lds + ((blk + 1) & 1) * TILE, lds + (2 + ((blk + 1) & 1)) * TILE, k0 + BN, s_rev);
-      if (blk + 2 < nblk) load_rebuild32<R, SHARED>(rg, rbase, (int)k0 + 2 * BN, klast);
+      TPA_PF32_STORE(lds + ((blk + 1) & 1) * TILE, lds + (2 + ((blk + 1) & 1)) * TILE, k0 + BN);
+      if (blk + 2 < nblk) TPA_PF32_LOAD((int)k0 + 2 * BN);
     }
     __syncthreads();
   }
+
+#undef TPA_PF32_LOAD
+#undef TPA_PF32_STORE
 
   // ---- normalise and store: value e of tile (qt, dt) is d = 32*dt + 8*(e/4)
   //      + 4*lh + e%4 of query l32; its two lanes (l32, l32 + 32) hold the
@@ -466,30 +547,111 @@ bool prefill_mfma32_supported(int dtype, const AttnArgs& a) {
   return true;
 }
 
-template <bool SHARED>
-static hipError_t launch_pf32(const AttnArgs& a, const RopeTable& tab, hipStream_t st) {
+// K and V of every (sequence, head) and key 0 .. T-1, formed once:
+// km[b][h][t][:] = bf16(sum_r A_K[b,t,h,r] B~_K[b,t,r,:]) and vm likewise, the
+// same arithmetic and rounding as the rebuild in LDS.  One thread per (key,
+// head, 8-wide slice) of sequence blockIdx.y; consecutive threads share a key,
+// so its dim-factor rows are read once per key from the cache.
+template <int R>
+__global__ void __launch_bounds__(256) kv_material32_kernel(AttnArgs a, int64_t T, bf16_t* km, bf16_t* vm) {
+  typedef typename RankWordP<R>::type W;
+  const int h = a.h;
+  const int i = (int)(blockIdx.x * 256 + threadIdx.x);
+  if ((int64_t)i >= T * h * 8) return;
+  const int64_t b = blockIdx.y;
+  const int slice = i & 7, r = i >> 3;
+  const int hh = r % h, t = r / h;
+  const int64_t row = b * a.max_seq + t;
+  const W ak = *reinterpret_cast<const W*>(reinterpret_cast<const bf16_t*>(a.c_ak) + (row * h + hh) * R);
+  const W av = *reinterpret_cast<const W*>(reinterpret_cast<const bf16_t*>(a.c_av) + (row * h + hh) * R);
+  uint4 bk[R], bv[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    bk[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.c_bk) + (row * R + q) * 64 + slice * 8);
+    bv[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.c_bv) + (row * R + q) * 64 + slice * 8);
+  }
+  float kv[8], vv[8];
+  factor_combine<R>(ak, bk, kv);
+  factor_combine<R>(av, bv, vv);
+  const int64_t o = ((b * h + hh) * T + t) * 64 + slice * 8;
+  *reinterpret_cast<bf16x8_t*>(km + o) = pack8(kv);
+  *reinterpret_cast<bf16x8_t*>(vm + o) = pack8(vv);
+}
+
+// Pairs per group for the materialised order: the largest divisor of an XCD's
+// pair count whose group holds at most about two rounds of the XCD's resident
+// workgroups (32 CUs x 2), at least 1.
+static int material_group(int64_t pairs, int nqb) {
+  if (pairs % 8) return 0;
+  const int64_t per_xcd = pairs / 8, budget = 128;
+  int64_t g = budget / nqb < 1 ? 1 : budget / nqb;
+  if (g > per_xcd) g = per_xcd;
+  while (per_xcd % g) --g;
+  return (int)g;
+}
+
+template <int SRC>
+static hipError_t launch_pf32(const AttnArgs& a, const RopeTable& tab, const bf16_t* kmat, const bf16_t* vmat,
+                              int64_t mat_len, hipStream_t st) {
   constexpr int bm = Pf32Cfg<2>::BM;
   const int nqb = (int)((a.S + bm - 1) / bm);
   const dim3 grid((unsigned)((int64_t)nqb * a.h * a.n_batch));
-  if (a.rk == 1)
-    hipLaunchKernelGGL((prefill_mfma32_kernel<1, SHARED>), grid, dim3(Pf32Cfg<1>::NT), (Pf32Cfg<1>::kLds), st, a, nqb,
-                       tab);
-  else if (a.rk == 2)
-    hipLaunchKernelGGL((prefill_mfma32_kernel<2, SHARED>), grid, dim3(Pf32Cfg<2>::NT), (Pf32Cfg<2>::kLds), st, a, nqb,
-                       tab);
+  const int grp = SRC == kFromMaterial ? material_group((int64_t)a.h * a.n_batch, nqb) : 0;
+  if (SRC == kFromMaterial || a.rk == 2)
+    hipLaunchKernelGGL((prefill_mfma32_kernel<2, SRC>), grid, dim3(Pf32Cfg<2>::NT), (Pf32Cfg<2>::kLds), st, a, nqb,
+                       tab, kmat, vmat, mat_len, grp);
+  else if (a.rk == 1)
+    hipLaunchKernelGGL((prefill_mfma32_kernel<1, SRC == kFromMaterial ? kFromFactors : SRC>), grid,
+                       dim3(Pf32Cfg<1>::NT), (Pf32Cfg<1>::kLds), st, a, nqb, tab, kmat, vmat, mat_len, grp);
   else
-    hipLaunchKernelGGL((prefill_mfma32_kernel<4, SHARED>), grid, dim3(Pf32Cfg<4>::NT), (Pf32Cfg<4>::kLds), st, a, nqb,
-                       tab);
+    hipLaunchKernelGGL((prefill_mfma32_kernel<4, SRC == kFromMaterial ? kFromFactors : SRC>), grid,
+                       dim3(Pf32Cfg<4>::NT), (Pf32Cfg<4>::kLds), st, a, nqb, tab, kmat, vmat, mat_len, grp);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_mfma32(const AttnArgs& a, hipStream_t st) {
   static const RopeTable unused = {};
-  return launch_pf32<false>(a, unused, st);
+  return launch_pf32<kFromFactors>(a, unused, nullptr, nullptr, 0, st);
 }
 
 hipError_t launch_prefill_mfma32_shared(const AttnArgs& a, const RopeTable& tab, hipStream_t st) {
-  return launch_pf32<true>(a, tab, st);
+  return launch_pf32<kFromSharedBasis>(a, tab, nullptr, nullptr, 0, st);
+}
+
+// The shapes the workspace path takes, from sizes alone (no device or pointer
+// checks: the workspace is sized and validated by these).
+bool prefill_material_shape_ok(int dtype, const AttnArgs& a) {
+  if (dtype != kBF16 || a.d_h != 64) return false;
+  if (a.rk != a.rv || !(a.rk == 1 || a.rk == 2 || a.rk == 4)) return false;
+  constexpr int bm = Pf32Cfg<2>::BM;
+  if ((a.S + bm - 1) / bm * (int64_t)a.h * a.n_batch >= ((int64_t)1 << 31)) return false;
+  // the materialising kernel indexes (key, head, slice) of a sequence in 32 bits
+  return (a.start_pos + a.S) * a.h * 8 < ((int64_t)1 << 31) - 256;
+}
+
+bool prefill_material_supported(int dtype, const AttnArgs& a) {
+  return prefill_material_shape_ok(dtype, a) && prefill_mfma32_supported(dtype, a);
+}
+
+size_t prefill_material_bytes(const AttnArgs& a) {
+  return (size_t)2 * a.n_batch * a.h * (a.start_pos + a.S) * 64 * sizeof(bf16_t);
+}
+
+hipError_t launch_prefill_material(const AttnArgs& a, void* ws, hipStream_t st) {
+  const int64_t T = a.start_pos + a.S;
+  bf16_t* km = reinterpret_cast<bf16_t*>(ws);
+  bf16_t* vm = km + a.n_batch * a.h * T * 64;
+  const dim3 mgrid((unsigned)((T * a.h * 8 + 255) / 256), (unsigned)a.n_batch);
+  if (a.rk == 1)
+    hipLaunchKernelGGL(kv_material32_kernel<1>, mgrid, dim3(256), 0, st, a, T, km, vm);
+  else if (a.rk == 2)
+    hipLaunchKernelGGL(kv_material32_kernel<2>, mgrid, dim3(256), 0, st, a, T, km, vm);
+  else
+    hipLaunchKernelGGL(kv_material32_kernel<4>, mgrid, dim3(256), 0, st, a, T, km, vm);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  static const RopeTable unused = {};
+  return launch_pf32<kFromMaterial>(a, unused, km, vm, T, st);
 }
 
 }  // namespace tpa

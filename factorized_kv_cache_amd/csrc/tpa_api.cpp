@@ -347,8 +347,9 @@ tpa_status tpa_cache_append(const tpa_dims* d, const tpa_cache* c, const tpa_fac
   return hip_status(tpa::launch_append(a, (hipStream_t)stream), "tpa_cache_append");
 }
 
-tpa_status tpa_prefill_attn(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
-                            int64_t seq_len, int64_t start_pos, int32_t causal, void* out, void* stream) {
+// Checks shared by the two prefill entry points; fills the kernel arguments.
+static tpa_status prefill_args(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
+                               int64_t seq_len, int64_t start_pos, int32_t causal, void* out, tpa::AttnArgs* a) {
   tpa_status st = check_dims(d);
   if (st != TPA_OK) return st;
   if ((st = check_query(d, q)) != TPA_OK) return st;
@@ -365,8 +366,45 @@ tpa_status tpa_prefill_attn(const tpa_dims* d, const tpa_factors* q, const tpa_c
                 (long long)seq_len, (long long)c->max_seq);
   int64_t qs;
   if ((st = resolve_stride(q->q_batch_stride, seq_len, "q_batch_stride", &qs)) != TPA_OK) return st;
-  tpa::AttnArgs a = attn_args(d, q, qs, c, n_batch, seq_len, start_pos, causal, out);
+  *a = attn_args(d, q, qs, c, n_batch, seq_len, start_pos, causal, out);
+  return TPA_OK;
+}
+
+tpa_status tpa_prefill_attn(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
+                            int64_t seq_len, int64_t start_pos, int32_t causal, void* out, void* stream) {
+  tpa::AttnArgs a;
+  const tpa_status st = prefill_args(d, q, c, n_batch, seq_len, start_pos, causal, out, &a);
+  if (st != TPA_OK) return st;
   return hip_status(tpa::launch_prefill(d->dtype, a, (hipStream_t)stream), "tpa_prefill_attn");
+}
+
+size_t tpa_prefill_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t seq_len, int64_t start_pos) {
+  if (check_dims(d) != TPA_OK || n_batch < 1 || seq_len < 1 || start_pos < 0) return 0;
+  if (n_batch > 65535 || !positions_ok(start_pos, seq_len)) return 0;   // sizes the call rejects
+  tpa_factors q;
+  memset(&q, 0, sizeof(q));
+  tpa_cache c;
+  memset(&c, 0, sizeof(c));
+  c.max_seq = start_pos + seq_len;
+  const tpa::AttnArgs a = attn_args(d, &q, seq_len, &c, n_batch, seq_len, start_pos, 1, nullptr);
+  return tpa::prefill_workspace_bytes(d->dtype, a);
+}
+
+tpa_status tpa_prefill_attn_ws(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
+                               int64_t seq_len, int64_t start_pos, int32_t causal, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  tpa::AttnArgs a;
+  const tpa_status st = prefill_args(d, q, c, n_batch, seq_len, start_pos, causal, out, &a);
+  if (st != TPA_OK) return st;
+  const size_t need = tpa::prefill_workspace_bytes(d->dtype, a);
+  if (need > 0) {
+    if (!workspace) return fail(TPA_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
+    if ((uintptr_t)workspace % 16) return fail(TPA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(TPA_ERR_CAPACITY, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  return hip_status(tpa::launch_prefill_ws(d->dtype, a, need > 0 ? workspace : nullptr, (hipStream_t)stream),
+                    "tpa_prefill_attn_ws");
 }
 
 size_t tpa_decode_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t ctx_len) {

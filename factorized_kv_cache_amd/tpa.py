@@ -69,6 +69,9 @@ def _load():
         "tpa_rope_b": (ctypes.c_int, [P(tpa_dims), vp, i64, i64, i32, i64, vp]),
         "tpa_cache_append": (ctypes.c_int, [P(tpa_dims), P(tpa_cache), P(tpa_factors), i64, i64, i64, vp]),
         "tpa_prefill_attn": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_cache), i64, i64, i64, i32, vp, vp]),
+        "tpa_prefill_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64, i64]),
+        "tpa_prefill_attn_ws": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_cache), i64, i64, i64, i32, vp,
+                                               vp, ctypes.c_size_t, vp]),
         "tpa_decode_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64]),
         "tpa_decode_attn": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_cache), i64, i64, vp, vp,
                                            ctypes.c_size_t, vp]),
@@ -104,7 +107,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("tpa_packed_weight_rows", "tpa_cache_elems_per_token", "tpa_factor_proj", "tpa_rope_b",
-            "tpa_cache_append", "tpa_prefill_attn", "tpa_decode_workspace_bytes", "tpa_decode_attn",
+            "tpa_cache_append", "tpa_prefill_attn", "tpa_prefill_workspace_bytes", "tpa_prefill_attn_ws",
+            "tpa_decode_workspace_bytes", "tpa_decode_attn",
             "tpa_decode_noalloc_max_bytes", "tpa_decode_attn_noalloc",
             "tpa_prefill_backward_workspace_bytes", "tpa_prefill_attn_backward", "tpa_rope_b_backward",
             "tpa_paged_cache_append", "tpa_paged_decode_workspace_bytes", "tpa_paged_decode_attn",
@@ -351,6 +355,22 @@ def tpa_prefill_attn(dims: Dims, q: Factors, cache: Cache, start_pos: int, causa
         out = torch.empty(B, S, dims.n_heads * dims.head_dim, dtype=dims.torch_dtype, device=q.b_q.device)
     _check(_lib.tpa_prefill_attn(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B, S,
                                  start_pos, 1 if causal else 0, _ptr(out), _stream(stream)))
+    return out
+
+
+def tpa_prefill_workspace_bytes(dims: Dims, batch: int, seq: int, start_pos: int) -> int:
+    return int(_lib.tpa_prefill_workspace_bytes(ctypes.byref(dims.c()), batch, seq, start_pos))
+
+
+def tpa_prefill_attn_ws(dims: Dims, q: Factors, cache: Cache, start_pos: int, workspace: Optional[torch.Tensor],
+                        causal: bool = True, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    B, S = q.b_q.shape[0], q.b_q.shape[1]
+    if out is None:
+        out = torch.empty(B, S, dims.n_heads * dims.head_dim, dtype=dims.torch_dtype, device=q.b_q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.tpa_prefill_attn_ws(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B, S,
+                                    start_pos, 1 if causal else 0, _ptr(out), _ptr(workspace), nbytes,
+                                    _stream(stream)))
     return out
 
 

@@ -180,6 +180,35 @@ tpa_status tpa_prefill_attn(const tpa_dims* dims, const tpa_factors* q, const tp
                             int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
                             void* stream);
 
+/* Bytes of device workspace tpa_prefill_attn_ws uses for these sizes:
+ * 2 * n_batch * h * (start_pos + seq_len) * d_h * 2 where the matrix-core path
+ * that forms K and V once applies (bf16, d_h = 64, R_K = R_V in {1, 2, 4}),
+ * else 0 (the call then needs no workspace).  0 also for dims or sizes the
+ * call rejects. */
+size_t tpa_prefill_workspace_bytes(const tpa_dims* dims, int64_t n_batch, int64_t seq_len, int64_t start_pos);
+
+/* tpa_prefill_attn with a caller-owned workspace: the same attention (same
+ * passage), computed by first forming k_t and v_t of every key 0 ..
+ * start_pos+S-1 and head once, rounded to the compute dtype exactly as
+ * tpa_prefill_attn rounds them in on-chip memory, into the workspace
+ * ([B][h][start_pos+S][d_h] for K, then V), and then attending over them.
+ * Prefill is bound by arithmetic, and forming each key and value once
+ * instead of once per 256-query block removes most of that work's vector
+ * instructions.  Outputs match tpa_prefill_attn's bit for bit at R_K = R_V
+ * in {1, 2}; at rank 4 the keys are taken in 64- rather than 32-key blocks,
+ * so only the online softmax's summation order differs.  Where
+ * tpa_prefill_workspace_bytes is 0 (or the pointers are not 16-byte
+ * aligned) the call runs tpa_prefill_attn and ignores the workspace.
+ * workspace: device memory of at least tpa_prefill_workspace_bytes bytes,
+ * 16-byte aligned, owned by the caller, overwritten; no contents are kept
+ * between calls.  Calls that share a workspace must be ordered on one stream.
+ * Errors: as tpa_prefill_attn; a NULL or misaligned workspace
+ * (TPA_ERR_INVALID_ARGUMENT) or one smaller than needed (TPA_ERR_CAPACITY)
+ * where one is needed. */
+tpa_status tpa_prefill_attn_ws(const tpa_dims* dims, const tpa_factors* q, const tpa_cache* cache,
+                               int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace tpa_decode_attn needs for this batch and context;
  * 0 for dims or sizes that call rejects (n_batch outside 1..65535, ctx_len
  * outside 1 .. 2^31 - 1). */

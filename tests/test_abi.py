@@ -137,6 +137,34 @@ def test_prefill_validation():
                                 ctypes.byref(c), 1, 1, 0, 1, FAKE, None) == INVALID
 
 
+def test_prefill_workspace_sizes_and_validation():
+    """The workspace prefill needs 2 * B * h * (start_pos + S) * d_h * 2 bytes
+    where K and V are formed once (bf16, d_h 64, R_K = R_V in {1, 2, 4}), none
+    elsewhere; a missing, misaligned or short workspace is rejected before
+    anything is enqueued, after the checks the plain prefill makes."""
+    lib = T.library()
+    ws = lambda dd, B, S, sp: lib.tpa_prefill_workspace_bytes(ctypes.byref(dd), B, S, sp)
+    d = dims()
+    assert ws(d, 2, 40, 24) == 2 * 2 * 16 * 64 * 64 * 2
+    assert ws(dims(rank_k=4, rank_v=4), 1, 1, 0) == 2 * 16 * 64 * 2
+    assert ws(dims(rank_k=1, rank_v=1, n_heads=5, d_model=320), 3, 7, 0) == 2 * 3 * 5 * 7 * 64 * 2
+    for other in (dims(dtype=0), dims(head_dim=128, d_model=2048), dims(rank_k=2, rank_v=1), dims(rank_k=3, rank_v=3)):
+        assert ws(other, 2, 40, 24) == 0
+    for B, S, sp in ((0, 1, 0), (1, 0, 0), (1, 1, -1), (65536, 1, 0), (1, 2**31, 0), (1, 1, 2**31), (1, 2**62, 2**62)):
+        assert ws(d, B, S, sp) == 0, (B, S, sp)
+    need = ws(d, 2, 8, 0)
+    c = T.tpa_cache(FAKE, FAKE, FAKE, FAKE, 2, 64)
+    q = T.tpa_factors(FAKE, FAKE, None, None, None, None, 0, 0)
+    pf = lambda B, S, sp, w=FAKE, n=need: lib.tpa_prefill_attn_ws(ctypes.byref(d), ctypes.byref(q), ctypes.byref(c),
+                                                                  B, S, sp, 1, FAKE, w, n, None)
+    assert pf(3, 4, 0) == CAPACITY
+    assert pf(2, 65, 0) == CAPACITY
+    assert pf(2, 8, 0, w=None) == INVALID
+    assert pf(2, 8, 0, w=FAKE + 8) == INVALID
+    assert pf(2, 8, 0, n=need - 1) == CAPACITY
+    assert pf(2, 8, 2, n=need) == CAPACITY   # two more keys than sized for
+
+
 def test_decode_validation():
     lib = T.library()
     d = dims()

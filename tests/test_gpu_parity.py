@@ -209,6 +209,8 @@ PREFILL_CASES = [
     ("dh256_f32", "f32", 1, 40, 0, True, 64, 2, 256, 2, 2, 2, 0.5),
     ("odd_heads_r1_bf16", "bf16", 2, 200, 7, True, 320, 5, 64, 3, 1, 1, 1.0),
     ("odd_heads_dh128_bf16", "bf16", 1, 150, 0, True, 384, 3, 128, 2, 2, 2, 1.0),
+    ("kvonly_chunk_bf16", "bf16", 2, 100, 150, True, 1536, 24, 64, 0, 4, 4, 1.0),
+    ("r1_noncausal_bf16", "bf16", 2, 77, 20, False, 256, 8, 64, 2, 1, 1, 1.0),
     # the dims limits
     ("limit_dh256_r64_fp32", "f32", 1, 24, 3, True, 128, 32, 256, 64, 64, 64, 3.0),
     ("limit_dh256_r64_bf16", "bf16", 1, 24, 3, True, 128, 32, 256, 64, 64, 64, 3.0),
@@ -217,12 +219,24 @@ PREFILL_CASES = [
 ]
 
 
+def prefill(dims, q, cache, sp, causal, path):
+    """tpa_prefill_attn, or (path "ws") tpa_prefill_attn_ws with a workspace of
+    the size the library asks for (none where it asks for none)."""
+    if path == "fused":
+        return T.tpa_prefill_attn(dims, q, cache, sp, causal)
+    B, S = q.b_q.shape[0], q.b_q.shape[1]
+    n = T.tpa_prefill_workspace_bytes(dims, B, S, sp)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+    return T.tpa_prefill_attn_ws(dims, q, cache, sp, ws, causal)
+
+
+@pytest.mark.parametrize("path", ["fused", "ws"])
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
-def test_prefill(case):
+def test_prefill(case, path):
     require_gpu()
     name, dtype, B, S, sp, causal, dm, h, dh, rq, rk, rv, std = case
     dims = D(dm, h, dh, rq, rk, rv, dtype)
-    announce(f"prefill {name} B={B} S={S} sp={sp} causal={causal}")
+    announce(f"prefill {name} B={B} S={S} sp={sp} causal={causal} path={path}")
     sh = shape_of(dims)
     Tn = sp + S
     kv = I.factors(sh, B, Tn, seed=71, dtype=dtype, std=std, with_query=False, v_std=value_std(std))
@@ -230,11 +244,45 @@ def test_prefill(case):
     cache = T.new_cache(dims, B, Tn + 5)
     fill_cache(cache, kv)
     q = query_factors_gpu(T, dims, fq)
-    out = T.tpa_prefill_attn(dims, q, cache, sp, causal)
+    out = prefill(dims, q, cache, sp, causal, path)
     torch.cuda.synchronize()
     od = oracle_dims(dims)
     ref = O.prefill(oracle_query(fq, dims), oracle_cache(kv, od, B, Tn + 5), od, B, S, sp, causal)
-    assert_close(out, ref, dtype, f"prefill {name}")
+    assert_close(out, ref, dtype, f"prefill {name} ({path})")
+
+
+WS_BITWISE_CASES = [
+    # dtype bf16, d_h 64: B, S, start_pos, causal, d_model, h, rq, rk, rv
+    (2, 300, 0, True, 1024, 16, 6, 2, 2),
+    (3, 257, 41, True, 320, 5, 3, 1, 1),
+    (2, 90, 30, False, 1024, 16, 6, 2, 2),
+    (1, 1, 0, True, 256, 8, 2, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", WS_BITWISE_CASES)
+def test_prefill_ws_matches_fused_bitwise(case):
+    """At ranks 1 and 2 the workspace path forms the same bf16 K and V as the
+    rebuild in LDS and attends in the same 64-key blocks and order: the outputs
+    are equal bit for bit.  Workspace contents from an earlier, larger call do
+    not leak into a later one."""
+    require_gpu()
+    B, S, sp, causal, dm, h, rq, rk, rv = case
+    dims = D(dm, h, 64, rq, rk, rv, "bf16")
+    announce(f"prefill ws vs fused bitwise case={case}")
+    sh = shape_of(dims)
+    kv = I.factors(sh, B, sp + S, seed=75, dtype="bf16", std=1.0, with_query=False, v_std=value_std(1.0))
+    fq = I.factors(sh, B, S, seed=76, dtype="bf16", std=1.0)
+    cache = T.new_cache(dims, B, sp + S)
+    fill_cache(cache, kv)
+    q = query_factors_gpu(T, dims, fq)
+    n = T.tpa_prefill_workspace_bytes(dims, B, S, sp)
+    assert n == 2 * B * h * (sp + S) * 64 * 2
+    ws = torch.full((n + 4096,), 0x7f, dtype=torch.uint8, device="cuda")   # stale bytes: huge bf16 values
+    fused = T.tpa_prefill_attn(dims, q, cache, sp, causal)
+    staged = T.tpa_prefill_attn_ws(dims, q, cache, sp, ws, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, staged)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -324,23 +372,24 @@ def test_decode_general_path_matches_fast_path():
     assert_close(slow, ref, "bf16", "decode general path")
 
 
+@pytest.mark.parametrize("path", ["fused", "ws"])
 @pytest.mark.parametrize("wl_name,B,S,n_rows", [
     ("prefill_b4_s4k", 4, 4096, 48),       # the causal prefill workload at full size
     ("kvonly_b32_ctx16k", 2, 2048, 32),    # the KV-only shape, two sequences of 2048
 ])
-def test_prefill_full_size_sampled_rows(wl_name, B, S, n_rows):
+def test_prefill_full_size_sampled_rows(wl_name, B, S, n_rows, path):
     """Prefill in the launch configuration the benchmark times; the oracle computes
     sampled query rows one by one (each row is its own definition)."""
     require_gpu()
     wl = I.WORKLOADS[wl_name]
     sh = wl.shape
     dims = D(sh.d_model, sh.n_heads, sh.head_dim, sh.rank_q, sh.rank_k, sh.rank_v, "bf16")
-    announce(f"prefill full size {wl_name} B={B} S={S}")
+    announce(f"prefill full size {wl_name} B={B} S={S} path={path}")
     kv = I.factors(sh, B, S, seed=101, dtype="bf16", with_query=False)
     fq = I.factors(sh, B, S, seed=102, dtype="bf16")
     cache = T.new_cache(dims, B, S)
     fill_cache(cache, kv)
-    out = T.tpa_prefill_attn(dims, query_factors_gpu(T, dims, fq), cache, 0, True)
+    out = prefill(dims, query_factors_gpu(T, dims, fq), cache, 0, True, path)
     torch.cuda.synchronize()
     rng = np.random.default_rng(7)
     rows = np.unique(np.concatenate([[0, 1, S - 1], rng.integers(0, S, n_rows)]))
@@ -349,7 +398,8 @@ def test_prefill_full_size_sampled_rows(wl_name, B, S, n_rows):
     assert_close(out[:, rows], ref[:, rows], "bf16", f"prefill {wl_name} sampled rows")
 
 
-def test_prefill_kvonly_full_size_sampled_rows():
+@pytest.mark.parametrize("path", ["fused", "ws"])
+def test_prefill_kvonly_full_size_sampled_rows(path):
     """The KV-only prefill at its full size (32 sequences of 16,384 tokens, 24
     heads of 64, plain Q, R 4) in one call; the oracle checks 256 sampled query
     rows (16 per sequence, 16 sequences, every head), rebuilding each sampled
@@ -359,12 +409,12 @@ def test_prefill_kvonly_full_size_sampled_rows():
     sh = wl.shape
     dims = D(sh.d_model, sh.n_heads, sh.head_dim, sh.rank_q, sh.rank_k, sh.rank_v, "bf16")
     B, S = wl.batch, wl.seq
-    announce(f"prefill full size kvonly_b32_ctx16k B={B} S={S}")
+    announce(f"prefill full size kvonly_b32_ctx16k B={B} S={S} path={path}")
     kv = I.factors(sh, B, S, seed=141, dtype="bf16", with_query=False)
     fq = I.factors(sh, B, S, seed=142, dtype="bf16")
     cache = T.new_cache(dims, B, S)
     fill_cache(cache, kv)
-    out = T.tpa_prefill_attn(dims, query_factors_gpu(T, dims, fq), cache, 0, True)
+    out = prefill(dims, query_factors_gpu(T, dims, fq), cache, 0, True, path)
     torch.cuda.synchronize()
     del cache
     rng = np.random.default_rng(143)
