@@ -215,21 +215,25 @@ def run_kvonly(reps: int = 8, dec_reps: int = 100):
     cache = T.new_cache(d, B, S + 1)
     f = T.new_factors(d, B, S)
     out = torch.empty(B, S, d.n_heads * d.head_dim, dtype=torch.bfloat16, device="cuda")
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    times = {"proj": [], "append": [], "attn": []}
+    ws = torch.empty(T.tpa_prefill_workspace_bytes(d, B, S, 0), dtype=torch.uint8, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    times = {"proj": [], "append": [], "attn": [], "attn_no_ws": []}
     for r in range(reps + 1):
         ev[0].record()
         T.tpa_factor_proj(d, x, wp, f, start_pos=0)
         ev[1].record()
         T.tpa_cache_append(d, cache, f, 0)
         ev[2].record()
-        T.tpa_prefill_attn(d, f, cache, 0, True, out=out)
+        T.tpa_prefill_attn_ws(d, f, cache, 0, ws, True, out=out)
         ev[3].record()
+        T.tpa_prefill_attn(d, f, cache, 0, True, out=out)
+        ev[4].record()
         torch.cuda.synchronize()
         if r:
             times["proj"].append(ev[0].elapsed_time(ev[1]))
             times["append"].append(ev[1].elapsed_time(ev[2]))
             times["attn"].append(ev[2].elapsed_time(ev[3]))
+            times["attn_no_ws"].append(ev[3].elapsed_time(ev[4]))
     n_out = T.tpa_packed_weight_rows(d)
     attn_flop = 4.0 * B * d.n_heads * d.head_dim * S * (S + 1) / 2
     proj_flop = 2.0 * B * S * d.d_model * n_out
@@ -240,6 +244,10 @@ def run_kvonly(reps: int = 8, dec_reps: int = 100):
         "attn_ms": round(st["attn"]["mean"], 3), "attn_ms_p10_p90": [round(st["attn"]["p10"], 3), round(st["attn"]["p90"], 3)],
         "attn_tflops": round(attn_flop / st["attn"]["mean"] / 1e9, 1),
         "attn_frac_bf16_peak": round(attn_flop / st["attn"]["mean"] / 1e9 / BF16_PEAK_TFLOPS, 4),
+        "attn_path": "tpa_prefill_attn_ws (K and V formed once into a workspace, then attended)",
+        "workspace_bytes": ws.numel(),
+        "attn_no_workspace_ms": round(st["attn_no_ws"]["mean"], 3),
+        "attn_no_workspace_frac_bf16_peak": round(attn_flop / st["attn_no_ws"]["mean"] / 1e9 / BF16_PEAK_TFLOPS, 4),
         "proj_ms": round(st["proj"]["mean"], 4), "proj_tflops": round(proj_flop / st["proj"]["mean"] / 1e9, 1),
         "proj_frac_bf16_peak": round(proj_flop / st["proj"]["mean"] / 1e9 / BF16_PEAK_TFLOPS, 4),
         "append_ms": round(st["append"]["mean"], 4),
@@ -247,7 +255,7 @@ def run_kvonly(reps: int = 8, dec_reps: int = 100):
         "append_frac_hbm": round(app_bytes / (st["append"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "attn_flop": attn_flop, "proj_flop": proj_flop, "append_bytes": app_bytes,
     }
-    del f, out
+    del f, out, ws
     torch.cuda.synchronize()
     # the decode step over the 16385 keys: the prefilled cache plus the new token
     L = DecodeLayer(wl, seed=1005, x_ctx=x)
@@ -432,19 +440,25 @@ def run_prefill(reps: int = 50):
     cache = T.new_cache(d, B, S)
     f = T.new_factors(d, B, S)
     out = torch.empty(B, S, d.n_heads * d.head_dim, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(T.tpa_prefill_workspace_bytes(d, B, S, 0), dtype=torch.uint8, device="cuda")
     st = {
         "proj": stats_ms(time_calls(lambda: T.tpa_factor_proj(d, x, wp, f, start_pos=0), reps)),
         "append": stats_ms(time_calls(lambda: T.tpa_cache_append(d, cache, f, 0), reps)),
-        "attn": stats_ms(time_calls(lambda: T.tpa_prefill_attn(d, f, cache, 0, True, out=out), reps)),
+        "attn": stats_ms(time_calls(lambda: T.tpa_prefill_attn_ws(d, f, cache, 0, ws, True, out=out), reps)),
+        "attn_no_ws": stats_ms(time_calls(lambda: T.tpa_prefill_attn(d, f, cache, 0, True, out=out), reps)),
     }
     n_out = T.tpa_packed_weight_rows(d)
     attn_flop = 4.0 * B * d.n_heads * d.head_dim * S * (S + 1) / 2
     proj_flop = 2.0 * B * S * d.d_model * n_out
-    a, p = st["attn"]["mean"], st["proj"]["mean"]
+    a, p, a0 = st["attn"]["mean"], st["proj"]["mean"], st["attn_no_ws"]["mean"]
     return {
         "workload": wl.name, "batch": B, "seq": S,
         "attn_us": us(st["attn"]), "attn_tflops": round(attn_flop / a / 1e9, 1),
         "attn_frac_bf16_peak": round(attn_flop / a / 1e9 / BF16_PEAK_TFLOPS, 4),
+        "attn_path": "tpa_prefill_attn_ws (K and V formed once into a workspace, then attended)",
+        "workspace_bytes": ws.numel(),
+        "attn_no_workspace_us": us(st["attn_no_ws"]),
+        "attn_no_workspace_frac_bf16_peak": round(attn_flop / a0 / 1e9 / BF16_PEAK_TFLOPS, 4),
         "proj_us": us(st["proj"]), "proj_tflops": round(proj_flop / p / 1e9, 1),
         "proj_frac_bf16_peak": round(proj_flop / p / 1e9 / BF16_PEAK_TFLOPS, 4),
         "append_us": us(st["append"]),

@@ -549,33 +549,45 @@ bool prefill_mfma32_supported(int dtype, const AttnArgs& a) {
 
 // K and V of every (sequence, head) and key 0 .. T-1, formed once:
 // km[b][h][t][:] = bf16(sum_r A_K[b,t,h,r] B~_K[b,t,r,:]) and vm likewise, the
-// same arithmetic and rounding as the rebuild in LDS.  One thread per (key,
-// head, 8-wide slice) of sequence blockIdx.y; consecutive threads share a key,
-// so its dim-factor rows are read once per key from the cache.
+// same arithmetic and rounding as the rebuild in LDS.  One thread per (group
+// of kMatHeads heads, key, 8-wide slice) of sequence blockIdx.y, group-major:
+// a thread loads the key's dim-factor slices once for its heads, and a wave's
+// stores for one head are 1 KB runs.
+constexpr int kMatHeads = 4;
+
 template <int R>
 __global__ void __launch_bounds__(256) kv_material32_kernel(AttnArgs a, int64_t T, bf16_t* km, bf16_t* vm) {
   typedef typename RankWordP<R>::type W;
   const int h = a.h;
   const int i = (int)(blockIdx.x * 256 + threadIdx.x);
-  if ((int64_t)i >= T * h * 8) return;
+  const int T32 = (int)T, groups = (h + kMatHeads - 1) / kMatHeads;
+  if ((int64_t)i >= T * 8 * groups) return;
   const int64_t b = blockIdx.y;
   const int slice = i & 7, r = i >> 3;
-  const int hh = r % h, t = r / h;
+  const int t = r % T32, h0 = (r / T32) * kMatHeads;
   const int64_t row = b * a.max_seq + t;
-  const W ak = *reinterpret_cast<const W*>(reinterpret_cast<const bf16_t*>(a.c_ak) + (row * h + hh) * R);
-  const W av = *reinterpret_cast<const W*>(reinterpret_cast<const bf16_t*>(a.c_av) + (row * h + hh) * R);
   uint4 bk[R], bv[R];
 #pragma unroll
   for (int q = 0; q < R; ++q) {
     bk[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.c_bk) + (row * R + q) * 64 + slice * 8);
     bv[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.c_bv) + (row * R + q) * 64 + slice * 8);
   }
-  float kv[8], vv[8];
-  factor_combine<R>(ak, bk, kv);
-  factor_combine<R>(av, bv, vv);
-  const int64_t o = ((b * h + hh) * T + t) * 64 + slice * 8;
-  *reinterpret_cast<bf16x8_t*>(km + o) = pack8(kv);
-  *reinterpret_cast<bf16x8_t*>(vm + o) = pack8(vv);
+  const bf16_t* ak = reinterpret_cast<const bf16_t*>(a.c_ak) + row * h * R;
+  const bf16_t* av = reinterpret_cast<const bf16_t*>(a.c_av) + row * h * R;
+  const int64_t hstride = T * 64;
+  bf16_t* ko = km + b * h * hstride + (int64_t)t * 64 + slice * 8;
+  bf16_t* vo = vm + b * h * hstride + (int64_t)t * 64 + slice * 8;
+#pragma unroll
+  for (int j = 0; j < kMatHeads; ++j) {
+    const int hh = h0 + j;
+    if (hh < h) {
+      float kv[8], vv[8];
+      factor_combine<R>(*reinterpret_cast<const W*>(ak + hh * R), bk, kv);
+      factor_combine<R>(*reinterpret_cast<const W*>(av + hh * R), bv, vv);
+      *reinterpret_cast<bf16x8_t*>(ko + hh * hstride) = pack8(kv);
+      *reinterpret_cast<bf16x8_t*>(vo + hh * hstride) = pack8(vv);
+    }
+  }
 }
 
 // Pairs per group for the materialised order: the largest divisor of an XCD's
@@ -641,7 +653,8 @@ hipError_t launch_prefill_material(const AttnArgs& a, void* ws, hipStream_t st) 
   const int64_t T = a.start_pos + a.S;
   bf16_t* km = reinterpret_cast<bf16_t*>(ws);
   bf16_t* vm = km + a.n_batch * a.h * T * 64;
-  const dim3 mgrid((unsigned)((T * a.h * 8 + 255) / 256), (unsigned)a.n_batch);
+  const int64_t groups = (a.h + kMatHeads - 1) / kMatHeads;
+  const dim3 mgrid((unsigned)((T * 8 * groups + 255) / 256), (unsigned)a.n_batch);
   if (a.rk == 1)
     hipLaunchKernelGGL(kv_material32_kernel<1>, mgrid, dim3(256), 0, st, a, T, km, vm);
   else if (a.rk == 2)
