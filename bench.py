@@ -447,6 +447,11 @@ def run_prefill(reps: int = 50):
         "attn": stats_ms(time_calls(lambda: T.tpa_prefill_attn_ws(d, f, cache, 0, ws, True, out=out), reps)),
         "attn_no_ws": stats_ms(time_calls(lambda: T.tpa_prefill_attn(d, f, cache, 0, True, out=out), reps)),
     }
+    # the same projection writing the key/value factors straight into the cache
+    # slots (kv_batch_stride = max_seq), so the step needs no separate append
+    slot = cache.slot_factors(0)
+    into = T.Factors(f.a_q, f.b_q, slot.a_k, slot.b_k, slot.a_v, slot.b_v, 0, slot.kv_batch_stride)
+    st["proj_into_cache"] = stats_ms(time_calls(lambda: T.tpa_factor_proj(d, x, wp, into, start_pos=0), reps))
     n_out = T.tpa_packed_weight_rows(d)
     attn_flop = 4.0 * B * d.n_heads * d.head_dim * S * (S + 1) / 2
     proj_flop = 2.0 * B * S * d.d_model * n_out
@@ -463,6 +468,9 @@ def run_prefill(reps: int = 50):
         "proj_frac_bf16_peak": round(proj_flop / p / 1e9 / BF16_PEAK_TFLOPS, 4),
         "append_us": us(st["append"]),
         "step_ms": round((a + p + st["append"]["mean"]), 4),
+        "proj_into_cache_us": us(st["proj_into_cache"]),
+        "step_fused_ms": round(a + st["proj_into_cache"]["mean"], 4),
+        "step_fused": "projection into the cache slots, then the attention (no append launch)",
     }
 
 
