@@ -372,6 +372,30 @@ def test_decode_general_path_matches_fast_path():
     assert_close(slow, ref, "bf16", "decode general path")
 
 
+def test_prefill_ws_misaligned_output_takes_the_rebuild_path():
+    """An output 2 bytes past a 16-byte boundary: the workspace call runs the
+    kernels that take any alignment, leaves the workspace untouched and still
+    matches the oracle."""
+    require_gpu()
+    dims = D(1024, 16, 64, 6, 2, 2, "bf16")
+    B, S, sp = 2, 150, 10
+    announce("prefill ws misaligned output")
+    sh = shape_of(dims)
+    kv = I.factors(sh, B, sp + S, seed=77, dtype="bf16", std=1.0, with_query=False, v_std=value_std(1.0))
+    fq = I.factors(sh, B, S, seed=78, dtype="bf16", std=1.0)
+    cache = T.new_cache(dims, B, sp + S)
+    fill_cache(cache, kv)
+    n = T.tpa_prefill_workspace_bytes(dims, B, S, sp)
+    ws = torch.full((n,), 0x5a, dtype=torch.uint8, device="cuda")
+    out = _misaligned(torch.zeros(B, S, dims.n_heads * dims.head_dim, dtype=torch.bfloat16, device="cuda"))
+    T.tpa_prefill_attn_ws(dims, query_factors_gpu(T, dims, fq), cache, sp, ws, True, out=out)
+    torch.cuda.synchronize()
+    assert bool((ws == 0x5a).all()), "the workspace was written on the fallback path"
+    od = oracle_dims(dims)
+    ref = O.prefill(oracle_query(fq, dims), oracle_cache(kv, od, B, sp + S), od, B, S, sp, True)
+    assert_close(out, ref, "bf16", "prefill ws, misaligned output")
+
+
 @pytest.mark.parametrize("path", ["fused", "ws"])
 @pytest.mark.parametrize("wl_name,B,S,n_rows", [
     ("prefill_b4_s4k", 4, 4096, 48),       # the causal prefill workload at full size
