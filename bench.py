@@ -653,6 +653,26 @@ def cpu_baseline():
                           "sample": f"kvonly_b32_ctx16k: 2048 seeded query rows of 1 of 32 sequences, all "
                                     f"{s.n_heads} heads, causal over up to {S} keys; rate of those rows' "
                                     f"algorithmic flops"}
+        del cache, kv, outs
+    # ---- projection sample: the oracle's six products are matrix products, so
+    #      here the BLAS library takes all the threads
+    wl = I.WORKLOADS["kvonly_b32_ctx16k"]
+    s = wl.shape
+    od = O.Dims(s.d_model, s.n_heads, s.head_dim, s.rank_q, s.rank_k, s.rank_v, s.rope_base)
+    n_tok = 8192
+    x = I.to_f64(I.activations(1, n_tok, s.d_model, seed=2004, dtype="bf16"))
+    w = {k: I.to_f64(v) for k, v in I.weights(s, seed=2004, dtype="bf16").items()}
+    n_out = sum(v.shape[0] for v in w.values())
+    with threadpool_limits(limits=n_thr):
+        O.project(x[:, :64], w, od)   # (warm the library)
+        t0 = time.perf_counter()
+        f = O.project(x, w, od)
+        t_proj = time.perf_counter() - t0
+    assert all(np.all(np.isfinite(v)) for v in f.values())
+    res["projection"] = {"tflops": round(2.0 * n_tok * s.d_model * n_out / t_proj / 1e12, 5), "unit": "TFLOP/s",
+                         "seconds": round(t_proj, 3),
+                         "sample": f"kvonly_b32_ctx16k: {n_tok} of the 524288 tokens through the {n_out} x "
+                                   f"{s.d_model} packed projection (fp64 matrix products, BLAS on {n_thr} threads)"}
     return res
 
 
