@@ -178,6 +178,15 @@ def back_to_back_ms(fn, reps: int, warm: int = 3) -> float:
     return s.elapsed_time(e) / reps
 
 
+def call_stats(fn, reps: int):
+    """Spread (ms) of single calls with an event around each (stats_ms), plus
+    "avg": the mean over back-to-back calls between two events, which the
+    rates use (an event between calls costs a few microseconds)."""
+    st = stats_ms(time_calls(fn, reps))
+    st["avg"] = back_to_back_ms(fn, reps)
+    return st
+
+
 def decode_roofline(layer: DecodeLayer, reps: int = ROOFLINE_REPS):
     """The decode call's average duration over `reps` back-to-back calls (the
     roofline's time), and the spread of single calls from a second pass with
@@ -388,16 +397,18 @@ def run_paged(layers, reps: int = 64):
             it[0] += 1
             L = layers[i]
             T.tpa_paged_decode_attn(d, L.q, pcs[i], lens, ctx, L.ws, out=L.out)
-        return stats_ms(time_calls(call, reps, warm=2 * len(layers)))
+        for _ in range(2 * len(layers)):
+            call()
+        return call_stats(call, reps)
 
     full_st, ragged_st = timed(full), timed(ragged)
     full_bytes = B * ctx * e_tok * 2
     ragged_bytes = int(ragged_cpu.sum()) * e_tok * 2
     return {"page_tokens": PAGE_TOKENS, "pages": B * pps, "table": "seeded random permutation",
-            "full_call_us": us(full_st), "full_GBps": round(full_bytes / (full_st["mean"] * 1e-3) / 1e9, 1),
+            "full_call_us": us(full_st), "full_GBps": round(full_bytes / (full_st["avg"] * 1e-3) / 1e9, 1),
             "ragged_keys": int(ragged_cpu.sum()), "ragged_call_us": us(ragged_st),
-            "ragged_GBps": round(ragged_bytes / (ragged_st["mean"] * 1e-3) / 1e9, 1),
-            "timing": "events around eager calls"}
+            "ragged_GBps": round(ragged_bytes / (ragged_st["avg"] * 1e-3) / 1e9, 1),
+            "timing": "rates from avg: eager calls back to back between two events; the spread: an event around each"}
 
 
 def run_shared(layers, reps: int = 64):
@@ -425,10 +436,12 @@ def run_shared(layers, reps: int = 64):
         it[0] += 1
         T.tpa_shared_decode_attn(d, layers[i].q, scs[i], ctx, ws, out=layers[i].out)
 
-    st = stats_ms(time_calls(call, reps, warm=2 * len(layers)))
+    for _ in range(2 * len(layers)):
+        call()
+    st = call_stats(call, reps)
     nbytes = B * ctx * s.n_heads * (s.rank_k + s.rank_v) * 2
     flop = 2.0 * B * ctx * s.n_heads * s.rank_k * s.head_dim
-    ms = st["mean"]
+    ms = st["avg"]
     return {"call_us": us(st), "bytes_per_call": nbytes,
             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "products_TFLOPs": round(flop / (ms * 1e-3) / 1e12, 2),
@@ -453,8 +466,8 @@ def run_shared_long(reps: int = 50):
     q = T.Factors(rnd(B, s.n_heads, s.rank_q), rnd(B, s.rank_q, s.head_dim), None, None, None, None)
     ws = torch.empty(T.tpa_shared_decode_workspace_bytes(d, B, ctx), dtype=torch.uint8, device="cuda")
     out = torch.empty(B, s.n_heads * s.head_dim, dtype=torch.bfloat16, device="cuda")
-    st = stats_ms(time_calls(lambda: T.tpa_shared_decode_attn(d, q, sc, ctx, ws, out=out), reps))
-    ms = st["mean"]
+    st = call_stats(lambda: T.tpa_shared_decode_attn(d, q, sc, ctx, ws, out=out), reps)
+    ms = st["avg"]
     nbytes = B * ctx * s.n_heads * (s.rank_k + s.rank_v) * 2
     flop = 2.0 * B * ctx * s.n_heads * s.rank_k * s.head_dim
     return {"workload": wl.name, "batch": B, "context": ctx, "call_us": us(st),
@@ -481,20 +494,20 @@ def run_prefill(reps: int = 50):
     out = torch.empty(B, S, d.n_heads * d.head_dim, dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(T.tpa_prefill_workspace_bytes(d, B, S, 0), dtype=torch.uint8, device="cuda")
     st = {
-        "proj": stats_ms(time_calls(lambda: T.tpa_factor_proj(d, x, wp, f, start_pos=0), reps)),
-        "append": stats_ms(time_calls(lambda: T.tpa_cache_append(d, cache, f, 0), reps)),
-        "attn": stats_ms(time_calls(lambda: T.tpa_prefill_attn_ws(d, f, cache, 0, ws, True, out=out), reps)),
-        "attn_no_ws": stats_ms(time_calls(lambda: T.tpa_prefill_attn(d, f, cache, 0, True, out=out), reps)),
+        "proj": call_stats(lambda: T.tpa_factor_proj(d, x, wp, f, start_pos=0), reps),
+        "append": call_stats(lambda: T.tpa_cache_append(d, cache, f, 0), reps),
+        "attn": call_stats(lambda: T.tpa_prefill_attn_ws(d, f, cache, 0, ws, True, out=out), reps),
+        "attn_no_ws": call_stats(lambda: T.tpa_prefill_attn(d, f, cache, 0, True, out=out), reps),
     }
     # the same projection writing the key/value factors straight into the cache
     # slots (kv_batch_stride = max_seq), so the step needs no separate append
     slot = cache.slot_factors(0)
     into = T.Factors(f.a_q, f.b_q, slot.a_k, slot.b_k, slot.a_v, slot.b_v, 0, slot.kv_batch_stride)
-    st["proj_into_cache"] = stats_ms(time_calls(lambda: T.tpa_factor_proj(d, x, wp, into, start_pos=0), reps))
+    st["proj_into_cache"] = call_stats(lambda: T.tpa_factor_proj(d, x, wp, into, start_pos=0), reps)
     n_out = T.tpa_packed_weight_rows(d)
     attn_flop = 4.0 * B * d.n_heads * d.head_dim * S * (S + 1) / 2
     proj_flop = 2.0 * B * S * d.d_model * n_out
-    a, p, a0 = st["attn"]["mean"], st["proj"]["mean"], st["attn_no_ws"]["mean"]
+    a, p, a0 = st["attn"]["avg"], st["proj"]["avg"], st["attn_no_ws"]["avg"]
     return {
         "workload": wl.name, "batch": B, "seq": S,
         "attn_us": us(st["attn"]), "attn_tflops": round(attn_flop / a / 1e9, 1),
@@ -506,9 +519,9 @@ def run_prefill(reps: int = 50):
         "proj_us": us(st["proj"]), "proj_tflops": round(proj_flop / p / 1e9, 1),
         "proj_frac_bf16_peak": round(proj_flop / p / 1e9 / BF16_PEAK_TFLOPS, 4),
         "append_us": us(st["append"]),
-        "step_ms": round((a + p + st["append"]["mean"]), 4),
+        "step_ms": round((a + p + st["append"]["avg"]), 4),
         "proj_into_cache_us": us(st["proj_into_cache"]),
-        "step_fused_ms": round(a + st["proj_into_cache"]["mean"], 4),
+        "step_fused_ms": round(a + st["proj_into_cache"]["avg"], 4),
         "step_fused": "projection into the cache slots, then the attention (no append launch)",
     }
 
@@ -534,13 +547,13 @@ def run_shared_prefill(reps: int = 50):
     out = torch.empty(B, S, d.n_heads * d.head_dim, dtype=torch.bfloat16, device="cuda")
     T.tpa_shared_factor_proj(d, x, wp, f, start_pos=0)
     st = {
-        "proj": stats_ms(time_calls(lambda: T.tpa_shared_factor_proj(d, x, wp, f, start_pos=0), reps)),
-        "append": stats_ms(time_calls(lambda: T.tpa_shared_cache_append(d, cache, f, 0), reps)),
-        "attn": stats_ms(time_calls(lambda: T.tpa_shared_prefill_attn(d, f, cache, 0, True, out=out), reps)),
+        "proj": call_stats(lambda: T.tpa_shared_factor_proj(d, x, wp, f, start_pos=0), reps),
+        "append": call_stats(lambda: T.tpa_shared_cache_append(d, cache, f, 0), reps),
+        "attn": call_stats(lambda: T.tpa_shared_prefill_attn(d, f, cache, 0, True, out=out), reps),
     }
     attn_flop = 4.0 * B * d.n_heads * d.head_dim * S * (S + 1) / 2
     proj_flop = 2.0 * B * S * d.d_model * T.tpa_shared_packed_weight_rows(d)
-    a, p = st["attn"]["mean"], st["proj"]["mean"]
+    a, p = st["attn"]["avg"], st["proj"]["avg"]
     return {
         "workload": wl.name + " (shared basis)", "batch": B, "seq": S,
         "attn_us": us(st["attn"]), "attn_tflops": round(attn_flop / a / 1e9, 1),
@@ -548,7 +561,7 @@ def run_shared_prefill(reps: int = 50):
         "proj_us": us(st["proj"]), "proj_tflops": round(proj_flop / p / 1e9, 1),
         "proj_frac_bf16_peak": round(proj_flop / p / 1e9 / BF16_PEAK_TFLOPS, 4),
         "append_us": us(st["append"]),
-        "step_ms": round((a + p + st["append"]["mean"]), 4),
+        "step_ms": round((a + p + st["append"]["avg"]), 4),
     }
 
 
