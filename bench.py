@@ -545,11 +545,13 @@ def run_shared_prefill(reps: int = 50):
     f = T.new_factors(d, B, S)
     f = T.Factors(f.a_q, f.b_q, f.a_k, None, f.a_v, None)
     out = torch.empty(B, S, d.n_heads * d.head_dim, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(T.tpa_prefill_workspace_bytes(d, B, S, 0), dtype=torch.uint8, device="cuda")
     T.tpa_shared_factor_proj(d, x, wp, f, start_pos=0)
     st = {
         "proj": call_stats(lambda: T.tpa_shared_factor_proj(d, x, wp, f, start_pos=0), reps),
         "append": call_stats(lambda: T.tpa_shared_cache_append(d, cache, f, 0), reps),
-        "attn": call_stats(lambda: T.tpa_shared_prefill_attn(d, f, cache, 0, True, out=out), reps),
+        "attn": call_stats(lambda: T.tpa_shared_prefill_attn_ws(d, f, cache, 0, ws, True, out=out), reps),
+        "attn_no_ws": call_stats(lambda: T.tpa_shared_prefill_attn(d, f, cache, 0, True, out=out), reps),
     }
     attn_flop = 4.0 * B * d.n_heads * d.head_dim * S * (S + 1) / 2
     proj_flop = 2.0 * B * S * d.d_model * T.tpa_shared_packed_weight_rows(d)
@@ -558,6 +560,9 @@ def run_shared_prefill(reps: int = 50):
         "workload": wl.name + " (shared basis)", "batch": B, "seq": S,
         "attn_us": us(st["attn"]), "attn_tflops": round(attn_flop / a / 1e9, 1),
         "attn_frac_bf16_peak": round(attn_flop / a / 1e9 / BF16_PEAK_TFLOPS, 4),
+        "attn_path": "tpa_shared_prefill_attn_ws (keys rotated and formed once into a workspace, then attended)",
+        "attn_no_workspace_us": us(st["attn_no_ws"]),
+        "attn_no_workspace_frac_bf16_peak": round(attn_flop / st["attn_no_ws"]["avg"] / 1e9 / BF16_PEAK_TFLOPS, 4),
         "proj_us": us(st["proj"]), "proj_tflops": round(proj_flop / p / 1e9, 1),
         "proj_frac_bf16_peak": round(proj_flop / p / 1e9 / BF16_PEAK_TFLOPS, 4),
         "append_us": us(st["append"]),

@@ -160,6 +160,9 @@ hipError_t launch_prefill_ws(int dtype, const AttnArgs& a, void* ws, hipStream_t
 // Prefill over a shared-basis cache: c_bk / c_bv are the bases B_K [R_K, d_h]
 // (unrotated) and B_V [R_V, d_h]; key t is rotated at position t with tab.
 hipError_t launch_prefill_shared(int dtype, const AttnArgs& a, const RopeTable& tab, hipStream_t st);
+// The same with a workspace (sized by prefill_workspace_bytes), as
+// launch_prefill_ws: keys formed and rotated once, then attended.
+hipError_t launch_prefill_shared_ws(int dtype, const AttnArgs& a, const RopeTable& tab, void* ws, hipStream_t st);
 
 // ---- shared-basis variant: decode over a cache of head factors ------------------
 // AttnArgs as for the decode, except c_bk / c_bv are the bases shared by every

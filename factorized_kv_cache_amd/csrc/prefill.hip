@@ -195,7 +195,7 @@ hipError_t launch_prefill_mfma32_shared(const AttnArgs& a, const RopeTable& tab,
 bool prefill_material_shape_ok(int dtype, const AttnArgs& a);
 bool prefill_material_supported(int dtype, const AttnArgs& a);
 size_t prefill_material_bytes(const AttnArgs& a);
-hipError_t launch_prefill_material(const AttnArgs& a, void* ws, hipStream_t st);
+hipError_t launch_prefill_material(const AttnArgs& a, void* ws, const RopeTable* tab, hipStream_t st);
 
 // d_h = 64 runs on the 32x32x16 matrix-core kernel, d_h = 128 on the 16x16x32
 // one, every other shape (and fp32) on the general kernel.
@@ -214,8 +214,13 @@ size_t prefill_workspace_bytes(int dtype, const AttnArgs& a) {
 }
 
 hipError_t launch_prefill_ws(int dtype, const AttnArgs& a, void* ws, hipStream_t st) {
-  if (ws && prefill_material_supported(dtype, a)) return launch_prefill_material(a, ws, st);
+  if (ws && prefill_material_supported(dtype, a)) return launch_prefill_material(a, ws, nullptr, st);
   return launch_prefill(dtype, a, st);
+}
+
+hipError_t launch_prefill_shared_ws(int dtype, const AttnArgs& a, const RopeTable& tab, void* ws, hipStream_t st) {
+  if (ws && prefill_material_supported(dtype, a)) return launch_prefill_material(a, ws, &tab, st);
+  return launch_prefill_shared(dtype, a, tab, st);
 }
 
 // Shared-basis cache: the 32x32x16 matrix-core kernel where it takes the shape

@@ -41,7 +41,7 @@
 //
 // The same kernel also reads K and V formed once for the whole call into a
 // workspace (kv_material32_kernel, same arithmetic and rounding as the
-// rebuild): each block is then two 16-byte loads and LDS stores per thread
+// rebuild, for the standard and the shared-basis cache): each block is then two 16-byte loads and LDS stores per thread
 // instead of the rebuild's rank sums, which a 256-query workgroup would
 // otherwise repeat for every key it attends to.
 #include "kernels.h"
@@ -147,6 +147,15 @@ __device__ __forceinline__ void load_basis32(Rebuild32<R>& g, const AttnArgs& a)
     }
 }
 
+// One rotary pair turned by (c, s), contractions written out so every kernel
+// that forms shared-basis keys rounds them the same way.
+__device__ __forceinline__ void rotate_pair(float& x0, float& x1, float c, float s) {
+  const float y0 = fmaf(x0, c, -(x1 * s));
+  const float y1 = fmaf(x0, s, x1 * c);
+  x0 = y0;
+  x1 = y1;
+}
+
 // SHARED: k0 is the block's first key (= its position) and s_rev the rotary
 // frequencies; each key is rotated at its own position after the rank sum.
 template <int R, bool SHARED = false>
@@ -165,9 +174,7 @@ __device__ __forceinline__ void store_rebuild32(const Rebuild32<R>& g, bf16_t* k
       for (int q = 0; q < 4; ++q) {
         float c, sn;
         rope_cos_sin(s_rev, k0 + key, (d0 >> 1) + q, c, sn);
-        const float x0 = kv[2 * q], x1 = kv[2 * q + 1];
-        kv[2 * q] = x0 * c - x1 * sn;
-        kv[2 * q + 1] = x0 * sn + x1 * c;
+        rotate_pair(kv[2 * q], kv[2 * q + 1], c, sn);
       }
     }
     *reinterpret_cast<bf16x8_t*>(k_lds + key * LD + d0) = pack8(kv);
@@ -555,9 +562,17 @@ bool prefill_mfma32_supported(int dtype, const AttnArgs& a) {
 // stores for one head are 1 KB runs.
 constexpr int kMatHeads = 4;
 
-template <int R>
-__global__ void __launch_bounds__(256) kv_material32_kernel(AttnArgs a, int64_t T, bf16_t* km, bf16_t* vm) {
+// SHARED: the shared-basis cache (c_bk / c_bv are the bases); each key is
+// rotated at its own position after the rank sum, as the shared rebuild does.
+template <int R, bool SHARED>
+__global__ void __launch_bounds__(256) kv_material32_kernel(AttnArgs a, int64_t T, bf16_t* km, bf16_t* vm,
+                                                            RopeTable tab) {
   typedef typename RankWordP<R>::type W;
+  __shared__ double s_rev[SHARED ? 32 : 1];   // d_h = 64: 32 rotary pairs
+  if constexpr (SHARED) {
+    rope_stage(tab, 32, s_rev);
+    __syncthreads();
+  }
   const int h = a.h;
   const int i = (int)(blockIdx.x * 256 + threadIdx.x);
   const int T32 = (int)T, groups = (h + kMatHeads - 1) / kMatHeads;
@@ -566,11 +581,17 @@ __global__ void __launch_bounds__(256) kv_material32_kernel(AttnArgs a, int64_t 
   const int slice = i & 7, r = i >> 3;
   const int t = r % T32, h0 = (r / T32) * kMatHeads;
   const int64_t row = b * a.max_seq + t;
+  const int64_t brow = SHARED ? 0 : row;   // the shared bases have one row
   uint4 bk[R], bv[R];
 #pragma unroll
   for (int q = 0; q < R; ++q) {
-    bk[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.c_bk) + (row * R + q) * 64 + slice * 8);
-    bv[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.c_bv) + (row * R + q) * 64 + slice * 8);
+    bk[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.c_bk) + (brow * R + q) * 64 + slice * 8);
+    bv[q] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(a.c_bv) + (brow * R + q) * 64 + slice * 8);
+  }
+  float cs[4], sn[4];
+  if constexpr (SHARED) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rope_cos_sin(s_rev, t, 4 * slice + q, cs[q], sn[q]);
   }
   const bf16_t* ak = reinterpret_cast<const bf16_t*>(a.c_ak) + row * h * R;
   const bf16_t* av = reinterpret_cast<const bf16_t*>(a.c_av) + row * h * R;
@@ -584,6 +605,10 @@ __global__ void __launch_bounds__(256) kv_material32_kernel(AttnArgs a, int64_t 
       float kv[8], vv[8];
       factor_combine<R>(*reinterpret_cast<const W*>(ak + hh * R), bk, kv);
       factor_combine<R>(*reinterpret_cast<const W*>(av + hh * R), bv, vv);
+      if constexpr (SHARED) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rotate_pair(kv[2 * q], kv[2 * q + 1], cs[q], sn[q]);
+      }
       *reinterpret_cast<bf16x8_t*>(ko + hh * hstride) = pack8(kv);
       *reinterpret_cast<bf16x8_t*>(vo + hh * hstride) = pack8(vv);
     }
@@ -649,21 +674,31 @@ size_t prefill_material_bytes(const AttnArgs& a) {
   return (size_t)2 * a.n_batch * a.h * (a.start_pos + a.S) * 64 * sizeof(bf16_t);
 }
 
-hipError_t launch_prefill_material(const AttnArgs& a, void* ws, hipStream_t st) {
-  const int64_t T = a.start_pos + a.S;
-  bf16_t* km = reinterpret_cast<bf16_t*>(ws);
-  bf16_t* vm = km + a.n_batch * a.h * T * 64;
+template <bool SHARED>
+static void launch_material(const AttnArgs& a, int64_t T, bf16_t* km, bf16_t* vm, const RopeTable& tab,
+                            hipStream_t st) {
   const int64_t groups = (a.h + kMatHeads - 1) / kMatHeads;
   const dim3 mgrid((unsigned)((T * 8 * groups + 255) / 256), (unsigned)a.n_batch);
   if (a.rk == 1)
-    hipLaunchKernelGGL(kv_material32_kernel<1>, mgrid, dim3(256), 0, st, a, T, km, vm);
+    hipLaunchKernelGGL((kv_material32_kernel<1, SHARED>), mgrid, dim3(256), 0, st, a, T, km, vm, tab);
   else if (a.rk == 2)
-    hipLaunchKernelGGL(kv_material32_kernel<2>, mgrid, dim3(256), 0, st, a, T, km, vm);
+    hipLaunchKernelGGL((kv_material32_kernel<2, SHARED>), mgrid, dim3(256), 0, st, a, T, km, vm, tab);
   else
-    hipLaunchKernelGGL(kv_material32_kernel<4>, mgrid, dim3(256), 0, st, a, T, km, vm);
+    hipLaunchKernelGGL((kv_material32_kernel<4, SHARED>), mgrid, dim3(256), 0, st, a, T, km, vm, tab);
+}
+
+// tab: the rotary table for a shared-basis cache, nullptr for the standard one.
+hipError_t launch_prefill_material(const AttnArgs& a, void* ws, const RopeTable* tab, hipStream_t st) {
+  const int64_t T = a.start_pos + a.S;
+  bf16_t* km = reinterpret_cast<bf16_t*>(ws);
+  bf16_t* vm = km + a.n_batch * a.h * T * 64;
+  static const RopeTable unused = {};
+  if (tab)
+    launch_material<true>(a, T, km, vm, *tab, st);
+  else
+    launch_material<false>(a, T, km, vm, unused, st);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  static const RopeTable unused = {};
   return launch_pf32<kFromMaterial>(a, unused, km, vm, T, st);
 }
 

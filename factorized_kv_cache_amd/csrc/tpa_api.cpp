@@ -390,19 +390,24 @@ size_t tpa_prefill_workspace_bytes(const tpa_dims* d, int64_t n_batch, int64_t s
   return tpa::prefill_workspace_bytes(d->dtype, a);
 }
 
+// A workspace where one is needed: present, large enough, 16-byte aligned.
+static tpa_status check_prefill_workspace(size_t need, const void* workspace, size_t workspace_bytes) {
+  if (need == 0) return TPA_OK;
+  if (!workspace || workspace_bytes < need)
+    return fail(TPA_ERR_WORKSPACE, "prefill workspace needs %zu bytes (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  if ((uintptr_t)workspace % 16) return fail(TPA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  return TPA_OK;
+}
+
 tpa_status tpa_prefill_attn_ws(const tpa_dims* d, const tpa_factors* q, const tpa_cache* c, int64_t n_batch,
                                int64_t seq_len, int64_t start_pos, int32_t causal, void* out, void* workspace,
                                size_t workspace_bytes, void* stream) {
   tpa::AttnArgs a;
-  const tpa_status st = prefill_args(d, q, c, n_batch, seq_len, start_pos, causal, out, &a);
+  tpa_status st = prefill_args(d, q, c, n_batch, seq_len, start_pos, causal, out, &a);
   if (st != TPA_OK) return st;
   const size_t need = tpa::prefill_workspace_bytes(d->dtype, a);
-  if (need > 0) {
-    if (!workspace) return fail(TPA_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
-    if ((uintptr_t)workspace % 16) return fail(TPA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-    if (workspace_bytes < need)
-      return fail(TPA_ERR_CAPACITY, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-  }
+  if ((st = check_prefill_workspace(need, workspace, workspace_bytes)) != TPA_OK) return st;
   return hip_status(tpa::launch_prefill_ws(d->dtype, a, need > 0 ? workspace : nullptr, (hipStream_t)stream),
                     "tpa_prefill_attn_ws");
 }
@@ -707,9 +712,10 @@ tpa_status tpa_shared_decode_attn(const tpa_dims* d, const tpa_factors* q, const
                     "tpa_shared_decode_attn");
 }
 
-tpa_status tpa_shared_prefill_attn(const tpa_dims* d, const tpa_factors* q, const tpa_shared_cache* c,
-                                   int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
-                                   void* stream) {
+// Checks shared by the two shared-basis prefill entry points.
+static tpa_status shared_prefill_args(const tpa_dims* d, const tpa_factors* q, const tpa_shared_cache* c,
+                                      int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
+                                      tpa::AttnArgs* a) {
   tpa_status st = check_dims(d);
   if (st != TPA_OK) return st;
   if ((st = check_query(d, q)) != TPA_OK) return st;
@@ -727,9 +733,31 @@ tpa_status tpa_shared_prefill_attn(const tpa_dims* d, const tpa_factors* q, cons
   int64_t qs;
   if ((st = resolve_stride(q->q_batch_stride, seq_len, "q_batch_stride", &qs)) != TPA_OK) return st;
   const tpa_cache cc = shared_as_cache(c);
-  const tpa::AttnArgs a = attn_args(d, q, qs, &cc, n_batch, seq_len, start_pos, causal, out);
+  *a = attn_args(d, q, qs, &cc, n_batch, seq_len, start_pos, causal, out);
+  return TPA_OK;
+}
+
+tpa_status tpa_shared_prefill_attn(const tpa_dims* d, const tpa_factors* q, const tpa_shared_cache* c,
+                                   int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
+                                   void* stream) {
+  tpa::AttnArgs a;
+  const tpa_status st = shared_prefill_args(d, q, c, n_batch, seq_len, start_pos, causal, out, &a);
+  if (st != TPA_OK) return st;
   return hip_status(tpa::launch_prefill_shared(d->dtype, a, rope_table(d), (hipStream_t)stream),
                     "tpa_shared_prefill_attn");
+}
+
+tpa_status tpa_shared_prefill_attn_ws(const tpa_dims* d, const tpa_factors* q, const tpa_shared_cache* c,
+                                      int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  tpa::AttnArgs a;
+  tpa_status st = shared_prefill_args(d, q, c, n_batch, seq_len, start_pos, causal, out, &a);
+  if (st != TPA_OK) return st;
+  const size_t need = tpa::prefill_workspace_bytes(d->dtype, a);
+  if ((st = check_prefill_workspace(need, workspace, workspace_bytes)) != TPA_OK) return st;
+  return hip_status(tpa::launch_prefill_shared_ws(d->dtype, a, rope_table(d), need > 0 ? workspace : nullptr,
+                                                  (hipStream_t)stream),
+                    "tpa_shared_prefill_attn_ws");
 }
 
 // Takes an int: a C caller may pass any int, and a value outside the enum's

@@ -92,6 +92,8 @@ def _load():
         "tpa_shared_factor_proj": (ctypes.c_int, [P(tpa_dims), vp, i64, i64, i64, vp, i32, P(tpa_factors), vp]),
         "tpa_shared_prefill_attn": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_shared_cache), i64, i64, i64,
                                                    i32, vp, vp]),
+        "tpa_shared_prefill_attn_ws": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_shared_cache), i64, i64,
+                                                      i64, i32, vp, vp, ctypes.c_size_t, vp]),
         "tpa_shared_decode_workspace_bytes": (ctypes.c_size_t, [P(tpa_dims), i64, i64]),
         "tpa_shared_decode_attn": (ctypes.c_int, [P(tpa_dims), P(tpa_factors), P(tpa_shared_cache), i64, i64, vp, vp,
                                                   ctypes.c_size_t, vp]),
@@ -113,7 +115,8 @@ EXPORTED = ("tpa_packed_weight_rows", "tpa_cache_elems_per_token", "tpa_factor_p
             "tpa_prefill_backward_workspace_bytes", "tpa_prefill_attn_backward", "tpa_rope_b_backward",
             "tpa_paged_cache_append", "tpa_paged_decode_workspace_bytes", "tpa_paged_decode_attn",
             "tpa_shared_cache_append", "tpa_shared_packed_weight_rows", "tpa_shared_factor_proj",
-            "tpa_shared_prefill_attn", "tpa_shared_decode_workspace_bytes", "tpa_shared_decode_attn",
+            "tpa_shared_prefill_attn", "tpa_shared_prefill_attn_ws", "tpa_shared_decode_workspace_bytes",
+            "tpa_shared_decode_attn",
             "tpa_status_string", "tpa_last_error")
 
 
@@ -470,6 +473,20 @@ def tpa_shared_prefill_attn(dims: Dims, q: Factors, cache: SharedCache, start_po
         out = torch.empty(B, S, dims.n_heads * dims.head_dim, dtype=dims.torch_dtype, device=q.b_q.device)
     _check(_lib.tpa_shared_prefill_attn(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B, S,
                                         start_pos, 1 if causal else 0, _ptr(out), _stream(stream)))
+    return out
+
+
+def tpa_shared_prefill_attn_ws(dims: Dims, q: Factors, cache: SharedCache, start_pos: int,
+                               workspace: Optional[torch.Tensor], causal: bool = True,
+                               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Workspace sized by tpa_prefill_workspace_bytes (None where it is 0)."""
+    B, S = q.b_q.shape[0], q.b_q.shape[1]
+    if out is None:
+        out = torch.empty(B, S, dims.n_heads * dims.head_dim, dtype=dims.torch_dtype, device=q.b_q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.tpa_shared_prefill_attn_ws(ctypes.byref(dims.c()), ctypes.byref(q.c()), ctypes.byref(cache.c()), B,
+                                           S, start_pos, 1 if causal else 0, _ptr(out), _ptr(workspace), nbytes,
+                                           _stream(stream)))
     return out
 
 

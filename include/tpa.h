@@ -72,7 +72,7 @@ typedef enum {
   TPA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, odd head_dim, ... */
   TPA_ERR_UNSUPPORTED = 2,      /* valid TPA, but outside what this library runs */
   TPA_ERR_CAPACITY = 3,         /* batch or positions beyond the cache */
-  TPA_ERR_WORKSPACE = 4,        /* decode workspace missing or too small */
+  TPA_ERR_WORKSPACE = 4,        /* a needed workspace missing or too small */
   TPA_ERR_HIP = 5               /* a HIP launch failed */
 } tpa_status;
 
@@ -202,9 +202,9 @@ size_t tpa_prefill_workspace_bytes(const tpa_dims* dims, int64_t n_batch, int64_
  * workspace: device memory of at least tpa_prefill_workspace_bytes bytes,
  * 16-byte aligned, owned by the caller, overwritten; no contents are kept
  * between calls.  Calls that share a workspace must be ordered on one stream.
- * Errors: as tpa_prefill_attn; a NULL or misaligned workspace
- * (TPA_ERR_INVALID_ARGUMENT) or one smaller than needed (TPA_ERR_CAPACITY)
- * where one is needed. */
+ * Errors: as tpa_prefill_attn; where a workspace is needed, a NULL one or one
+ * smaller than that (TPA_ERR_WORKSPACE), a misaligned one
+ * (TPA_ERR_INVALID_ARGUMENT). */
 tpa_status tpa_prefill_attn_ws(const tpa_dims* dims, const tpa_factors* q, const tpa_cache* cache,
                                int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
                                void* workspace, size_t workspace_bytes, void* stream);
@@ -423,6 +423,19 @@ tpa_status tpa_shared_factor_proj(const tpa_dims* dims, const void* x, int64_t n
 tpa_status tpa_shared_prefill_attn(const tpa_dims* dims, const tpa_factors* q, const tpa_shared_cache* cache,
                                    int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
                                    void* stream);
+
+/* tpa_shared_prefill_attn with a caller-owned workspace, as
+ * tpa_prefill_attn_ws: every key and value of the call is formed once (each
+ * key rotated at its own position, rounded as tpa_shared_prefill_attn rounds
+ * it on chip) into the workspace and then attended; outputs equal
+ * tpa_shared_prefill_attn's bit for bit at R_K = R_V in {1, 2}.  The
+ * workspace is sized by tpa_prefill_workspace_bytes with the same dims and
+ * sizes (0: none needed, the call runs tpa_shared_prefill_attn).
+ * Errors: as tpa_shared_prefill_attn, and the workspace errors of
+ * tpa_prefill_attn_ws. */
+tpa_status tpa_shared_prefill_attn_ws(const tpa_dims* dims, const tpa_factors* q, const tpa_shared_cache* cache,
+                                      int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device workspace for tpa_shared_decode_attn: float32 partials
  * (max, sum, R_V weights) per sequence, key chunk and head; 0 for dims or

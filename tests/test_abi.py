@@ -159,10 +159,21 @@ def test_prefill_workspace_sizes_and_validation():
                                                                   B, S, sp, 1, FAKE, w, n, None)
     assert pf(3, 4, 0) == CAPACITY
     assert pf(2, 65, 0) == CAPACITY
-    assert pf(2, 8, 0, w=None) == INVALID
+    assert pf(2, 8, 0, w=None) == WORKSPACE
     assert pf(2, 8, 0, w=FAKE + 8) == INVALID
-    assert pf(2, 8, 0, n=need - 1) == CAPACITY
-    assert pf(2, 8, 2, n=need) == CAPACITY   # two more keys than sized for
+    assert pf(2, 8, 0, n=need - 1) == WORKSPACE
+    assert pf(2, 8, 2, n=need) == WORKSPACE   # two more keys than sized for
+    # the shared-basis prefill takes the same sizes and checks
+    sc = T.tpa_shared_cache(FAKE, FAKE, FAKE, FAKE, 2, 64)
+    sf = lambda B, S, sp, w=FAKE, n=need: lib.tpa_shared_prefill_attn_ws(ctypes.byref(d), ctypes.byref(q),
+                                                                         ctypes.byref(sc), B, S, sp, 1, FAKE, w, n, None)
+    assert sf(3, 4, 0) == CAPACITY
+    assert sf(2, 8, 0, w=None) == WORKSPACE
+    assert sf(2, 8, 0, w=FAKE + 8) == INVALID
+    assert sf(2, 8, 0, n=need - 1) == WORKSPACE
+    fp32 = dims(dtype=0)
+    assert lib.tpa_shared_prefill_attn_ws(ctypes.byref(fp32), ctypes.byref(q), ctypes.byref(sc), 2, 8, 0, 1, None,
+                                          None, 0, None) == INVALID   # out NULL, before any workspace check
 
 
 def test_decode_validation():

@@ -185,26 +185,61 @@ SHARED_PREFILL_CASES = [
 ]
 
 
+def shared_prefill(dims, q, cache, sp, causal, path):
+    """tpa_shared_prefill_attn, or (path "ws") tpa_shared_prefill_attn_ws with a
+    workspace of the size the library asks for (none where it asks for none)."""
+    if path == "fused":
+        return T.tpa_shared_prefill_attn(dims, q, cache, sp, causal)
+    B, S = q.b_q.shape[0], q.b_q.shape[1]
+    n = T.tpa_prefill_workspace_bytes(dims, B, S, sp)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+    return T.tpa_shared_prefill_attn_ws(dims, q, cache, sp, ws, causal)
+
+
+@pytest.mark.parametrize("path", ["fused", "ws"])
 @pytest.mark.parametrize("case", SHARED_PREFILL_CASES, ids=[c[0] for c in SHARED_PREFILL_CASES])
-def test_shared_prefill(case):
+def test_shared_prefill(case, path):
     require_gpu()
     name, dtype, B, S, sp, causal, dm, h, dh, rq, rk, rv, std, vstd = case
     dims = D(dm, h, dh, rq, rk, rv, dtype)
     Tn = sp + S
-    announce(f"shared prefill {name} B={B} S={S} sp={sp} causal={causal}")
+    announce(f"shared prefill {name} B={B} S={S} sp={sp} causal={causal} path={path}")
     f, basis, _, cache = shared_setup(dims, B, Tn, seed=171, std=std, vstd=vstd)
     fq = I.factors(shape_of(dims), B, S, seed=172, dtype=dtype, std=std)
-    out = T.tpa_shared_prefill_attn(dims, query_factors_gpu(T, dims, fq), cache, sp, causal)
-    out2 = T.tpa_shared_prefill_attn(dims, query_factors_gpu(T, dims, fq), cache, sp, causal)
+    out = shared_prefill(dims, query_factors_gpu(T, dims, fq), cache, sp, causal, path)
+    out2 = shared_prefill(dims, query_factors_gpu(T, dims, fq), cache, sp, causal, path)
     torch.cuda.synchronize()
     assert torch.equal(out, out2), "repeated shared prefill calls are not bit-identical"
     cache_a = {"a_k": I.to_f64(f["a_k"]), "a_v": I.to_f64(f["a_v"])}
     ref = O.prefill_shared(oracle_query(fq, dims), cache_a, {k: I.to_f64(v) for k, v in basis.items()},
                            oracle_dims(dims), B, S, sp, causal)
-    assert_close(out, ref, dtype, f"shared prefill {name}")
+    assert_close(out, ref, dtype, f"shared prefill {name} ({path})")
 
 
-def test_shared_prefill_full_size_sampled_rows():
+@pytest.mark.parametrize("case", [(2, 300, 0, True, 1024, 16, 6, 2, 2), (3, 130, 41, True, 256, 8, 2, 1, 1),
+                                  (2, 90, 30, False, 1024, 16, 6, 2, 2)])
+def test_shared_prefill_ws_matches_fused_bitwise(case):
+    """At ranks 1 and 2 the workspace path forms the same rotated bf16 keys and
+    values as the shared rebuild in LDS and attends in the same order: equal
+    outputs bit for bit, also after a stale workspace."""
+    require_gpu()
+    B, S, sp, causal, dm, h, rq, rk, rv = case
+    dims = D(dm, h, 64, rq, rk, rv, "bf16")
+    announce(f"shared prefill ws vs fused bitwise case={case}")
+    f, basis, _, cache = shared_setup(dims, B, sp + S, seed=173, std=1.0, vstd=0.5)
+    fq = I.factors(shape_of(dims), B, S, seed=174, dtype="bf16", std=1.0)
+    q = query_factors_gpu(T, dims, fq)
+    n = T.tpa_prefill_workspace_bytes(dims, B, S, sp)
+    assert n == 2 * B * h * (sp + S) * 64 * 2
+    ws = torch.full((n,), 0x7f, dtype=torch.uint8, device="cuda")
+    fused = T.tpa_shared_prefill_attn(dims, q, cache, sp, causal)
+    staged = T.tpa_shared_prefill_attn_ws(dims, q, cache, sp, ws, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, staged)
+
+
+@pytest.mark.parametrize("path", ["fused", "ws"])
+def test_shared_prefill_full_size_sampled_rows(path):
     """The prefill workload's shapes (4 sequences of 4096 tokens, d_model 1024,
     h 16, d_h 64, R_Q 6, R 2) with a shared basis, in one call; the oracle
     attends 40 sampled query rows per sequence."""
@@ -213,10 +248,10 @@ def test_shared_prefill_full_size_sampled_rows():
     s = wl.shape
     dims = D(s.d_model, s.n_heads, s.head_dim, s.rank_q, s.rank_k, s.rank_v, "bf16", s.rope_base)
     B, S = wl.batch, wl.seq
-    announce(f"shared prefill full size B={B} S={S}")
+    announce(f"shared prefill full size B={B} S={S} path={path}")
     f, basis, _, cache = shared_setup(dims, B, S, seed=181, extra=0)
     fq = I.factors(shape_of(dims), B, S, seed=182, dtype="bf16")
-    out = T.tpa_shared_prefill_attn(dims, query_factors_gpu(T, dims, fq), cache, 0, True)
+    out = shared_prefill(dims, query_factors_gpu(T, dims, fq), cache, 0, True, path)
     torch.cuda.synchronize()
     rng = np.random.default_rng(183)
     rows = np.unique(np.concatenate([[0, 1, 63, 64, S - 1], rng.integers(0, S, 35)]))
