@@ -716,7 +716,7 @@ def cpu_baseline():
     wl = I.WORKLOADS["kvonly_b32_ctx16k"]
     s = wl.shape
     od = O.Dims(s.d_model, s.n_heads, s.head_dim, s.rank_q, s.rank_k, s.rank_v, s.rope_base)
-    n_tok = 8192
+    n_tok = 32768
     x = I.to_f64(I.activations(1, n_tok, s.d_model, seed=2004, dtype="bf16"))
     w = {k: I.to_f64(v) for k, v in I.weights(s, seed=2004, dtype="bf16").items()}
     n_out = sum(v.shape[0] for v in w.values())
