@@ -185,6 +185,10 @@ __device__ __forceinline__ void split_pair8(const float (&x)[8], bf16x8_t& hi, b
   lo = pack8(l);
 }
 
+// Slack (log2 units) by which a score may pass a lane's running maximum
+// before the lane's sums are rescaled (p <= 2^8 meanwhile).
+constexpr float kShSlack = 8.f;
+
 // NT tiles per wave at most, HPL heads per lane per tile (RKP = 4 / HPL
 // columns each), MRV >= R_V value ranks.  blockDim = 256 x tile groups.
 // WIDE: four tiles of two heads per lane in one tile group (256 threads), which
@@ -351,17 +355,22 @@ __global__ void __launch_bounds__(WIDE ? 256 : 64 * 4 * kShMaxG, WIDE ? 3 : 1) s
           float s = 0.f;
 #pragma unroll
           for (int r = 0; r < RKP; ++r) s = fmaf(raw_elem<T>(cur[k].k, j * RKP + r), acc[k][j * RKP + r], s);
-          // one exponential per key: exp2(-|s - m|) is the old terms' factor
-          // when s is the new maximum, else the new term's weight
-          const float d = s - m[k][j];
-          const float e2 = fast_exp2(-fabsf(d));
-          const bool up = d > 0.f;
-          const float alpha = up ? e2 : 1.f, p = up ? 1.f : e2;
-          m[k][j] = up ? s : m[k][j];
-          l[k][j] = fmaf(l[k][j], alpha, p);
+          // The lane's running maximum moves only when a score passes it by
+          // more than kShSlack (always at the lane's first key), so the
+          // terms are rescaled rarely and each key costs one exponential.
+          const bool up = s > m[k][j] + kShSlack;
+          if (__any(up)) {
+            const float mn = up ? s : m[k][j];
+            const float alpha = up ? fast_exp2(m[k][j] - mn) : 1.f;   // 0 at the first key
+            m[k][j] = mn;
+            l[k][j] *= alpha;
 #pragma unroll
-          for (int r = 0; r < MRV; ++r)
-            w[k][j][r] = fmaf(w[k][j][r], alpha, p * raw_elem<T>(cur[k].v, j * MRV + r));
+            for (int r = 0; r < MRV; ++r) w[k][j][r] *= alpha;
+          }
+          const float p = fast_exp2(s - m[k][j]);
+          l[k][j] += p;
+#pragma unroll
+          for (int r = 0; r < MRV; ++r) w[k][j][r] = fmaf(p, raw_elem<T>(cur[k].v, j * MRV + r), w[k][j][r]);
         }
       }
     }
