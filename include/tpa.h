@@ -180,11 +180,12 @@ tpa_status tpa_prefill_attn(const tpa_dims* dims, const tpa_factors* q, const tp
                             int64_t n_batch, int64_t seq_len, int64_t start_pos, int32_t causal, void* out,
                             void* stream);
 
-/* Bytes of device workspace tpa_prefill_attn_ws uses for these sizes:
+/* Bytes of device workspace tpa_prefill_attn_ws (and
+ * tpa_shared_prefill_attn_ws) uses for these sizes:
  * 2 * n_batch * h * (start_pos + seq_len) * d_h * 2 where the matrix-core path
  * that forms K and V once applies (bf16, d_h = 64, R_K = R_V in {1, 2, 4}),
  * else 0 (the call then needs no workspace).  0 also for dims or sizes the
- * call rejects. */
+ * call rejects.  Host only; depends on the sizes alone. */
 size_t tpa_prefill_workspace_bytes(const tpa_dims* dims, int64_t n_batch, int64_t seq_len, int64_t start_pos);
 
 /* tpa_prefill_attn with a caller-owned workspace: the same attention (same
