@@ -372,6 +372,35 @@ def test_decode_general_path_matches_fast_path():
     assert_close(slow, ref, "bf16", "decode general path")
 
 
+@pytest.mark.parametrize("path", ["fused", "ws"])
+@pytest.mark.parametrize("kv_only", [False, True])
+def test_prefill_strided_queries(path, kv_only):
+    """Query factors that are the first S tokens of longer per-sequence buffers
+    (q_batch_stride = S + 7 tokens): the same outputs as contiguous ones."""
+    require_gpu()
+    dims = D(1536, 24, 64, 0, 4, 4, "bf16") if kv_only else D(1024, 16, 64, 6, 2, 2, "bf16")
+    B, S, sp = 3, 100, 20
+    announce(f"prefill strided queries kv_only={kv_only} path={path}")
+    sh = shape_of(dims)
+    kv = I.factors(sh, B, sp + S, seed=79, dtype="bf16", std=1.0, with_query=False, v_std=value_std(1.0))
+    fq = I.factors(sh, B, S + 7, seed=80, dtype="bf16", std=1.0)
+    cache = T.new_cache(dims, B, sp + S)
+    fill_cache(cache, kv)
+    full = query_factors_gpu(T, dims, fq)
+    strided = T.Factors(None if full.a_q is None else full.a_q[:, :S], full.b_q[:, :S], None, None, None, None,
+                        S + 7, 0)
+    dense = T.Factors(None if full.a_q is None else full.a_q[:, :S].contiguous(), full.b_q[:, :S].contiguous(),
+                      None, None, None, None)
+    got = prefill(dims, strided, cache, sp, True, path)
+    want = prefill(dims, dense, cache, sp, True, path)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    od = oracle_dims(dims)
+    q_ref = {k: v[:, :S] for k, v in fq.items() if k in ("a_q", "b_q", "q")}
+    ref = O.prefill(oracle_query(q_ref, dims), oracle_cache(kv, od, B, sp + S), od, B, S, sp, True)
+    assert_close(got, ref, "bf16", f"prefill strided queries ({path})")
+
+
 def test_prefill_ws_misaligned_output_takes_the_rebuild_path():
     """An output 2 bytes past a 16-byte boundary: the workspace call runs the
     kernels that take any alignment, leaves the workspace untouched and still
