@@ -401,6 +401,35 @@ def test_prefill_strided_queries(path, kv_only):
     assert_close(got, ref, "bf16", f"prefill strided queries ({path})")
 
 
+@pytest.mark.parametrize("kv_only", [False, True])
+def test_decode_strided_queries(kv_only):
+    """The new tokens' query factors read from the last row of longer
+    per-sequence buffers (q_batch_stride = 5 tokens): the same outputs as
+    contiguous ones, on the matrix-core decode."""
+    require_gpu()
+    dims = D(1536, 24, 64, 0, 4, 4, "bf16") if kv_only else D(1024, 16, 64, 6, 2, 2, "bf16")
+    B, ctx = 4, 900
+    announce(f"decode strided queries kv_only={kv_only}")
+    sh = shape_of(dims)
+    kv = I.factors(sh, B, ctx, seed=83, dtype="bf16", std=1.0, with_query=False, v_std=value_std(1.0))
+    fq = I.factors(sh, B, 5, seed=84, dtype="bf16", std=1.0)
+    cache = T.new_cache(dims, B, ctx)
+    fill_cache(cache, kv)
+    full = query_factors_gpu(T, dims, fq)
+    strided = T.Factors(None if full.a_q is None else full.a_q[:, 4], full.b_q[:, 4], None, None, None, None, 5, 0)
+    dense = T.Factors(None if full.a_q is None else full.a_q[:, 4].contiguous(), full.b_q[:, 4].contiguous(),
+                      None, None, None, None)
+    ws = T.new_workspace(dims, B, ctx)
+    got = T.tpa_decode_attn(dims, strided, cache, ctx, ws)
+    want = T.tpa_decode_attn(dims, dense, cache, ctx, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    od = oracle_dims(dims)
+    q_ref = {k: v[:, 4:5] for k, v in fq.items() if k in ("a_q", "b_q", "q")}
+    ref = O.decode(oracle_query(q_ref, dims), oracle_cache(kv, od, B, ctx), od, B, ctx)
+    assert_close(got, ref, "bf16", "decode strided queries")
+
+
 def test_prefill_ws_misaligned_output_takes_the_rebuild_path():
     """An output 2 bytes past a 16-byte boundary: the workspace call runs the
     kernels that take any alignment, leaves the workspace untouched and still
