@@ -12,6 +12,30 @@
 
 namespace tpa {
 
+// The copy touches each byte once, so both sides carry the non-temporal hint:
+// at 32 x 16,384 tokens (738 MB each way) it took the copy from 258 to 237 us
+// (the hint on the loads alone gained nothing, on the stores alone 10 us).
+template <typename U>
+__device__ __forceinline__ U load_once(const U* p) {
+  if constexpr (sizeof(U) == 16) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return U{t.x, t.y, t.z, t.w};
+  } else {
+    return __builtin_nontemporal_load(p);
+  }
+}
+
+template <typename U>
+__device__ __forceinline__ void store_once(U* p, const U& v) {
+  if constexpr (sizeof(U) == 16) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p));
+  } else {
+    __builtin_nontemporal_store(v, p);
+  }
+}
+
 template <typename U>
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
   const int t = blockIdx.y;
@@ -23,8 +47,8 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int64_t b = idx / units_per_seq;
     const int64_t u = idx - b * units_per_seq;
-    const U v = reinterpret_cast<const U*>(src + b * a.src_bstride[t])[u];
-    reinterpret_cast<U*>(dst + b * a.dst_bstride[t])[u] = v;
+    const U v = load_once(reinterpret_cast<const U*>(src + b * a.src_bstride[t]) + u);
+    store_once(reinterpret_cast<U*>(dst + b * a.dst_bstride[t]) + u, v);
   }
 }
 
