@@ -239,6 +239,20 @@ def run_headline(args):
     return L, wl, total_ms / K, stats_ms(step_ms), stats_ms(call_ms), stats_ms(proj_ms), achieved, rst, nbytes, avg
 
 
+def rope_standalone(d, f, reps: int = 20) -> dict:
+    """The standalone rotation (tpa_rope_b, in place) of the query dim factors
+    (the plain queries in KV-only mode) and the key dim factors of a projection
+    output: HBM-bound, each element read and written once.  The rotations
+    change the values in f, which nothing times afterwards."""
+    t_q = back_to_back_ms(lambda: T.tpa_rope_b(d, f.b_q, 0), reps)
+    t_k = back_to_back_ms(lambda: T.tpa_rope_b(d, f.b_k, 0), reps)
+    nbytes = 2 * (f.b_q.numel() + f.b_k.numel()) * f.b_k.element_size()
+    gbps = nbytes / ((t_q + t_k) * 1e-3) / 1e9
+    return {"rope_b_q_us": round(t_q * 1e3, 2), "rope_b_k_us": round(t_k * 1e3, 2),
+            "rope_bytes": nbytes, "rope_GBps": round(gbps, 1), "rope_frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+            "rope_timing": "tpa_rope_b on the query and on the key dim factors, each averaged over back-to-back calls"}
+
+
 # ---------------------------------------------------------------------------
 # KV-only workload at full size: prefill of 32 x 16384 tokens, then a decode step
 # ---------------------------------------------------------------------------
@@ -295,6 +309,7 @@ def run_kvonly(reps: int = 8, dec_reps: int = 100):
         "append_frac_hbm": round(app_bytes / (st["append"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "attn_flop": attn_flop, "proj_flop": proj_flop, "append_bytes": app_bytes,
     }
+    pre.update(rope_standalone(d, f))
     del f, out, ws
     torch.cuda.synchronize()
     # the decode step over the 16385 keys: the prefilled cache plus the new token
@@ -523,6 +538,7 @@ def run_prefill(reps: int = 50):
         "proj_into_cache_us": us(st["proj_into_cache"]),
         "step_fused_ms": round(a + st["proj_into_cache"]["avg"], 4),
         "step_fused": "projection into the cache slots, then the attention (no append launch)",
+        **rope_standalone(d, f),
     }
 
 

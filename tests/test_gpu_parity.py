@@ -57,6 +57,7 @@ def test_cache_append_bitwise(dtype, B, S, sp, max_b, max_s, dims_args):
     (3, 33, 6, 64, 5, 10000.0),
     (1, 4, 2, 128, 131069, 10000.0),     # positions near 128K
     (2, 5, 24, 64, 16380, 500000.0),
+    (2, 9, 3, 6, 7, 10000.0),            # d_h 6: no whole 16-byte pieces, the element kernel
 ])
 def test_rope_b(dtype, B, S, rows, dh, sp, base):
     require_gpu()
@@ -68,6 +69,26 @@ def test_rope_b(dtype, B, S, rows, dh, sp, base):
     T.tpa_rope_b(dims, g, sp)
     torch.cuda.synchronize()
     assert_close(g, ref, dtype, "rope_b", max_abs=(2e-6 if dtype == "f32" else None))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rope_b_piece_and_element_kernels_agree(dtype):
+    """The same rotation through the 16-byte-piece kernel (aligned b) and the
+    element kernel (b two bytes past a 16-byte boundary): bit for bit, and both
+    within the oracle bound."""
+    require_gpu()
+    B, S, rows, dh, sp, base = 3, 41, 5, 64, 1000, 10000.0
+    dims = D(16, 2, dh, 1, 1, 1, dtype, base)
+    announce(f"rope_b piece vs element {dtype}")
+    b = I.normal((B, S, rows, dh), 1.0, seed=43, stream="f_b_k", dtype=dtype)
+    ref = O.rope(I.to_f64(b), O.positions(sp, S), base)
+    g_piece = b.cuda()
+    g_elem = _misaligned(b.cuda())
+    T.tpa_rope_b(dims, g_piece, sp)
+    T.tpa_rope_b(dims, g_elem, sp)
+    torch.cuda.synchronize()
+    assert torch.equal(g_piece.cpu(), g_elem.cpu())
+    assert_close(g_piece, ref, dtype, "rope_b piece", max_abs=(2e-6 if dtype == "f32" else None))
 
 
 # --------------------------------------------------------------------------
