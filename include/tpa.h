@@ -286,7 +286,9 @@ size_t tpa_prefill_backward_workspace_bytes(const tpa_dims* dims, int64_t n_batc
  * dA[t,h,r] = (1/R) dX[t,h,:].B[t,r,:] and dB[t,r,:] = (1/R) sum_h A[t,h,r] dX[t,h,:].
  * The forward output is not an argument: the row sums rowsum(dO*O) take O as
  * recomputed in fp32 (a stored bf16 output would perturb every dS by its
- * rounding, which the cancelling rows of dS magnify).
+ * rounding, which the cancelling rows of dS magnify).  In bf16 the matrix-core
+ * passes form the scores from q and k as bf16 hi + lo pairs; dS, P, dO, v and
+ * the q and k that multiply dS enter their products as plain bf16.
  * Deterministic: repeated calls give the same bits.
  *   Passage: the Q_t/K_t/V_t equations and the attention of the code
  *   walk-through (前向传播), differentiated.
